@@ -1,0 +1,341 @@
+"""Plain float64 attention on the CPU: the oracle (test infrastructure only).
+
+Nothing in the product imports this module.  It states, as plainly as numpy
+allows, what the exact IO-aware attention forward pass returns:
+
+* the output ``O = softmax(scale * Q K^T) V``, the standard attention
+  formula given on the Kotaemon page ("Kotaemon FlashAttention应用：加快注意力
+  计算", the formula paragraph), with ``scale = 1/sqrt(d_k)`` in the
+  configurations used here;
+* the per-row normaliser that the tiling sketch on the HolySheep article
+  ("Flash Attention", French edition, section "Principe fondamental : tiling
+  et streaming") returns next to O.  It is read here as the natural-log
+  logsumexp of the scaled, masked scores of the row,
+  ``L_r = ln sum_c exp(scale * q_r . k_c)``.
+
+The pages state that the tiled method with an online running maximum and
+normaliser gives exactly this result (Kotaemon page, method list and the
+paragraph after it; HolySheep article, Chinese edition, section
+"IO 感知的算法设计").  So the oracle is the definition written out: it
+materialises the whole score matrix (in row chunks, each row complete),
+which is exactly what the GPU path must avoid.
+
+Readings of points the pages leave open:
+
+* Causal masking is top-left aligned: query row r of a sequence sees keys
+  c <= r (indices within the sequence).  The manual chunking recipe in the
+  French HolySheep article ("Erreurs courantes", item 1) gives query chunk
+  [i, i+c) the key prefix [0, i+c), which is this alignment.
+* Grouped-query attention: query head h reads key/value head
+  ``h // (Hq // Hkv)``, contiguous groups; the page on transformer memory
+  footprint ("Empreinte mémoire et calcul des couches Transformer dans les
+  LLM en production", section "Les deux géants consommateurs") uses H_KV = 8
+  for Llama-style models.
+* Varlen packing: sequences are packed token-major ``[T, H, d]`` with
+  int32 offsets ``cu_seqlens`` ``[B+1]``; L is returned as ``[B, Hq, Nmax]``
+  with NaN in rows past a sequence's length.
+
+Every array argument is float64 (the exact upcast of the stored inputs).
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ProcessPoolExecutor
+from typing import Iterable, Optional, Sequence, Tuple
+
+import numpy as np
+
+# Row chunk budget for the materialised score matrix (bytes of float64).
+_CHUNK_BYTES = 256 << 20
+
+
+def visible_keys(r: int, n: int, causal: bool) -> int:
+    """Number of keys query row ``r`` of an ``n``-long sequence sees."""
+    return r + 1 if causal else n
+
+
+def softmax_rows(S: np.ndarray) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Row softmax of a score block whose masked entries are -inf.
+
+    Returns ``(P, m, ell)``: the probabilities, the row maxima and the row
+    sums of ``exp(S - m)``; the logsumexp of row r is ``m_r + ln ell_r``.
+    Every row must hold at least one finite entry.
+    """
+    m = S.max(axis=1, keepdims=True)
+    E = np.exp(S - m)
+    ell = E.sum(axis=1, keepdims=True)
+    return E / ell, m[:, 0], ell[:, 0]
+
+
+def _group(h: int, Hq: int, Hkv: int) -> int:
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return h // (Hq // Hkv)
+
+
+def _head_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool,
+               scale: float, rows: Optional[np.ndarray] = None):
+    """Attention of one head of one sequence, by the definition.
+
+    q: [n, d], k/v: [n, d].  Returns O [R, d] and L [R] for the requested
+    rows (all rows if ``rows`` is None).  The score rows are formed in
+    chunks so that a very long sequence never holds more than
+    ``_CHUNK_BYTES`` of scores; every row is complete within its chunk.
+    """
+    n = q.shape[0]
+    if rows is None:
+        rows = np.arange(n)
+    rows = np.asarray(rows, dtype=np.int64)
+    O = np.empty((rows.size, v.shape[1]), dtype=np.float64)
+    L = np.empty(rows.size, dtype=np.float64)
+    chunk = max(1, _CHUNK_BYTES // (8 * max(n, 1)))
+    cols = np.arange(n)
+    for s in range(0, rows.size, chunk):
+        r = rows[s:s + chunk]
+        S = scores(q[r], k, scale)                        # [R, n]
+        if causal:
+            S = causal_mask(S, r, cols)
+        P, m, ell = softmax_rows(S)
+        O[s:s + chunk] = combine(P, v)
+        L[s:s + chunk] = logsumexp_of(m, ell)
+    return O, L
+
+
+def scores(q: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
+    """``scale * q k^T`` (the scaled dot products of the formula)."""
+    return scale * (q @ k.T)
+
+
+def causal_mask(S: np.ndarray, rows: np.ndarray, cols: np.ndarray) -> np.ndarray:
+    """Set the scores of keys after the query (col > row) to -inf."""
+    return np.where(cols[None, :] > rows[:, None], -np.inf, S)
+
+
+def combine(P: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """The probability-weighted sum of value rows, ``P v``."""
+    return P @ v
+
+
+def logsumexp_of(m: np.ndarray, ell: np.ndarray) -> np.ndarray:
+    """Natural-log logsumexp from the row maximum and the row sum of
+    ``exp(S - m)``."""
+    return m + np.log(ell)
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, causal: bool,
+              scale: float, cu_seqlens: Optional[np.ndarray] = None,
+              workers: int = 1):
+    """Exact attention forward: returns ``(O, L)`` in float64.
+
+    Fixed layout: q ``[B, Hq, N, d]``, k/v ``[B, Hkv, N, d]``; O has q's
+    shape and L is ``[B, Hq, N]``.
+    Varlen layout (``cu_seqlens`` given): q ``[T, Hq, d]``, k/v
+    ``[T, Hkv, d]``; O is ``[T, Hq, d]`` and L is ``[B, Hq, Nmax]`` with NaN
+    past each sequence's length.
+    ``workers`` > 1 spreads the (sequence, head) units over processes.
+    """
+    units = list(_units(q, k, cu_seqlens))
+    results = _map(units, q, k, v, causal, scale, cu_seqlens, workers)
+    return _assemble(q, cu_seqlens, units, results)
+
+
+def _units(q, k, cu_seqlens):
+    if cu_seqlens is None:
+        B, Hq = q.shape[0], q.shape[1]
+    else:
+        B, Hq = len(cu_seqlens) - 1, q.shape[1]
+    for b in range(B):
+        for h in range(Hq):
+            yield (b, h)
+
+
+def _slices(q, k, v, b, h, cu_seqlens):
+    Hq, Hkv = q.shape[1], k.shape[1]
+    g = _group(h, Hq, Hkv)
+    if cu_seqlens is None:
+        return q[b, h], k[b, g], v[b, g]
+    s, e = int(cu_seqlens[b]), int(cu_seqlens[b + 1])
+    return q[s:e, h], k[s:e, g], v[s:e, g]
+
+
+def _run_unit(args):
+    qs, ks, vs, causal, scale = args
+    return _head_rows(qs, ks, vs, causal, scale)
+
+
+def _map(units, q, k, v, causal, scale, cu_seqlens, workers):
+    jobs = [(*_slices(q, k, v, b, h, cu_seqlens), causal, scale) for b, h in units]
+    if workers <= 1:
+        return [_run_unit(j) for j in jobs]
+    with ProcessPoolExecutor(max_workers=workers, initializer=_one_blas_thread) as ex:
+        return list(ex.map(_run_unit, jobs, chunksize=1))
+
+
+def _one_blas_thread():
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    try:  # the environment variables only help before BLAS starts
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+
+
+def _assemble(q, cu_seqlens, units, results):
+    O = np.empty(q.shape, dtype=np.float64)
+    if cu_seqlens is None:
+        B, Hq, N = q.shape[0], q.shape[1], q.shape[2]
+        L = np.empty((B, Hq, N), dtype=np.float64)
+        for (b, h), (o, l) in zip(units, results):
+            O[b, h] = o
+            L[b, h] = l
+        return O, L
+    B, Hq = len(cu_seqlens) - 1, q.shape[1]
+    lens = np.diff(np.asarray(cu_seqlens, dtype=np.int64))
+    L = np.full((B, Hq, int(lens.max()) if B else 0), np.nan)
+    for (b, h), (o, l) in zip(units, results):
+        s = int(cu_seqlens[b])
+        O[s:s + o.shape[0], h] = o
+        L[b, h, :o.shape[0]] = l
+    return O, L
+
+
+def attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, causal: bool,
+                   scale: float, picks: Iterable[Tuple[int, int, int]],
+                   cu_seqlens: Optional[np.ndarray] = None):
+    """The same definition, for a few ``(b, h, row)`` picks only.
+
+    Used to check very large workloads row by row.  Returns O rows
+    ``[P, d]`` and L ``[P]`` in the order of ``picks``.
+    """
+    picks = list(picks)
+    O = np.empty((len(picks), v.shape[-1]), dtype=np.float64)
+    L = np.empty(len(picks), dtype=np.float64)
+    by_unit = {}
+    for i, (b, h, r) in enumerate(picks):
+        by_unit.setdefault((b, h), []).append((i, r))
+    for (b, h), items in by_unit.items():
+        qs, ks, vs = _slices(q, k, v, b, h, cu_seqlens)
+        idx = [i for i, _ in items]
+        rows = np.array([r for _, r in items], dtype=np.int64)
+        if rows.size and (rows.min() < 0 or rows.max() >= qs.shape[0]):
+            raise IndexError("row out of range")
+        o, l = _head_rows(qs, ks, vs, causal, scale, rows)
+        O[idx] = o
+        L[idx] = l
+    return O, L
+
+
+def attention_bruteforce(q, k, v, *, causal: bool, scale: float):
+    """Element-by-element attention with pure Python loops (tiny inputs).
+
+    No maximum is subtracted: every weight is ``exp(scale * q_r . k_c)``
+    summed with ``math.fsum``, so it checks the stabilised oracle through a
+    different route.  Fixed layout only: q ``[B, Hq, N, d]``,
+    k/v ``[B, Hkv, N, d]``.  Returns nested lists O[b][h][r][j], L[b][h][r].
+    """
+    B, Hq, N, d = (len(q), len(q[0]), len(q[0][0]), len(q[0][0][0]))
+    Hkv = len(k[0])
+    per_group = Hq // Hkv
+    O, L = [], []
+    for b in range(B):
+        Ob, Lb = [], []
+        for h in range(Hq):
+            g = 0
+            while not (g * per_group <= h < (g + 1) * per_group):
+                g += 1
+            Oh, Lh = [], []
+            for r in range(N):
+                last = r if causal else N - 1
+                w = []
+                for c in range(last + 1):
+                    dot = math.fsum(float(q[b][h][r][i]) * float(k[b][g][c][i])
+                                    for i in range(d))
+                    w.append(math.exp(scale * dot))
+                den = math.fsum(w)
+                Oh.append([math.fsum(w[c] * float(v[b][g][c][j])
+                                     for c in range(last + 1)) / den
+                           for j in range(d)])
+                Lh.append(math.log(den))
+            Ob.append(Oh)
+            Lb.append(Lh)
+        O.append(Ob)
+        L.append(Lb)
+    return O, L
+
+
+def attention_tiled_online(q, k, v, *, causal: bool, scale: float,
+                           Br: int, Bc: int,
+                           cu_seqlens: Optional[np.ndarray] = None):
+    """The tiled method with an online softmax, in float64.
+
+    Follows the method as the Kotaemon page lists it (method list, and the
+    online maximum/normaliser update that follows): Q is cut into row blocks
+    of ``Br``; for each row block, key/value blocks of ``Bc`` rows are taken
+    in order; each block's scores update a running row maximum ``m`` and
+    normaliser ``ell``, the accumulated output is rescaled by
+    ``exp(m_old - m_new)``, and the block's ``P V`` is added.  At the end
+    ``O = acc / ell`` and ``L = m + ln ell``.  exp(-inf) is taken as 0.
+    Same layouts and return values as :func:`attention`.
+    """
+    O = np.empty(q.shape, dtype=np.float64)
+    units = list(_units(q, k, cu_seqlens))
+    if cu_seqlens is None:
+        L = np.empty(q.shape[:3], dtype=np.float64)
+    else:
+        lens = np.diff(np.asarray(cu_seqlens, dtype=np.int64))
+        L = np.full((len(lens), q.shape[1], int(lens.max())), np.nan)
+    for b, h in units:
+        qs, ks, vs = _slices(q, k, v, b, h, cu_seqlens)
+        n = qs.shape[0]
+        o = np.empty_like(qs)
+        lse = np.empty(n)
+        for i0 in range(0, n, Br):
+            rows = np.arange(i0, min(i0 + Br, n))
+            m = np.full(rows.size, -np.inf)
+            ell = np.zeros(rows.size)
+            acc = np.zeros((rows.size, vs.shape[1]))
+            for j0 in range(0, n, Bc):
+                cols = np.arange(j0, min(j0 + Bc, n))
+                S = scale * (qs[rows] @ ks[cols].T)
+                if causal:
+                    S = np.where(cols[None, :] > rows[:, None], -np.inf, S)
+                m_new = np.maximum(m, S.max(axis=1))
+                safe = np.where(np.isneginf(m_new), 0.0, m_new)
+                P = np.exp(S - safe[:, None])
+                alpha = np.where(np.isneginf(m), 0.0, np.exp(m - safe))
+                ell = alpha * ell + P.sum(axis=1)
+                acc = alpha[:, None] * acc + P @ vs[cols]
+                m = m_new
+            o[rows] = acc / ell[:, None]
+            lse[rows] = m + np.log(ell)
+        if cu_seqlens is None:
+            O[b, h] = o
+            L[b, h] = lse
+        else:
+            s = int(cu_seqlens[b])
+            O[s:s + n, h] = o
+            L[b, h, :n] = lse
+    return O, L
+
+
+def unit_flops(n: int, d: int, causal: bool) -> float:
+    """Algorithmic FLOP of one head of one sequence: the two contractions
+    over the visible (query, key) pairs, 2*d each."""
+    pairs = n * (n + 1) // 2 if causal else n * n
+    return 4.0 * d * pairs
+
+
+def default_workers() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+__all__ = [
+    "attention", "attention_rows", "attention_bruteforce",
+    "attention_tiled_online", "softmax_rows", "visible_keys",
+    "unit_flops", "default_workers",
+]

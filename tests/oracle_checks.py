@@ -1,0 +1,255 @@
+"""Pins of the CPU oracle: facts fixed by the pages and by mathematics.
+
+Each ``check_*`` function takes an attention callable with the oracle's
+signature ``attn(q, k, v, *, causal, scale, cu_seqlens=None) -> (O, L)``
+and returns the largest deviation it finds from a fact that does not come
+from the oracle itself.  The real oracle must score at or below ``TOL`` on
+every check; each planted mistake (see ``test_oracle_pins.py``) must exceed
+it on at least one.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+
+TOL = 1e-10
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_2x2.txt")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _rand(seed, B=2, Hq=4, Hkv=2, N=7, d=5):
+    r = _rng(seed)
+    return (r.standard_normal((B, Hq, N, d)), r.standard_normal((B, Hkv, N, d)),
+            r.standard_normal((B, Hkv, N, d)))
+
+
+def _err(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if a.shape != b.shape:
+        return math.inf
+    if not (np.isfinite(a).all() and np.isfinite(b).all()):
+        return math.inf
+    return float(np.max(np.abs(a - b))) if a.size else 0.0
+
+
+def check_golden(attn):
+    """The hand-worked 2x2 example (tests/golden/hand_2x2.txt)."""
+    q = np.array([[[[math.log(3), 0.0], [0.0, math.log(7)]]]])
+    k = np.array([[[[1.0, 0.0], [0.0, 1.0]]]])
+    v = np.array([[[[4.0, 0.0], [0.0, 8.0]]]])
+    worst = 0.0
+    with open(GOLDEN) as f:
+        rows = [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+    for causal in (False, True):
+        O, L = attn(q, k, v, causal=causal, scale=1.0)
+        for c, r, o0, o1, lexpr in rows:
+            if int(c) != int(causal):
+                continue
+            r = int(r)
+            Lexp = math.log(float(lexpr[2:]))
+            worst = max(worst, abs(O[0, 0, r, 0] - float(o0)),
+                        abs(O[0, 0, r, 1] - float(o1)), abs(L[0, 0, r] - Lexp))
+    return worst
+
+
+def check_bruteforce(attn):
+    """Pure-Python, no-max-subtraction sums with math.fsum (tiny inputs)."""
+    from oracle import attention_bruteforce
+    worst = 0.0
+    for causal in (False, True):
+        q, k, v = _rand(11 + causal)
+        O, L = attn(q, k, v, causal=causal, scale=0.41)
+        Ob, Lb = attention_bruteforce(q.tolist(), k.tolist(), v.tolist(),
+                                      causal=causal, scale=0.41)
+        worst = max(worst, _err(O, Ob), _err(L, Lb))
+    return worst
+
+
+def check_library(attn):
+    """torch's scaled_dot_product_attention (the routine the French
+    HolySheep article calls) and torch.logsumexp, in float64 on the CPU."""
+    import torch
+    import torch.nn.functional as F
+    worst = 0.0
+    for causal in (False, True):
+        q, k, v = _rand(21 + causal, B=2, Hq=6, Hkv=2, N=37, d=16)
+        scale = 0.23
+        O, L = attn(q, k, v, causal=causal, scale=scale)
+        tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+        To = F.scaled_dot_product_attention(tq, tk, tv, is_causal=causal,
+                                            scale=scale, enable_gqa=True)
+        kr = tk.repeat_interleave(q.shape[1] // k.shape[1], dim=1)
+        S = scale * torch.matmul(tq, kr.transpose(-1, -2))
+        if causal:
+            n = q.shape[2]
+            S = S.masked_fill(torch.ones(n, n, dtype=torch.bool).triu(1), -math.inf)
+        TL = torch.logsumexp(S, dim=-1)
+        worst = max(worst, _err(O, To.numpy()), _err(L, TL.numpy()))
+    return worst
+
+
+def check_identical_keys(attn):
+    """All keys equal: every visible key gets the same weight, so O is the
+    mean of the visible values and L = scale*q.k + ln(#visible).  With
+    q = 0 as well, L = ln(#visible)."""
+    worst = 0.0
+    r = _rng(31)
+    B, Hq, Hkv, N, d = 1, 4, 2, 9, 6
+    for causal in (False, True):
+        for zero_q in (False, True):
+            q = np.zeros((B, Hq, N, d)) if zero_q else r.standard_normal((B, Hq, N, d))
+            k = np.broadcast_to(r.standard_normal((B, Hkv, 1, d)), (B, Hkv, N, d)).copy()
+            v = r.standard_normal((B, Hkv, N, d))
+            scale = 0.7
+            O, L = attn(q, k, v, causal=causal, scale=scale)
+            for h in range(Hq):
+                g = h // (Hq // Hkv)
+                n_vis = np.arange(1, N + 1) if causal else np.full(N, N)
+                mean = (np.cumsum(v[0, g], axis=0) / np.arange(1, N + 1)[:, None]
+                        if causal else np.broadcast_to(v[0, g].mean(axis=0), (N, d)))
+                Lx = scale * (q[0, h] @ k[0, g, 0]) + np.log(n_vis)
+                worst = max(worst, _err(O[0, h], mean), _err(L[0, h], Lx))
+    return worst
+
+
+def check_causal_row0(attn):
+    """Causal row 0 sees only key 0: O_0 = V_0 and L_0 = scale*q_0.k_0."""
+    q, k, v = _rand(41)
+    scale = 0.9
+    O, L = attn(q, k, v, causal=True, scale=scale)
+    worst = 0.0
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            g = h // (q.shape[1] // k.shape[1])
+            worst = max(worst, _err(O[b, h, 0], v[b, g, 0]),
+                        abs(L[b, h, 0] - scale * math.fsum(q[b, h, 0] * k[b, g, 0])))
+    return worst
+
+
+def check_tiled_online(attn):
+    """The tiled method with the online maximum/normaliser update gives the
+    materialised result (block sizes that do and do not divide N)."""
+    from oracle import attention_tiled_online
+    worst = 0.0
+    q, k, v = _rand(51, B=1, Hq=4, Hkv=2, N=101, d=8)
+    for causal in (False, True):
+        O, L = attn(q, k, v, causal=causal, scale=0.3)
+        for Br, Bc in ((48, 40), (16, 16), (7, 13), (128, 64), (1, 1)):
+            Ot, Lt = attention_tiled_online(q, k, v, causal=causal, scale=0.3, Br=Br, Bc=Bc)
+            worst = max(worst, _err(O, Ot), _err(L, Lt))
+    return worst
+
+
+def check_prefix(attn):
+    """Causal row r equals the last row of non-causal attention over the
+    prefix [0, r]."""
+    q, k, v = _rand(61, B=1, Hq=2, Hkv=1, N=12, d=4)
+    O, L = attn(q, k, v, causal=True, scale=0.5)
+    worst = 0.0
+    for r in range(q.shape[2]):
+        Op, Lp = attn(q[:, :, :r + 1], k[:, :, :r + 1], v[:, :, :r + 1],
+                      causal=False, scale=0.5)
+        worst = max(worst, _err(O[:, :, r], Op[:, :, r]), _err(L[:, :, r], Lp[:, :, r]))
+    return worst
+
+
+def check_permutation(attn):
+    """Non-causal: permuting key/value rows together changes nothing."""
+    q, k, v = _rand(71, N=10)
+    perm = _rng(72).permutation(10)
+    O, L = attn(q, k, v, causal=False, scale=0.6)
+    Op, Lp = attn(q, k[:, :, perm], v[:, :, perm], causal=False, scale=0.6)
+    return max(_err(O, Op), _err(L, Lp))
+
+
+def check_shift(attn):
+    """Adding w to every key adds scale*q.w to a row's scores: O unchanged,
+    L shifted by scale*q.w."""
+    q, k, v = _rand(81, N=8, d=5)
+    w = _rng(82).standard_normal(5)
+    worst = 0.0
+    for causal in (False, True):
+        O, L = attn(q, k, v, causal=causal, scale=0.8)
+        Os, Ls = attn(q, k + w, v, causal=causal, scale=0.8)
+        worst = max(worst, _err(O, Os), _err(Ls - L, 0.8 * (q @ w)))
+    return worst
+
+
+def check_gqa_equals_repeated(attn):
+    """GQA equals multi-head attention with each K/V head repeated for the
+    query heads of its group (contiguous groups)."""
+    q, k, v = _rand(91, B=2, Hq=6, Hkv=3, N=9, d=4)
+    worst = 0.0
+    for causal in (False, True):
+        O, L = attn(q, k, v, causal=causal, scale=0.4)
+        Om, Lm = attn(q, np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1),
+                      causal=causal, scale=0.4)
+        worst = max(worst, _err(O, Om), _err(L, Lm))
+    return worst
+
+
+def check_varlen_equals_fixed(attn):
+    """Packed sequences give the same result as each sequence run alone."""
+    r = _rng(101)
+    lens = [5, 1, 9, 3]
+    Hq, Hkv, d = 4, 2, 3
+    T = sum(lens)
+    q, k, v = (r.standard_normal((T, H, d)) for H in (Hq, Hkv, Hkv))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    worst = 0.0
+    for causal in (False, True):
+        O, L = attn(q, k, v, causal=causal, scale=0.5, cu_seqlens=cu)
+        for b, n in enumerate(lens):
+            s = cu[b]
+            sl = slice(s, s + n)
+            Of, Lf = attn(q[sl].transpose(1, 0, 2)[None], k[sl].transpose(1, 0, 2)[None],
+                          v[sl].transpose(1, 0, 2)[None], causal=causal, scale=0.5)
+            worst = max(worst, _err(O[sl], Of[0].transpose(1, 0, 2)),
+                        _err(L[b, :, :n], Lf[0]))
+            if not np.isnan(L[b, :, n:]).all():
+                worst = math.inf
+    return worst
+
+
+def check_large_scale(attn):
+    """A huge scale must not overflow: the softmax becomes the argmax."""
+    q, k, v = _rand(111, B=1, Hq=2, Hkv=2, N=6, d=4)
+    O, L = attn(q, k, v, causal=False, scale=1e3)
+    worst = 0.0
+    for h in range(2):
+        s = q[0, h] @ k[0, h].T
+        top = np.argmax(s, axis=1)
+        worst = max(worst, _err(O[0, h], v[0, h][top]),
+                    _err(L[0, h] / 1e3, s.max(axis=1)))
+    return worst if np.isfinite(O).all() else math.inf
+
+
+def check_convex(attn):
+    """Each output is a convex combination of the visible value rows."""
+    q, k, v = _rand(121, N=11)
+    worst = 0.0
+    for causal in (False, True):
+        O, _ = attn(q, k, v, causal=causal, scale=1.3)
+        for b in range(2):
+            for h in range(4):
+                g = h // 2
+                for r in range(11):
+                    vis = v[b, g, :r + 1] if causal else v[b, g]
+                    lo, hi = vis.min(axis=0), vis.max(axis=0)
+                    worst = max(worst, float(np.max(lo - O[b, h, r])),
+                                float(np.max(O[b, h, r] - hi)), 0.0)
+    return worst
+
+
+CHECKS = [
+    check_golden, check_bruteforce, check_library, check_identical_keys,
+    check_causal_row0, check_tiled_online, check_prefix, check_permutation,
+    check_shift, check_gqa_equals_repeated, check_varlen_equals_fixed,
+    check_large_scale, check_convex,
+]

@@ -1,0 +1,129 @@
+"""The oracle against facts that do not come from the oracle (CPU only)."""
+from __future__ import annotations
+
+import importlib
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests import oracle_checks as C
+
+exact = importlib.import_module("oracle.exact")
+
+
+@pytest.mark.parametrize("check", C.CHECKS, ids=lambda f: f.__name__)
+def test_oracle_pin(check):
+    assert check(oracle.attention) <= C.TOL
+
+
+def test_softmax_rows_sum_to_one():
+    r = np.random.default_rng(5)
+    S = r.standard_normal((17, 23)) * 30
+    S[np.triu_indices(17, 1, 23)] = -np.inf
+    P, m, ell = oracle.softmax_rows(S)
+    assert np.allclose(P.sum(axis=1), 1.0, atol=1e-14, rtol=0)
+    assert (P >= 0).all()
+    assert np.array_equal(m, S.max(axis=1))
+    assert np.allclose(m + np.log(ell), np.log(np.exp(S).sum(axis=1)), atol=1e-12)
+
+
+def test_attention_rows_matches_full():
+    w = workloads.make_custom(2, 4, 2, 16, "bf16", seed=7, N=300)
+    q, k, v = (workloads.to_f64(w[x], "bf16") for x in "qkv")
+    O, L = oracle.attention(q, k, v, causal=True, scale=0.25)
+    picks = [(0, 0, 0), (1, 3, 299), (0, 2, 150), (1, 1, 63)]
+    Or, Lr = oracle.attention_rows(q, k, v, causal=True, scale=0.25, picks=picks)
+    for i, (b, h, r) in enumerate(picks):
+        # BLAS blocking differs with the row count: equal up to rounding
+        assert np.max(np.abs(Or[i] - O[b, h, r])) < 1e-13
+        assert abs(Lr[i] - L[b, h, r]) < 1e-13
+
+
+def test_pool_matches_serial():
+    w = workloads.make_custom(1, 4, 4, 32, "fp16", seed=8, N=200)
+    q, k, v = (workloads.to_f64(w[x], "fp16") for x in "qkv")
+    O1, L1 = oracle.attention(q, k, v, causal=True, scale=0.2, workers=1)
+    O2, L2 = oracle.attention(q, k, v, causal=True, scale=0.2, workers=2)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: each plausible error in a piece of the oracle must be
+# caught by at least one pin above.
+
+def _mutants():
+    ln2 = np.log(2.0)
+    return {
+        "drop_scale": ("scores", lambda q, k, scale: q @ k.T),
+        "square_scale": ("scores", lambda q, k, scale: scale * scale * (q @ k.T)),
+        "transposed_scores": ("scores", lambda q, k, scale: scale * (q @ k.T).T),
+        "causal_off_by_one": ("causal_mask", lambda S, r, c: np.where(
+            c[None, :] > r[:, None] + 1, -np.inf, S)),
+        "causal_strict": ("causal_mask", lambda S, r, c: np.where(
+            c[None, :] >= np.maximum(r[:, None], 1), -np.inf, S)),
+        "causal_reversed": ("causal_mask", lambda S, r, c: np.where(
+            c[None, :] < r[:, None], -np.inf, S)),
+        "gqa_modulo": ("_group", lambda h, Hq, Hkv: h % Hkv),
+        "lse_log2": ("logsumexp_of", lambda m, ell: m / ln2 + np.log2(ell)),
+        "lse_no_max": ("logsumexp_of", lambda m, ell: np.log(ell)),
+        "unnormalised": ("softmax_rows", lambda S: (
+            np.exp(S - S.max(1, keepdims=True)), S.max(1),
+            np.exp(S - S.max(1, keepdims=True)).sum(1))),
+        "values_reversed": ("combine", lambda P, v: P @ v[::-1]),
+        "keys_as_values": ("combine", None),
+    }
+
+
+@pytest.mark.parametrize("name", sorted(_mutants()))
+def test_pins_catch_planted_mistake(name, monkeypatch):
+    attr, fn = _mutants()[name]
+    if name == "keys_as_values":
+        orig_head = exact._head_rows
+        monkeypatch.setattr(exact, "_head_rows",
+                            lambda q, k, v, causal, scale, rows=None:
+                            orig_head(q, k, k, causal, scale, rows))
+    else:
+        monkeypatch.setattr(exact, attr, fn)
+    worst = 0.0
+    for check in C.CHECKS:
+        try:
+            worst = max(worst, check(oracle.attention))
+        except Exception:
+            worst = np.inf
+        if worst > C.TOL:
+            break
+    assert worst > C.TOL, f"no pin caught the planted mistake {name}"
+
+
+# ---------------------------------------------------------------------------
+# Input generation (shared with the GPU side): rounding and lengths.
+
+def test_bf16_rounding_matches_torch():
+    import torch
+    x = np.random.default_rng(3).standard_normal(100000).astype(np.float32) * 7
+    x[:4] = [1.00390625, 1.01171875, -1.00390625, 3.0]   # ties to even
+    ours = workloads.round_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    back = workloads.bf16_bits_to_f32(ours)
+    assert np.array_equal(back, torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def test_varlen_lengths():
+    w = workloads.make_inputs("varlen_bf16")
+    lens = np.diff(w["cu_seqlens"])
+    assert lens.min() >= 1024 and lens.max() <= 8192 and len(lens) == 16
+    assert w["cu_seqlens"][0] == 0 and w["cu_seqlens"].dtype == np.int32
+    assert w["q"].shape == (int(w["cu_seqlens"][-1]), 32, 128)
+    assert w["N"] == lens.max()
+
+
+def test_workload_shapes():
+    for name, wl in workloads.WORKLOADS.items():
+        if wl.varlen or wl.N > 4096:
+            continue
+        x = workloads.make_inputs(name)
+        assert x["q"].shape == (wl.B, wl.Hq, wl.N, wl.d)
+        assert x["k"].shape == (wl.B, wl.Hkv, wl.N, wl.d)

@@ -1,0 +1,161 @@
+"""Seeded synthetic attention workloads.
+
+This module is shared by the CPU oracle and the HIP path's tests and bench.
+It only draws and rounds inputs; it holds none of the attention arithmetic.
+
+Each workload is a shape, an input precision and a seed.  Inputs are drawn
+as N(0, 1) in float32 with ``numpy.random.default_rng(seed)`` (in the order
+lengths (varlen only), q, k, v, each in C order) and then rounded to the
+storage precision with round-to-nearest-even.  The five named workloads are:
+
+* ``tiny_fp32``   B=1, H=2, N=256, d=64, fp32, non-causal (exactness case)
+* ``mha_fp16``    B=8, H=12, N=2048, d=64, fp16, causal
+* ``gqa_bf16``    B=4, Hq=32, Hkv=8, N=4096, d=128, bf16, causal (headline)
+* ``long_bf16``   B=1, Hq=32, Hkv=8, N=32768, d=128, bf16, causal
+* ``varlen_bf16`` 16 packed sequences, lengths uniform in [1024, 8192],
+                  Hq=32, Hkv=8, d=128, bf16, causal
+
+Storage formats returned by :func:`make_inputs`:
+
+* fp32 -> ``numpy.float32``
+* fp16 -> ``numpy.float16``
+* bf16 -> ``numpy.uint16`` holding the bfloat16 bit patterns
+
+Fixed-length layout is ``[B, H, N, d]``; varlen layout is token-major packed
+``[T, H, d]`` with ``cu_seqlens`` (int32, ``[B+1]``) giving offsets.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "Workload", "WORKLOADS", "HEADLINE", "make_inputs", "make_custom",
+    "round_to_bf16_bits", "bf16_bits_to_f32", "to_f64", "varlen_lengths",
+]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int               # batch size, or number of packed sequences (varlen)
+    Hq: int
+    Hkv: int
+    N: int               # sequence length, or max sequence length (varlen)
+    d: int
+    dtype: str           # "fp32" | "fp16" | "bf16"
+    causal: bool
+    seed: int
+    varlen: bool = False
+    len_lo: int = 0      # varlen: inclusive range of the uniform lengths
+    len_hi: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+WORKLOADS = {
+    w.name: w for w in [
+        Workload("tiny_fp32", 1, 2, 2, 256, 64, "fp32", False, 1001),
+        Workload("mha_fp16", 8, 12, 12, 2048, 64, "fp16", True, 1002),
+        Workload("gqa_bf16", 4, 32, 8, 4096, 128, "bf16", True, 1003),
+        Workload("long_bf16", 1, 32, 8, 32768, 128, "bf16", True, 1004),
+        Workload("varlen_bf16", 16, 32, 8, 8192, 128, "bf16", True, 1005,
+                 varlen=True, len_lo=1024, len_hi=8192),
+    ]
+}
+
+HEADLINE = "gqa_bf16"
+
+
+def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest even.
+
+    Inputs here are finite, so no NaN special-casing is needed.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float32 (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32)
+            << np.uint32(16)).view(np.float32)
+
+
+def to_f64(arr: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact upcast of stored inputs to float64."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(arr).astype(np.float64)
+    return np.asarray(arr).astype(np.float64)
+
+
+def _round(x32: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "fp32":
+        return x32
+    if dtype == "fp16":
+        return x32.astype(np.float16)      # numpy rounds to nearest even
+    if dtype == "bf16":
+        return round_to_bf16_bits(x32)
+    raise ValueError(dtype)
+
+
+def varlen_lengths(rng: np.random.Generator, count: int, lo: int, hi: int) -> np.ndarray:
+    """Sequence lengths uniform over the inclusive integer range [lo, hi]."""
+    return rng.integers(lo, hi + 1, count)
+
+
+def make_custom(B: int, Hq: int, Hkv: int, d: int, dtype: str, seed: int,
+                N: Optional[int] = None,
+                lengths: Optional[Sequence[int]] = None) -> dict:
+    """Draw q, k, v for an arbitrary shape.
+
+    Give ``N`` for the fixed layout or ``lengths`` for the varlen layout.
+    Returns a dict with q, k, v (storage format), cu_seqlens (varlen) or
+    None, N (max length), dtype and the lengths.
+    """
+    rng = np.random.default_rng(seed)
+    return _draw(rng, B, Hq, Hkv, d, dtype, N, lengths)
+
+
+def _draw(rng, B, Hq, Hkv, d, dtype, N, lengths):
+    if lengths is not None:
+        lengths = np.asarray(lengths, dtype=np.int64)
+        assert lengths.shape == (B,)
+        cu = np.zeros(B + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(lengths)
+        T = int(cu[-1])
+        qs, ks = (T, Hq, d), (T, Hkv, d)
+        nmax = int(lengths.max()) if B > 0 else 0
+    else:
+        cu = None
+        qs, ks = (B, Hq, N, d), (B, Hkv, N, d)
+        nmax = N
+    q = _round(rng.standard_normal(qs, dtype=np.float32), dtype)
+    k = _round(rng.standard_normal(ks, dtype=np.float32), dtype)
+    v = _round(rng.standard_normal(ks, dtype=np.float32), dtype)
+    return dict(q=q, k=k, v=v, cu_seqlens=cu, N=nmax, dtype=dtype,
+                lengths=None if lengths is None else lengths.tolist(),
+                B=B, Hq=Hq, Hkv=Hkv, d=d)
+
+
+def make_inputs(w: Workload | str) -> dict:
+    """Seeded inputs of a named workload (see the module docstring)."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    rng = np.random.default_rng(w.seed)
+    lengths = None
+    if w.varlen:
+        lengths = varlen_lengths(rng, w.B, w.len_lo, w.len_hi)
+    out = _draw(rng, w.B, w.Hq, w.Hkv, w.d, w.dtype,
+                None if w.varlen else w.N, lengths)
+    out["causal"] = w.causal
+    out["scale"] = w.scale
+    out["name"] = w.name
+    return out
