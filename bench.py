@@ -1,0 +1,170 @@
+"""Benchmark of the exact attention forward on one MI355X.
+
+One step = one forward pass (all steps of the path: grid map, Q load, K/V
+streaming, QK^T, masking, online softmax, PV, epilogue) over the headline
+workload: B=4, Hq=32, Hkv=8, N=4096, d=128, bf16, causal, fp32 O.  Inputs are
+resident in HBM before timing starts.
+
+Prints one JSON line: throughput (algorithmic TFLOP/s: 4*d*Hq per visible
+(query, key) pair), the roofline of the kernel (average launch time measured
+with HIP events on the launch stream), and the CPU oracle timed on a bounded
+sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s at 1 MI355X (% of MFMA peak), bf16 causal d=128 N=4096"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+KERNEL_SRC = os.path.join(ROOT, "exact_io_aware_amd", "csrc", "fa_fwd_kernels.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gqa_bf16")
+    ap.add_argument("--out-dtype", choices=["fp32", "in"], default="fp32")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-heads", type=int, default=64,
+                    help="query heads (from the first sequences) the oracle is timed on")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != source_digest() or t.get("kernel") != kernel:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, heads: int):
+    """The oracle, as it stands, on the first `heads` query heads (whole
+    sequences) of the workload, over a process pool of the host's cores."""
+    import numpy as np
+
+    import oracle
+    import workloads
+    G = w["Hq"] // w["Hkv"]
+    heads = max(G, (heads // G) * G)
+    q, k, v = (workloads.to_f64(w[x], w["dtype"]) for x in "qkv")
+    nb = max(1, heads // w["Hq"])
+    hq = min(heads, w["Hq"])
+    qs = np.ascontiguousarray(q[:nb, :hq])
+    ks = np.ascontiguousarray(k[:nb, :hq // G])
+    vs = np.ascontiguousarray(v[:nb, :hq // G])
+    workers = oracle.default_workers()
+    t0 = time.perf_counter()
+    oracle.attention(qs, ks, vs, causal=w["causal"], scale=w["scale"], workers=workers)
+    dt = time.perf_counter() - t0
+    fl = nb * hq * oracle.unit_flops(w["N"], w["d"], w["causal"])
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "sample": f"{nb} sequence(s) x {hq} query heads of {w['name']} "
+                      f"({nb * hq} of {w['B'] * w['Hq']} head-sequences), float64 numpy, "
+                      f"{dt:.2f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "multi-GPU runs are not part of this path", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import exact_io_aware_amd as fa
+    import workloads
+
+    w = workloads.make_inputs(args.workload)
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        if w["dtype"] == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    q, k, v = (up(w[x]) for x in "qkv")
+    cu = None if w["cu_seqlens"] is None else torch.from_numpy(w["cu_seqlens"]).to(dev)
+    out_dtype = torch.float32 if args.out_dtype == "fp32" else q.dtype
+    o = torch.empty(q.shape, dtype=out_dtype, device=dev)
+    lse = torch.empty((w["B"], w["Hq"], w["N"]), dtype=torch.float32, device=dev)
+    lengths = [w["N"]] * w["B"] if cu is None else list(np.diff(w["cu_seqlens"]))
+    flop = fa.flops(w["Hq"], w["d"], lengths, w["causal"])
+    dt_code = {"fp32": fa.FA_F32, "fp16": fa.FA_F16, "bf16": fa.FA_BF16}[w["dtype"]]
+    kname = fa.kernel_name(dt_code, w["d"], w["causal"], cu is not None,
+                           fa.FA_F32 if args.out_dtype == "fp32" else dt_code)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fa.fwd(q, k, v, causal=w["causal"], scale=w["scale"], cu_seqlens=cu,
+               max_seqlen=w["N"] if cu is not None else None, out_dtype=out_dtype,
+               out=o, lse=lse, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: exactly `steps` launches back to back on one stream,
+    # bracketed by device synchronisation; events on the launch stream give
+    # the per-launch durations.
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    total_ms = ev[0].elapsed_time(ev[-1])
+    ms_per_step = total_ms / args.steps
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    avg_launch_ms = sum(per) / len(per)
+    achieved = flop / (avg_launch_ms * 1e-3) / 1e12
+
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w["dtype"], "data": "synthetic",
+        "config": {"workload": w["name"], "B": w["B"], "Hq": w["Hq"], "Hkv": w["Hkv"],
+                   "N": w["N"], "d": w["d"], "causal": w["causal"],
+                   "out_dtype": args.out_dtype, "kernel": kname,
+                   "algorithmic_flop_per_step": flop},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_for(kname, w["name"])},
+        "timing": {"launch_ms_min": round(min(per), 4), "launch_ms_median":
+                   round(sorted(per)[len(per) // 2], 4), "wall_s": round(wall, 4)},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_heads)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

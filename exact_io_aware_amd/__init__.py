@@ -1,0 +1,12 @@
+"""Exact IO-aware attention forward (FlashAttention) for MI355X / gfx950.
+
+The computation runs in the HIP kernels of ``libfa.so`` (C ABI in
+``include/fa.h``); this package only marshals torch tensors into that call.
+There is no CPU or PyTorch fallback: if the library is missing or the device
+is not gfx950, calls raise.
+"""
+from ._lib import (  # noqa: F401
+    FA_BF16, FA_F16, FA_F32, STATUS, kernel_name, load, status_string,
+    supported, version,
+)
+from .fwd import fwd, flops  # noqa: F401

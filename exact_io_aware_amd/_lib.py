@@ -1,0 +1,75 @@
+"""ctypes binding of libfa.so (include/fa.h).  Argument marshalling only."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+FA_OK = 0
+STATUS = {
+    "FA_OK": 0, "FA_ERR_NULL": -1, "FA_ERR_SHAPE": -2, "FA_ERR_HEADDIM": -3,
+    "FA_ERR_GQA": -4, "FA_ERR_DTYPE": -5, "FA_ERR_ALIGN": -6, "FA_ERR_ALIAS": -7,
+    "FA_ERR_SCALE": -8, "FA_ERR_DEVICE": -9, "FA_ERR_LAUNCH": -10,
+}
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libfa.so once.  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m exact_io_aware_amd.build` "
+            "(there is no fallback path)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, i, i]
+    lib.fa_fwd.restype = i
+    lib.fa_fwd_check.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i, i]
+    lib.fa_fwd_check.restype = i
+    lib.fa_kernel_name.argtypes = [i, i, i, i, i]
+    lib.fa_kernel_name.restype = ctypes.c_char_p
+    lib.fa_supported.argtypes = [i, i, i]
+    lib.fa_supported.restype = i
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = i
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().fa_status_string(status).decode()
+
+
+def version() -> int:
+    return load().fa_version()
+
+
+def kernel_name(in_dtype: int, d: int, causal: bool, varlen: bool, out_dtype: int):
+    s = load().fa_kernel_name(in_dtype, d, int(causal), int(varlen), out_dtype)
+    return None if s is None else s.decode()
+
+
+def supported(in_dtype: int, d: int, causal: bool) -> bool:
+    return bool(load().fa_supported(in_dtype, d, int(causal)))
+
+
+def fwd_check(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, cu_seqlens,
+              in_dtype, out_dtype) -> int:
+    """fa_fwd_check with raw integer addresses (no GPU needed)."""
+    return load().fa_fwd_check(q, k, v, o, lse, B, Hq, Hkv, N, d, int(causal),
+                               scale, cu_seqlens, in_dtype, out_dtype)
+
+
+def fwd_raw(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, cu_seqlens,
+            stream, in_dtype, out_dtype) -> int:
+    """fa_fwd with raw integer device addresses and a raw hipStream_t."""
+    return load().fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, int(causal), scale,
+                         cu_seqlens, stream, in_dtype, out_dtype)

@@ -1,0 +1,84 @@
+// C ABI of libfa (declared and documented in include/fa.h).
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <mutex>
+
+#include "fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Per-device "is gfx950" answer, filled once per device.
+std::once_flag g_dev_once[kMaxDevices];
+int g_dev_ok[kMaxDevices];
+
+int device_status() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return FA_ERR_DEVICE;
+  std::call_once(g_dev_once[dev], [dev] {
+    hipDeviceProp_t prop;
+    g_dev_ok[dev] = hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+                    std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  });
+  return g_dev_ok[dev] ? FA_OK : FA_ERR_DEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd_check(const void* q, const void* k, const void* v, const void* o,
+                 const float* lse, int B, int Hq, int Hkv, int N, int d,
+                 int causal, float scale, const int* cu_seqlens, int in_dtype,
+                 int out_dtype) {
+  return fa::check_args(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale,
+                        cu_seqlens, in_dtype, out_dtype);
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+           const int* cu_seqlens, void* stream, int in_dtype, int out_dtype) {
+  int st = fa::check_args(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale,
+                          cu_seqlens, in_dtype, out_dtype);
+  if (st != FA_OK) return st;
+  st = device_status();
+  if (st != FA_OK) return st;
+  fa::LaunchArgs a{q, k, v, o, lse, cu_seqlens, B, Hq, Hkv, N, d, causal,
+                   scale, in_dtype, out_dtype};
+  return fa::launch_fwd(a, stream);
+}
+
+const char* fa_kernel_name(int in_dtype, int d, int causal, int varlen,
+                           int out_dtype) {
+  return fa::kernel_name(in_dtype, d, causal, varlen, out_dtype);
+}
+
+int fa_supported(int in_dtype, int d, int causal) {
+  const bool dt = in_dtype == FA_F32 || in_dtype == FA_F16 || in_dtype == FA_BF16;
+  return dt && (d == 64 || d == 128) && (causal == 0 || causal == 1);
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "bad shape: B, Hq, Hkv, N must be >= 1, causal 0 or 1, sizes in range";
+    case FA_ERR_HEADDIM: return "head dimension d must be 64 or 128";
+    case FA_ERR_GQA: return "Hq must be a multiple of Hkv";
+    case FA_ERR_DTYPE: return "bad dtype: in_dtype F32/F16/BF16, out_dtype F32 or in_dtype";
+    case FA_ERR_ALIGN: return "misaligned pointer: q, k, v, o need 16 bytes, lse and cu_seqlens 4";
+    case FA_ERR_ALIAS: return "o overlaps q, k, v or lse";
+    case FA_ERR_SCALE: return "scale must be finite and > 0";
+    case FA_ERR_DEVICE: return "no usable device: the current HIP device is not gfx950";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int fa_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+
+}  // extern "C"

@@ -1,0 +1,562 @@
+// Exact IO-aware attention forward ("FlashAttention") for gfx950 (MI355X).
+//
+// What is computed: O = softmax(scale * Q K^T) V and the per-row natural-log
+// logsumexp L (the standard formula of the Kotaemon page, "Kotaemon
+// FlashAttention应用：加快注意力计算", formula paragraph; L is the normaliser
+// the tiling sketch of the HolySheep Flash Attention article, French edition,
+// returns next to O).
+//
+// How (the method list of the Kotaemon page): Q is cut into row blocks; for
+// each row block the K/V blocks are streamed through on-chip memory (LDS);
+// each block's local dot products update a running row maximum and
+// normaliser, the accumulated output is rescaled and the block's P.V added;
+// O is normalised and written once at the end.  The score matrix never
+// leaves registers.
+//
+// gfx950 mapping (our design, not the pages'):
+//  * A workgroup is 4 waves.  Each wave owns 32 query rows of one query head.
+//    For GQA, up to 4 query heads sharing a K/V head share the workgroup, so
+//    one K/V tile in LDS feeds all of them.
+//  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16:
+//    the 32x32 accumulator puts one query per lane column (lane l and l+32
+//    hold the same query), so the row max / row sum are in-lane except one
+//    exchange between the two half-waves.
+//  * The probabilities P^T stay in registers: the accumulator layout of
+//    S^T is exactly the B-operand layout of O^T = V^T P^T once the key order
+//    inside each 16-key chunk is permuted (0-3,8-11 | 4-7,12-15); the
+//    A operand V^T is read with the same permutation straight from the
+//    row-major V tile with ds_read_b64_tr_b16 (LDS transpose read).
+//  * K/V tiles are double-buffered in LDS (one barrier per tile); global
+//    loads of tile j+1 are in flight while tile j is computed.
+//  * Online softmax in the log2 domain (scale*log2(e) folded into one FMA
+//    per score), with the running maximum only moved when a row's new
+//    maximum exceeds it by more than 8 (in log2 units).  The rescale is then
+//    exact as before, and P stays <= 2^8, so the result is the same
+//    mathematically; most tiles skip the O rescale.
+//  * Causal: tiles entirely above the diagonal are never visited; only
+//    diagonal and ragged-tail tiles take the per-element mask.
+//  * Workgroups are ordered longest-first within each (sequence, head group)
+//    and the units are laid out so that all workgroups of one K/V head land
+//    on the same XCD (workgroups are dealt round-robin over the 8 XCDs),
+//    keeping that head's K/V in one L2.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "fa.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Largest increase of a row maximum (log2 units) tolerated before the
+// running maximum is moved and the accumulators rescaled.
+constexpr float kRescaleSlack = 8.0f;
+
+struct FwdParams {
+  const void* q; const void* k; const void* v; void* o; float* lse;
+  const int* cu_seqlens;
+  int N, Hq, G;            // max length, query heads, Hq / Hkv
+  int hp, rows_per_wg, n_rblocks, n_hgroups, total_wg, xcd_remap;
+  float scale_log2;        // scale * log2(e)
+  long long q_bs, q_hs, q_rs;    // element strides of q (and o): batch, head, row
+  long long kv_bs, kv_hs, kv_rs; // element strides of k and v
+};
+
+// ---------------------------------------------------------------------------
+// Element-type traits for the 16-bit MFMA path.
+template <typename T> struct Ops;
+
+template <> struct Ops<__bf16> {
+  using vec8 = bf16x8;
+  static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // Two fp32 -> two bf16 (round to nearest even), packed in one dword.
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    f32x2 f = {lo, hi};
+    bf16x2 r = __builtin_convertvector(f, bf16x2);
+    return __builtin_bit_cast(uint32_t, r);
+  }
+};
+
+template <> struct Ops<_Float16> {
+  using vec8 = f16x8;
+  static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    f32x2 f = {lo, hi};
+    f16x2 r = __builtin_convertvector(f, f16x2);
+    return __builtin_bit_cast(uint32_t, r);
+  }
+};
+
+__device__ __forceinline__ float wave_swap_halves(float x) {
+  // value of lane l ^ 32
+  return __shfl_xor(x, 32, 64);
+}
+
+// LDS byte offset of 16-byte chunk c of tile row r.
+//  K tiles: chunk ^ (row % 8) — the 8 rows read together by one
+//  ds_read_b128 phase hit 8 different bank groups.
+//  V tiles: chunk ^ 2*(row % 4) — the 4 rows x 32 bytes read together by a
+//  16-lane group of ds_read_b64_tr_b16 hit 8 different bank groups.
+template <int D>
+__device__ __forceinline__ int k_off(int r, int c) {
+  return r * (D * 2) + ((c ^ (r & 7)) << 4);
+}
+template <int D>
+__device__ __forceinline__ int v_off(int r, int c) {
+  return r * (D * 2) + ((c ^ ((r & 3) << 1)) << 4);
+}
+
+// ---------------------------------------------------------------------------
+// 16-bit (bf16 / fp16) inputs: MFMA kernel.
+template <typename T, int D, bool CAUSAL, bool VARLEN, bool OUT_F32>
+__global__ __launch_bounds__(256, 2) void fa_fwd_mfma(FwdParams p) {
+  using vec8 = typename Ops<T>::vec8;
+  constexpr int BC = (D == 128) ? 64 : 128;  // keys per K/V tile
+  constexpr int NB = BC / 32;                // 32-key score blocks per tile
+  constexpr int KC = BC / 16;                // 16-key chunks (P.V k-steps)
+  constexpr int DB = D / 32;                 // 32-wide blocks of the output
+  constexpr int DC = D / 16;                 // 16-wide chunks of Q.K
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int LOADS = BC * CPR / 256;      // 16-byte loads per thread per tile
+  constexpr int TILE_BYTES = BC * D * 2;
+
+  __shared__ __attribute__((aligned(16))) char smem[2][2][TILE_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+
+  // a1: workgroup -> (sequence b, head group, row block).
+  int x = blockIdx.x;
+  if (p.xcd_remap) x = (x & 7) * (p.total_wg >> 3) + (x >> 3);
+  const int unit = x / p.n_rblocks;
+  int rb = x - unit * p.n_rblocks;
+  if (CAUSAL) rb = p.n_rblocks - 1 - rb;     // longest row blocks first
+  const int b = unit / p.n_hgroups;
+  const int hgrp = unit - b * p.n_hgroups;
+  const int h = hgrp * p.hp + (wave % p.hp);
+  const int kvh = (hgrp * p.hp) / p.G;
+
+  int seq0 = 0, len = p.N;
+  if (VARLEN) {
+    seq0 = p.cu_seqlens[b];
+    len = p.cu_seqlens[b + 1] - seq0;
+  }
+  const int wg_row0 = rb * p.rows_per_wg;
+  if (wg_row0 >= len) return;                 // uniform over the workgroup
+  const int row0 = wg_row0 + (wave / p.hp) * 32;
+  const int wg_rows_end = min(wg_row0 + p.rows_per_wg, len);
+  const int kv_end = CAUSAL ? wg_rows_end : len;
+  const int ntiles = (kv_end + BC - 1) / BC;
+  const bool active = row0 < len;
+  const int wave_kv_end = CAUSAL ? min(row0 + 32, len) : len;
+  const int wave_ntiles = active ? (wave_kv_end + BC - 1) / BC : 0;
+
+  const long long qbase = (VARLEN ? (long long)seq0 * p.q_rs : (long long)b * p.q_bs) +
+                          (long long)h * p.q_hs;
+  const long long kvbase = (VARLEN ? (long long)seq0 * p.kv_rs : (long long)b * p.kv_bs) +
+                           (long long)kvh * p.kv_hs;
+  const T* __restrict__ qp = (const T*)p.q + qbase;
+  const char* __restrict__ kp = (const char*)((const T*)p.k + kvbase);
+  const char* __restrict__ vp = (const char*)((const T*)p.v + kvbase);
+  const long long kv_rs_bytes = p.kv_rs * 2;
+
+  // a2: this wave's Q rows as MFMA B operands (d-chunk dc, 8 values per lane:
+  // Q[row0 + l32][16*dc + 8*hf .. +7]).  Rows past the end are clamped; their
+  // results are never stored.
+  vec8 qf[DC];
+  {
+    const int qr = min(row0 + l32, len - 1);
+    const T* src = qp + (long long)qr * p.q_rs + hf * 8;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) qf[dc] = *(const vec8*)(src + dc * 16);
+  }
+
+  // a3: tile loads.  Thread t moves 16-byte chunks t, t+256, ... of the
+  // BC x D tile of K and of V (row-major).  Key rows past the end are
+  // clamped to the last row (finite values; their scores are masked).
+  u32x4 kreg[LOADS], vreg[LOADS];
+  auto gload = [&](int tile) {
+    const int kb = tile * BC;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int cid = tid + 256 * i;
+      const int r = cid / CPR, c = cid % CPR;
+      const long long off = (long long)min(kb + r, len - 1) * kv_rs_bytes + c * 16;
+      kreg[i] = *(const u32x4*)(kp + off);
+      vreg[i] = *(const u32x4*)(vp + off);
+    }
+  };
+  auto swrite = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int cid = tid + 256 * i;
+      const int r = cid / CPR, c = cid % CPR;
+      *(u32x4*)(&smem[buf][0][k_off<D>(r, c)]) = kreg[i];
+      *(u32x4*)(&smem[buf][1][v_off<D>(r, c)]) = vreg[i];
+    }
+  };
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
+  float m_run = -__builtin_inff();  // running max of scaled scores (log2 units)
+  float ell = 0.0f;                 // this lane's part of the row sum
+
+  const int qrow = row0 + l32;      // query index of this lane
+
+  gload(0);
+  swrite(0);
+  __syncthreads();
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < ntiles) gload(j + 1);
+
+    if (j < wave_ntiles) {
+      const int kb = j * BC;
+      const char* ks = smem[buf][0];
+      const char* vs = smem[buf][1];
+
+      // a4: S^T = K Q^T, block nb covers keys kb + 32*nb .. +31.
+      f32x16 s[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        s[nb] = f32x16{};
+        const int kr = 32 * nb + l32;
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) {
+          const vec8 kf = *(const vec8*)(ks + k_off<D>(kr, 2 * dc + hf));
+          s[nb] = Ops<T>::mfma(kf, qf[dc], s[nb]);
+        }
+      }
+
+      // a5: masks, only on tiles that cross the diagonal or the end.
+      const bool need_mask = (CAUSAL && kb + BC - 1 > row0) || (kb + BC > len);
+      if (need_mask) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kb + 32 * nb + 8 * (i >> 2) + 4 * hf + (i & 3);
+            const bool dead = (CAUSAL && key > qrow) || key >= len;
+            if (dead) s[nb][i] = -__builtin_inff();
+          }
+      }
+
+      // a6: online softmax.
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[nb][i]);
+      mx = fmaxf(mx, wave_swap_halves(mx));
+      const float mt = mx * p.scale_log2;
+      if (__any(mt > m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
+        ell *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        m_run = m_new;
+      }
+      const float neg_m = -m_run;
+      uint32_t pk[NB][8];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][i], p.scale_log2, neg_m));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][i + 1], p.scale_log2, neg_m));
+          ell += p0 + p1;
+          pk[nb][i >> 1] = Ops<T>::pack(p0, p1);
+        }
+
+      // a7: O^T += V^T P^T over the 16-key chunks of the tile.
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const int nb = kc >> 1, half = kc & 1;
+        u32x4 pb = {pk[nb][4 * half + 0], pk[nb][4 * half + 1],
+                    pk[nb][4 * half + 2], pk[nb][4 * half + 3]};
+        const vec8 pf = __builtin_bit_cast(vec8, pb);
+        // Transposed reads: lane i of each 16-lane group receives, for its
+        // output column d, the 4 keys held by lanes 4e + i/4 (e = 0..3).
+        const int g = lane >> 4, li = lane & 15;
+        const int vr0 = kc * 16 + 4 * hf + (li >> 2);   // first 4-key group
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int dcol = 32 * db + 16 * (g & 1) + 4 * (li & 3);
+          const int c = dcol >> 3, within = (dcol & 7) * 2;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(vs + v_off<D>(vr0, c) + within));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(vs + v_off<D>(vr0 + 8, c) + within));
+          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+          u32x4 vv = {lo2[0], lo2[1], hi2[0], hi2[1]};
+          oacc[db] = Ops<T>::mfma(__builtin_bit_cast(vec8, vv), pf, oacc[db]);
+        }
+      }
+    }
+
+    if (j + 1 < ntiles) swrite(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!active) return;
+
+  // a8: epilogue.  O = acc / ell, L = (m + log2 ell) * ln 2.
+  const float ell_t = ell + wave_swap_halves(ell);
+  const float inv = 1.0f / ell_t;
+  if (qrow < len) {
+    const long long orow = qbase + (long long)qrow * p.q_rs;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * db + 8 * g4 + 4 * hf;
+        const float a0 = oacc[db][4 * g4 + 0] * inv, a1 = oacc[db][4 * g4 + 1] * inv;
+        const float a2 = oacc[db][4 * g4 + 2] * inv, a3 = oacc[db][4 * g4 + 3] * inv;
+        if (OUT_F32) {
+          *(f32x4*)((float*)p.o + orow + d0) = f32x4{a0, a1, a2, a3};
+        } else {
+          u32x2 w = {Ops<T>::pack(a0, a1), Ops<T>::pack(a2, a3)};
+          *(u32x2*)((T*)p.o + orow + d0) = w;
+        }
+      }
+    if (hf == 0) {
+      const long long li = ((long long)b * p.Hq + h) * p.N + qrow;
+      p.lse[li] = (m_run + __builtin_amdgcn_logf(ell_t)) * kLn2;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 inputs: v_mfma_f32_32x32x2_f32 (full fp32 products and sums), P kept
+// in fp32.  Same transposed formulation; one 32-key tile at a time.  Each
+// wave owns 32 query rows; 4 waves cover 128 rows of one head.
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(256, 2) void fa_fwd_f32(FwdParams p) {
+  constexpr int BC = 32;
+  constexpr int KP = D + 1;      // padded K row (floats): conflict-free column reads
+  constexpr int DB = D / 32;
+  constexpr int DK = D / 2;      // k-steps of Q.K (2 per MFMA)
+  __shared__ float ks[BC * KP];
+  __shared__ float vs[BC * D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+
+  const int unit = blockIdx.x / p.n_rblocks;
+  int rb = blockIdx.x - unit * p.n_rblocks;
+  if (CAUSAL) rb = p.n_rblocks - 1 - rb;
+  const int b = unit / p.Hq;
+  const int h = unit - b * p.Hq;
+  const int kvh = h / p.G;
+  int seq0 = 0, len = p.N;
+  if (VARLEN) {
+    seq0 = p.cu_seqlens[b];
+    len = p.cu_seqlens[b + 1] - seq0;
+  }
+  const int wg_row0 = rb * 128;
+  if (wg_row0 >= len) return;
+  const int row0 = wg_row0 + wave * 32;
+  const int kv_end = CAUSAL ? min(wg_row0 + 128, len) : len;
+  const int ntiles = (kv_end + BC - 1) / BC;
+  const bool active = row0 < len;
+  const int wave_ntiles = active ? ((CAUSAL ? min(row0 + 32, len) : len) + BC - 1) / BC : 0;
+
+  const long long qbase = (VARLEN ? (long long)seq0 * p.q_rs : (long long)b * p.q_bs) +
+                          (long long)h * p.q_hs;
+  const long long kvbase = (VARLEN ? (long long)seq0 * p.kv_rs : (long long)b * p.kv_bs) +
+                           (long long)kvh * p.kv_hs;
+  const float* qp = (const float*)p.q + qbase;
+  const float* kp = (const float*)p.k + kvbase;
+  const float* vp = (const float*)p.v + kvbase;
+
+  const int qrow = row0 + l32;
+  float qf[DK];  // Q[qrow][2*t + hf]
+  {
+    const float* src = qp + (long long)min(qrow, len - 1) * p.q_rs;
+#pragma unroll
+    for (int t = 0; t < DK; ++t) qf[t] = src[2 * t + hf];
+  }
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
+  float m_run = -__builtin_inff(), ell = 0.0f;
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int kb = j * BC;
+    for (int e = tid; e < BC * D; e += 256) {
+      const int r = e / D, c = e % D;
+      const long long row = (long long)min(kb + r, len - 1) * p.kv_rs;
+      ks[r * KP + c] = kp[row + c];
+      vs[r * D + c] = vp[row + c];
+    }
+    __syncthreads();
+    if (j < wave_ntiles) {
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int t = 0; t < DK; ++t)
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(ks[l32 * KP + 2 * t + hf], qf[t], s, 0, 0, 0);
+      const bool need_mask = (CAUSAL && kb + BC - 1 > row0) || (kb + BC > len);
+      if (need_mask) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kb + 8 * (i >> 2) + 4 * hf + (i & 3);
+          if ((CAUSAL && key > qrow) || key >= len) s[i] = -__builtin_inff();
+        }
+      }
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
+      mx = fmaxf(mx, wave_swap_halves(mx));
+      const float mt = mx * p.scale_log2;
+      if (__any(mt > m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        ell *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        m_run = m_new;
+      }
+      float pr[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.scale_log2, -m_run));
+        ell += pr[i];
+      }
+      // O^T += V^T P^T: step i pairs key(i, half 0) and key(i, half 1).
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = 8 * (i >> 2) + 4 * hf + (i & 3);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[key * D + 32 * db + l32], pr[i],
+                                                         oacc[db], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+  if (!active) return;
+  const float ell_t = ell + wave_swap_halves(ell);
+  const float inv = 1.0f / ell_t;
+  if (qrow < len) {
+    float* orow = (float*)p.o + qbase + (long long)qrow * p.q_rs;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * db + 8 * g4 + 4 * hf;
+        *(f32x4*)(orow + d0) = f32x4{oacc[db][4 * g4] * inv, oacc[db][4 * g4 + 1] * inv,
+                                     oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv};
+      }
+    if (hf == 0)
+      p.lse[((long long)b * p.Hq + h) * p.N + qrow] = (m_run + __builtin_amdgcn_logf(ell_t)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch table.
+typedef void (*KernelFn)(FwdParams);
+
+struct Variant {
+  int in_dtype, d, causal, varlen, out_dtype;
+  KernelFn fn;
+  const char* name;
+};
+
+#define FA_SFX_C_0 ""
+#define FA_SFX_C_1 "_causal"
+#define FA_SFX_V_0 ""
+#define FA_SFX_V_1 "_varlen"
+#define FA_SFX_O_0 ""
+#define FA_SFX_O_1 "_of32"
+#define FA_CAT(a, b) a##b
+#define FA_V16(T, TN, DT, D, C, VL, OF)                                          \
+  {DT, D, C, VL, (OF) ? FA_F32 : DT, fa_fwd_mfma<T, D, (C != 0), (VL != 0), (OF != 0)>, \
+   "fa_fwd_mfma_" TN "_d" #D FA_CAT(FA_SFX_C_, C) FA_CAT(FA_SFX_V_, VL)           \
+       FA_CAT(FA_SFX_O_, OF)}
+#define FA_V16_ALL(T, TN, DT, D)                                                  \
+  FA_V16(T, TN, DT, D, 0, 0, 0), FA_V16(T, TN, DT, D, 0, 0, 1),                    \
+  FA_V16(T, TN, DT, D, 0, 1, 0), FA_V16(T, TN, DT, D, 0, 1, 1),                    \
+  FA_V16(T, TN, DT, D, 1, 0, 0), FA_V16(T, TN, DT, D, 1, 0, 1),                    \
+  FA_V16(T, TN, DT, D, 1, 1, 0), FA_V16(T, TN, DT, D, 1, 1, 1)
+#define FA_V32(D, C, VL)                                                           \
+  {FA_F32, D, C, VL, FA_F32, fa_fwd_f32<D, (C != 0), (VL != 0)>,                   \
+   "fa_fwd_f32_d" #D FA_CAT(FA_SFX_C_, C) FA_CAT(FA_SFX_V_, VL)}
+
+const Variant kVariants[] = {
+    FA_V16_ALL(__bf16, "bf16", FA_BF16, 64), FA_V16_ALL(__bf16, "bf16", FA_BF16, 128),
+    FA_V16_ALL(_Float16, "f16", FA_F16, 64), FA_V16_ALL(_Float16, "f16", FA_F16, 128),
+    FA_V32(64, 0, 0), FA_V32(64, 0, 1), FA_V32(64, 1, 0), FA_V32(64, 1, 1),
+    FA_V32(128, 0, 0), FA_V32(128, 0, 1), FA_V32(128, 1, 0), FA_V32(128, 1, 1),
+};
+
+const Variant* find_variant(int in_dtype, int d, int causal, int varlen, int out_dtype) {
+  for (const Variant& v : kVariants)
+    if (v.in_dtype == in_dtype && v.d == d && v.causal == causal && v.varlen == varlen &&
+        v.out_dtype == out_dtype)
+      return &v;
+  return nullptr;
+}
+
+}  // namespace
+
+const char* kernel_name(int in_dtype, int d, int causal, int varlen, int out_dtype) {
+  const Variant* v = find_variant(in_dtype, d, causal != 0, varlen != 0, out_dtype);
+  return v ? v->name : nullptr;
+}
+
+int launch_fwd(const LaunchArgs& a, void* stream) {
+  const bool varlen = a.cu_seqlens != nullptr;
+  const Variant* var = find_variant(a.in_dtype, a.d, a.causal, varlen, a.out_dtype);
+  if (!var) return FA_ERR_DTYPE;
+  const Plan plan = make_plan(a.B, a.Hq, a.Hkv, a.N, a.d, a.in_dtype);
+
+  FwdParams p;
+  p.q = a.q; p.k = a.k; p.v = a.v; p.o = a.o; p.lse = a.lse;
+  p.cu_seqlens = a.cu_seqlens;
+  p.N = a.N; p.Hq = a.Hq; p.G = a.Hq / a.Hkv;
+  p.hp = plan.hp; p.rows_per_wg = plan.rows_per_wg; p.n_rblocks = plan.n_rblocks;
+  p.n_hgroups = plan.n_hgroups; p.total_wg = (int)plan.total_wg;
+  p.xcd_remap = (a.in_dtype != FA_F32) && (plan.total_wg % 8 == 0);
+  p.scale_log2 = a.scale * kLog2e;
+  const long long d = a.d;
+  if (varlen) {
+    p.q_bs = 0; p.q_hs = d; p.q_rs = (long long)a.Hq * d;
+    p.kv_bs = 0; p.kv_hs = d; p.kv_rs = (long long)a.Hkv * d;
+  } else {
+    p.q_rs = d; p.q_hs = (long long)a.N * d; p.q_bs = (long long)a.Hq * a.N * d;
+    p.kv_rs = d; p.kv_hs = (long long)a.N * d; p.kv_bs = (long long)a.Hkv * a.N * d;
+  }
+  void* args[] = {&p};
+  const hipError_t e = hipLaunchKernel((const void*)var->fn, dim3((unsigned)plan.total_wg),
+                                       dim3(256), args, 0, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace fa

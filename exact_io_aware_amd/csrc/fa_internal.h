@@ -1,0 +1,63 @@
+// Internal interface between the C API (fa_api.cpp), the argument checks
+// (fa_validate.cpp) and the kernels (fa_fwd_kernels.hip).  Not installed.
+#ifndef FA_INTERNAL_H
+#define FA_INTERNAL_H
+
+#include <cstdint>
+
+#include "fa.h"
+
+namespace fa {
+
+// How the launch covers the work.  A workgroup is 4 waves; each wave owns
+// 32 query rows of one query head.  `hp` query heads that share one K/V head
+// are packed into a workgroup (GQA), so one K/V tile in LDS serves them all;
+// the workgroup then covers 128/hp rows of each of those heads.
+struct Plan {
+  int hp;            // query heads per workgroup (1, 2 or 4)
+  int rows_per_wg;   // query rows per head per workgroup (128 / hp)
+  int n_rblocks;     // row blocks per (sequence, head group): ceil(N / rows_per_wg)
+  int n_hgroups;     // head groups: Hq / hp
+  uint64_t total_wg; // B * n_hgroups * n_rblocks
+};
+
+inline Plan make_plan(int B, int Hq, int Hkv, int N, int d, int in_dtype) {
+  (void)d;
+  Plan p;
+  const int G = Hq / Hkv;
+  if (in_dtype == FA_F32) p.hp = 1;
+  else p.hp = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+  p.rows_per_wg = 128 / p.hp;
+  p.n_rblocks = (N + p.rows_per_wg - 1) / p.rows_per_wg;
+  p.n_hgroups = Hq / p.hp;
+  p.total_wg = (uint64_t)B * (uint64_t)p.n_hgroups * (uint64_t)p.n_rblocks;
+  return p;
+}
+
+inline uint64_t grid_size(int B, int Hq, int Hkv, int N, int d, int in_dtype) {
+  return make_plan(B, Hq, Hkv, N, d, in_dtype).total_wg;
+}
+
+int check_args(const void* q, const void* k, const void* v, const void* o,
+               const float* lse, int B, int Hq, int Hkv, int N, int d,
+               int causal, float scale, const int* cu_seqlens, int in_dtype,
+               int out_dtype);
+
+struct LaunchArgs {
+  const void* q; const void* k; const void* v; void* o; float* lse;
+  const int* cu_seqlens;
+  int B, Hq, Hkv, N, d, causal;
+  float scale;
+  int in_dtype, out_dtype;
+};
+
+// Enqueue the kernel for already-checked arguments.  Returns FA_OK or
+// FA_ERR_LAUNCH.  `stream` is a hipStream_t.
+int launch_fwd(const LaunchArgs& a, void* stream);
+
+// Static name of the kernel instance for these settings, or nullptr.
+const char* kernel_name(int in_dtype, int d, int causal, int varlen, int out_dtype);
+
+}  // namespace fa
+
+#endif  // FA_INTERNAL_H

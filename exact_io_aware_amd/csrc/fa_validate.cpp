@@ -1,0 +1,77 @@
+// Argument checks of fa_fwd (include/fa.h).  Pure C++: no HIP call, so the
+// checks run, and are tested, on a machine without a GPU.
+#include <cmath>
+#include <cstdint>
+
+#include "fa.h"
+#include "fa_internal.h"
+
+namespace fa {
+
+namespace {
+
+size_t elem_size(int dt) { return dt == FA_F32 ? 4 : 2; }
+
+bool mul_ok(uint64_t a, uint64_t b, uint64_t* out) {
+  if (a != 0 && b > UINT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+bool overlap(uintptr_t a, uint64_t na, uintptr_t b, uint64_t nb) {
+  return a < b + nb && b < a + na;
+}
+
+}  // namespace
+
+int check_args(const void* q, const void* k, const void* v, const void* o,
+               const float* lse, int B, int Hq, int Hkv, int N, int d,
+               int causal, float scale, const int* cu_seqlens, int in_dtype,
+               int out_dtype) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || (causal != 0 && causal != 1))
+    return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (Hq % Hkv != 0) return FA_ERR_GQA;
+  if (in_dtype != FA_F32 && in_dtype != FA_F16 && in_dtype != FA_BF16)
+    return FA_ERR_DTYPE;
+  if (out_dtype != FA_F32 && out_dtype != in_dtype) return FA_ERR_DTYPE;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_SCALE;
+
+  // Element counts; the packed layout's token count is bounded by B * N.
+  uint64_t rows, qn, kn, ln;
+  if (!mul_ok((uint64_t)B, (uint64_t)N, &rows)) return FA_ERR_SHAPE;
+  if (!mul_ok(rows, (uint64_t)Hq * (uint64_t)d, &qn)) return FA_ERR_SHAPE;
+  if (!mul_ok(rows, (uint64_t)Hkv * (uint64_t)d, &kn)) return FA_ERR_SHAPE;
+  if (!mul_ok(rows, (uint64_t)Hq, &ln)) return FA_ERR_SHAPE;
+  // Kernel index arithmetic uses 64-bit element offsets and 32-bit row,
+  // head and workgroup counts.
+  if (qn > (uint64_t)INT64_MAX / 4 || ln > (uint64_t)INT32_MAX * 64)
+    return FA_ERR_SHAPE;
+  if (grid_size(B, Hq, Hkv, N, d, in_dtype) > (uint64_t)INT32_MAX)
+    return FA_ERR_SHAPE;
+
+  auto mis = [](const void* p, uintptr_t a) { return ((uintptr_t)p) % a != 0; };
+  if (mis(q, 16) || mis(k, 16) || mis(v, 16) || mis(o, 16) || mis(lse, 4) ||
+      (cu_seqlens && mis(cu_seqlens, 4)))
+    return FA_ERR_ALIGN;
+
+  // o must not overlap any input or lse.  For the packed layout the true
+  // extent (T tokens) lives on the device, so only the B*N bound is known:
+  // there only identical start pointers are rejected.
+  const uintptr_t po = (uintptr_t)o;
+  if (po == (uintptr_t)q || po == (uintptr_t)k || po == (uintptr_t)v ||
+      po == (uintptr_t)lse)
+    return FA_ERR_ALIAS;
+  if (!cu_seqlens) {
+    const uint64_t ob = qn * elem_size(out_dtype), ib = elem_size(in_dtype);
+    if (overlap(po, ob, (uintptr_t)q, qn * ib) ||
+        overlap(po, ob, (uintptr_t)k, kn * ib) ||
+        overlap(po, ob, (uintptr_t)v, kn * ib) ||
+        overlap(po, ob, (uintptr_t)lse, ln * 4))
+      return FA_ERR_ALIAS;
+  }
+  return FA_OK;
+}
+
+}  // namespace fa

@@ -1,0 +1,126 @@
+/*
+ * fa.h — C ABI of libfa, an exact IO-aware attention forward pass
+ * ("FlashAttention") for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (fa_fwd): for every sequence b and query head h,
+ *
+ *     O[b,h] = softmax(scale * Q[b,h] K[b,g]^T) V[b,g],   g = h / (Hq/Hkv)
+ *     L[b,h,r] = ln sum_c exp(scale * Q[b,h,r] . K[b,g,c])   (visible c)
+ *
+ * - The formula is the standard attention formula of the Kotaemon page
+ *   ("Kotaemon FlashAttention应用：加快注意力计算", formula paragraph).
+ * - The method: Q is cut into row blocks; for each row block the K/V blocks
+ *   are streamed through on-chip memory; each block's scores update a running
+ *   row maximum and normaliser, so the result equals the formula exactly
+ *   (Kotaemon page, method list and the exactness paragraph after it;
+ *   HolySheep Flash Attention article, Chinese edition, section
+ *   "IO 感知的算法设计").  The N x N score matrix is never written to memory.
+ * - O and the per-row normaliser L are both returned, as in the tiling
+ *   sketch of the HolySheep article, French edition (section "Principe
+ *   fondamental : tiling et streaming"); L is read as the natural-log
+ *   logsumexp of the scaled, masked scores.
+ * - causal = 1 masks key c for query r when c > r (top-left alignment,
+ *   indices within the sequence), consistent with the manual chunking recipe
+ *   of the French HolySheep article ("Erreurs courantes", item 1).
+ * - Grouped-query attention: Hq must be a multiple of Hkv; query head h reads
+ *   K/V head h / (Hq/Hkv) (contiguous groups; the transformer memory page
+ *   "Empreinte mémoire et calcul des couches Transformer dans les LLM en
+ *   production" uses H_KV = 8 with d_head = 128).
+ *
+ * Layouts (all contiguous, head dimension fastest):
+ * - fixed length (cu_seqlens == NULL):
+ *       q, o   [B][Hq][N][d]       k, v   [B][Hkv][N][d]
+ * - packed variable length (cu_seqlens != NULL): B sequences packed token
+ *   by token; cu_seqlens is a DEVICE int32 array [B+1] with cu_seqlens[0] = 0
+ *   and non-decreasing offsets; T = cu_seqlens[B]; N must be >= the longest
+ *   sequence length (it sizes the launch, so no device value is read on the
+ *   host):
+ *       q, o   [T][Hq][d]          k, v   [T][Hkv][d]
+ * - lse is float32 [B][Hq][N] in both cases.  In the packed case the rows
+ *   r >= length of sequence b are left untouched.
+ *
+ * Types: q, k and v share in_dtype (FA_F32, FA_F16 or FA_BF16).  o is
+ * written in out_dtype, which is FA_F32 or in_dtype.  Scores, softmax
+ * statistics and accumulators are fp32; P is rounded to in_dtype (round to
+ * nearest even) for the P.V contraction; the normaliser is summed from the
+ * unrounded fp32 P.
+ *
+ * Supported: d in {64, 128}; B, Hq, Hkv, N >= 1; Hq % Hkv == 0; causal in
+ * {0, 1}; scale finite and > 0.  No dropout, no arbitrary mask.
+ *
+ * Ownership and threading: every pointer is a device pointer owned by the
+ * caller; the library allocates no device memory, keeps no per-call state,
+ * and never synchronises.  The work is enqueued on `stream` (a hipStream_t;
+ * NULL is the default stream) and fa_fwd returns at once.  Calls are
+ * thread-safe; calls on different streams may run concurrently.  o must not
+ * overlap q, k, v or lse.
+ *
+ * Errors: arguments are checked before anything is enqueued; on failure
+ * nothing is launched and a negative fa_status is returned.  Pointers q, k,
+ * v, o must be 16-byte aligned, lse and cu_seqlens 4-byte aligned.  A device
+ * that is not gfx950 gives FA_ERR_DEVICE; a launch failure gives
+ * FA_ERR_LAUNCH.  Corrupt cu_seqlens contents (decreasing offsets, a length
+ * above N, offsets past the buffers) are not detected: the caller must pass
+ * valid offsets.  Nothing is printed and no exception crosses the ABI.
+ */
+#ifndef FA_H
+#define FA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,     /* a required pointer is NULL */
+  FA_ERR_SHAPE = -2,    /* B, Hq, Hkv or N < 1, causal not 0/1, or size overflow */
+  FA_ERR_HEADDIM = -3,  /* d not in {64, 128} */
+  FA_ERR_GQA = -4,      /* Hq not a multiple of Hkv */
+  FA_ERR_DTYPE = -5,    /* unknown in_dtype, or out_dtype not in {FA_F32, in_dtype} */
+  FA_ERR_ALIGN = -6,    /* pointer misaligned */
+  FA_ERR_ALIAS = -7,    /* o overlaps q, k, v or lse */
+  FA_ERR_SCALE = -8,    /* scale not finite or not > 0 */
+  FA_ERR_DEVICE = -9,   /* current device is not gfx950, or no device */
+  FA_ERR_LAUNCH = -10   /* the kernel launch failed */
+} fa_status;
+
+/* Exact attention forward (see the header comment).  q, k, v: inputs in
+ * in_dtype; o: output in out_dtype; lse: float32 logsumexp; stream: a
+ * hipStream_t or NULL.  Returns FA_OK or a negative fa_status. */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+           const int* cu_seqlens, void* stream, int in_dtype, int out_dtype);
+
+/* The argument checks of fa_fwd alone: returns what fa_fwd would return
+ * before touching the device (FA_OK if it would go on to launch).  Makes no
+ * HIP call, so it is usable without a GPU. */
+int fa_fwd_check(const void* q, const void* k, const void* v, const void* o,
+                 const float* lse, int B, int Hq, int Hkv, int N, int d,
+                 int causal, float scale, const int* cu_seqlens,
+                 int in_dtype, int out_dtype);
+
+/* Name of the kernel fa_fwd launches for these settings, or NULL if they are
+ * unsupported.  Lets a caller confirm that this library, not a fallback, ran
+ * (the Kotaemon page's caveats recommend checking that the fast attention
+ * path is really active).  The string is static; do not free it. */
+const char* fa_kernel_name(int in_dtype, int d, int causal, int varlen,
+                           int out_dtype);
+
+/* 1 if fa_fwd supports (in_dtype, d, causal), else 0 — so a caller can pick
+ * another attention path when this one does not apply. */
+int fa_supported(int in_dtype, int d, int causal);
+
+/* Static description of a status code; never NULL. */
+const char* fa_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch (the Kotaemon page's
+ * caveats recommend pinning versions). */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

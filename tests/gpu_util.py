@@ -1,0 +1,67 @@
+"""Helpers for the GPU tests: upload seeded inputs, run the HIP path, compare
+with the oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import workloads
+
+# Bars on max |error| (O on the fp32-stored output, L natural log).
+O_TOL = {"fp32": 2e-3, "fp16": 2e-3, "bf16": 8e-3}
+L_TOL = 1e-3
+# fp32 inputs: the computation is fp32 throughout; far below the stated bars.
+FP32_STRICT = 1e-5
+
+
+def say(msg: str) -> None:
+    """Name the case before a GPU step, flushed, so a fault is attributable."""
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(arr: np.ndarray, dtype: str, dev):
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(dev)
+
+
+def torch_dtype(dtype: str):
+    import torch
+    return {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[dtype]
+
+
+def run_gpu(w: dict, *, out_dtype=None, lse_fill=None, dev="cuda:0"):
+    """Run the HIP path on inputs from workloads.make_*; returns (o, lse) as
+    float64 numpy arrays (o upcast from out_dtype)."""
+    import torch
+
+    import exact_io_aware_amd as fa
+    q, k, v = (to_device(w[x], w["dtype"], dev) for x in "qkv")
+    cu = None if w["cu_seqlens"] is None else torch.from_numpy(w["cu_seqlens"]).to(dev)
+    od = torch.float32 if out_dtype is None else out_dtype
+    lse = None
+    if lse_fill is not None:
+        B = w["B"]
+        lse = torch.full((B, w["Hq"], w["N"]), lse_fill, dtype=torch.float32, device=dev)
+    o, lse = fa.fwd(q, k, v, causal=w["causal"], scale=w["scale"], cu_seqlens=cu,
+                    max_seqlen=w["N"] if cu is not None else None, out_dtype=od, lse=lse)
+    torch.cuda.synchronize()
+    return o.double().cpu().numpy(), lse.double().cpu().numpy()
+
+
+def f64_inputs(w: dict):
+    return tuple(workloads.to_f64(w[x], w["dtype"]) for x in "qkv")
+
+
+def o_bar(dtype: str, out_dtype: str, ref: np.ndarray):
+    """Elementwise bar on O: the stated bar, plus the rounding of O itself when
+    it is stored in 16 bits (half an ulp of the reference value)."""
+    bar = O_TOL[dtype]
+    if out_dtype == "bf16":
+        return bar + np.abs(ref) * 2.0 ** -8
+    if out_dtype == "fp16":
+        return bar + np.abs(ref) * 2.0 ** -11
+    return bar

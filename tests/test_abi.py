@@ -1,0 +1,136 @@
+"""The C ABI without a GPU: the library loads, exports what include/fa.h
+declares, and rejects every bad argument before touching the device."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_io_aware_amd as fa
+from exact_io_aware_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert {"fa_fwd", "fa_fwd_check", "fa_kernel_name", "fa_supported",
+            "fa_status_string", "fa_version"} <= set(names)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fa.load()
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)$", out, re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
+
+
+def test_status_codes_match_header():
+    text = open(HEADER).read()
+    for name, value in _lib.STATUS.items():
+        assert re.search(rf"\b{name}\s*=\s*{value}\b", text), name
+    strings = {fa.status_string(v) for v in _lib.STATUS.values()}
+    assert len(strings) == len(_lib.STATUS)
+    assert fa.status_string(12345) == "unknown status"
+
+
+def test_version_and_support():
+    assert fa.version() == 10000
+    for dt in (fa.FA_F32, fa.FA_F16, fa.FA_BF16):
+        for d in (64, 128):
+            for c in (False, True):
+                assert fa.supported(dt, d, c)
+                for vl in (False, True):
+                    assert fa.kernel_name(dt, d, c, vl, fa.FA_F32) is not None
+                    if dt != fa.FA_F32:
+                        assert fa.kernel_name(dt, d, c, vl, dt) is not None
+    assert not fa.supported(fa.FA_BF16, 96, True)
+    assert not fa.supported(7, 128, True)
+    assert fa.kernel_name(fa.FA_BF16, 96, True, False, fa.FA_F32) is None
+    assert fa.kernel_name(fa.FA_F32, 64, False, False, fa.FA_BF16) is None
+
+
+# Fake, aligned, non-overlapping addresses: the checks never dereference them.
+BASE = dict(q=0x100000, k=0x200000, v=0x300000, o=0x400000, lse=0x500000,
+            B=2, Hq=8, Hkv=2, N=64, d=128, causal=1, scale=0.125, cu_seqlens=None,
+            in_dtype=fa.FA_BF16, out_dtype=fa.FA_F32)
+
+
+def check(**kw):
+    a = dict(BASE, **kw)
+    return _lib.fwd_check(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"],
+                          a["Hkv"], a["N"], a["d"], a["causal"], a["scale"],
+                          a["cu_seqlens"], a["in_dtype"], a["out_dtype"])
+
+
+S = _lib.STATUS
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, "FA_OK"),
+    ({"cu_seqlens": 0x600000}, "FA_OK"),
+    ({"in_dtype": fa.FA_F32}, "FA_OK"),
+    ({"out_dtype": fa.FA_BF16}, "FA_OK"),
+    ({"q": None}, "FA_ERR_NULL"), ({"k": None}, "FA_ERR_NULL"),
+    ({"v": None}, "FA_ERR_NULL"), ({"o": None}, "FA_ERR_NULL"),
+    ({"lse": None}, "FA_ERR_NULL"),
+    ({"B": 0}, "FA_ERR_SHAPE"), ({"Hq": 0}, "FA_ERR_SHAPE"), ({"Hkv": -1}, "FA_ERR_SHAPE"),
+    ({"N": 0}, "FA_ERR_SHAPE"), ({"causal": 2}, "FA_ERR_SHAPE"),
+    ({"B": 1 << 20, "N": 1 << 20, "Hq": 1 << 10, "Hkv": 1 << 10}, "FA_ERR_SHAPE"),
+    ({"d": 96}, "FA_ERR_HEADDIM"), ({"d": 0}, "FA_ERR_HEADDIM"), ({"d": 256}, "FA_ERR_HEADDIM"),
+    ({"Hq": 6, "Hkv": 4}, "FA_ERR_GQA"),
+    ({"in_dtype": 3}, "FA_ERR_DTYPE"), ({"in_dtype": -1}, "FA_ERR_DTYPE"),
+    ({"out_dtype": fa.FA_F16}, "FA_ERR_DTYPE"),
+    ({"in_dtype": fa.FA_F32, "out_dtype": fa.FA_BF16}, "FA_ERR_DTYPE"),
+    ({"scale": float("nan")}, "FA_ERR_SCALE"), ({"scale": float("inf")}, "FA_ERR_SCALE"),
+    ({"scale": 0.0}, "FA_ERR_SCALE"), ({"scale": -0.1}, "FA_ERR_SCALE"),
+    ({"q": 0x100008}, "FA_ERR_ALIGN"), ({"o": 0x400004}, "FA_ERR_ALIGN"),
+    ({"lse": 0x500002}, "FA_ERR_ALIGN"), ({"cu_seqlens": 0x600001}, "FA_ERR_ALIGN"),
+    ({"o": 0x100000}, "FA_ERR_ALIAS"),
+    ({"o": 0x300000 + 4096}, "FA_ERR_ALIAS"),           # inside v
+    ({"o": 0x500000 - 16}, "FA_ERR_ALIAS"),             # runs into lse
+    ({"o": 0x200000, "cu_seqlens": 0x600000}, "FA_ERR_ALIAS"),
+])
+def test_argument_checks(kw, code):
+    assert check(**kw) == S[code]
+
+
+def test_fwd_rejects_before_any_device_call():
+    # fa_fwd runs the same checks first: bad arguments never reach HIP.
+    for kw, code in [({"q": None}, "FA_ERR_NULL"), ({"d": 96}, "FA_ERR_HEADDIM"),
+                     ({"scale": -1.0}, "FA_ERR_SCALE"), ({"o": 0x100000}, "FA_ERR_ALIAS")]:
+        a = dict(BASE, **kw)
+        st = _lib.fwd_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"],
+                          a["Hkv"], a["N"], a["d"], a["causal"], a["scale"], None, None,
+                          a["in_dtype"], a["out_dtype"])
+        assert st == S[code]
+
+
+def test_python_front_end_validates():
+    import torch
+    q = torch.zeros(1, 2, 8, 64)
+    with pytest.raises(ValueError):
+        fa.fwd(q, q, q)            # host tensors are refused, nothing falls back
+    with pytest.raises(ValueError):
+        fa.fwd(q, q.half(), q)
+
+
+def test_flops_convention():
+    assert fa.flops(1, 2, [3], causal=False) == 4 * 2 * 9
+    assert fa.flops(2, 4, [3, 1], causal=True) == 4 * 4 * 2 * (6 + 1)
+    from workloads import WORKLOADS
+    w = WORKLOADS["gqa_bf16"]
+    assert abs(fa.flops(w.Hq, w.d, [w.N] * w.B, True) - 5.50e11) / 5.50e11 < 0.01
