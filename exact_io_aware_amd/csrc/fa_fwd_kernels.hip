@@ -110,6 +110,39 @@ __device__ __forceinline__ float wave_swap_halves(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// Combine a value with the one held by lane l ^ 32 (v_permlane32_swap: the
+// two results hold, in every lane, the values of lanes l and l ^ 32).
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Buffer resource over `bytes` bytes from `base`: loads at offsets >= bytes
+// return zeros, so ragged tails need no clamping.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One 16-byte-per-lane buffer load straight into LDS: lane L's bytes land at
+// lds_dst + 16 * L (lds_dst is wave-uniform).  The host pass of hipcc drops
+// any kernel that names this builtin, so its body is compiled for the device
+// pass only (the host pass never runs device code).
+__device__ __forceinline__ void lds_load16(rsrc_t r, char* lds_dst, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 16, voff, 0, 0, 0);
+#else
+  (void)r; (void)lds_dst; (void)voff;
+#endif
+}
+
 // LDS byte offset of 16-byte chunk c of tile row r.
 //  K tiles: chunk ^ (row % 8) — the 8 rows read together by one
 //  ds_read_b128 phase hit 8 different bank groups.
@@ -138,10 +171,16 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_mfma(FwdParams p) {
   constexpr int LOADS = BC * CPR / 256;      // 16-byte loads per thread per tile
   constexpr int TILE_BYTES = BC * D * 2;
 
-  __shared__ __attribute__((aligned(16))) char smem[2][2][TILE_BYTES];
+  // Two LDS buffers per operand, as separate objects so that reads of one
+  // are known not to alias the direct-to-LDS loads landing in the other.
+  __shared__ __attribute__((aligned(16))) char k_lds0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char k_lds1[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char v_lds0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char v_lds1[TILE_BYTES];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hf = lane >> 5;
 
   // a1: workgroup -> (sequence b, head group, row block).
@@ -174,158 +213,163 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_mfma(FwdParams p) {
                           (long long)h * p.q_hs;
   const long long kvbase = (VARLEN ? (long long)seq0 * p.kv_rs : (long long)b * p.kv_bs) +
                            (long long)kvh * p.kv_hs;
-  const T* __restrict__ qp = (const T*)p.q + qbase;
-  const char* __restrict__ kp = (const char*)((const T*)p.k + kvbase);
-  const char* __restrict__ vp = (const char*)((const T*)p.v + kvbase);
-  const long long kv_rs_bytes = p.kv_rs * 2;
+  const char* kp = (const char*)((const T*)p.k + kvbase);
+  const char* vp = (const char*)((const T*)p.v + kvbase);
+  const uint32_t kv_rs_bytes = (uint32_t)p.kv_rs * 2;
+
+  // a3: tile loads go straight from memory into LDS (buffer_load ... lds):
+  // lane L of wave w in load i fills 16-byte LDS chunk p = 256*i + 64*w + L of
+  // the tile, i.e. row p / CPR, stored chunk p % CPR, which holds the row's
+  // chunk (p % CPR) ^ swizzle(row).  Rows past the sequence end read zeros.
+  uint32_t koff[LOADS], voff[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int pch = tid + 256 * i;
+    const int r = pch / CPR, pc = pch % CPR;
+    koff[i] = r * kv_rs_bytes + ((pc ^ (r & 7)) << 4);
+    voff[i] = r * kv_rs_bytes + ((pc ^ ((r & 3) << 1)) << 4);
+  }
+  auto gload = [&](int tile, char* kdst, char* vdst) {
+    const int kb = tile * BC;
+    const long long off = (long long)kb * kv_rs_bytes;
+    const uint32_t bytes = (uint32_t)min(len - kb, BC) * kv_rs_bytes;
+    const rsrc_t rk = make_rsrc(kp + off, bytes), rv = make_rsrc(vp + off, bytes);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int dst = (256 * i + 64 * wave) * 16;
+      lds_load16(rk, kdst + dst, koff[i]);
+      lds_load16(rv, vdst + dst, voff[i]);
+    }
+  };
+
+  gload(0, k_lds0, v_lds0);
 
   // a2: this wave's Q rows as MFMA B operands (d-chunk dc, 8 values per lane:
-  // Q[row0 + l32][16*dc + 8*hf .. +7]).  Rows past the end are clamped; their
+  // Q[row0 + l32][16*dc + 8*hf .. +7]).  Rows past the end read zeros; their
   // results are never stored.
   vec8 qf[DC];
   {
-    const int qr = min(row0 + l32, len - 1);
-    const T* src = qp + (long long)qr * p.q_rs + hf * 8;
+    const int qrows = active ? min(32, len - row0) : 0;
+    const rsrc_t rq = make_rsrc((const T*)p.q + qbase + (long long)(active ? row0 : 0) * p.q_rs,
+                                (uint32_t)qrows * (uint32_t)p.q_rs * 2);
+    const uint32_t qo = (uint32_t)(l32 * p.q_rs + hf * 8) * 2;
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc) qf[dc] = *(const vec8*)(src + dc * 16);
+    for (int dc = 0; dc < DC; ++dc)
+      qf[dc] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(rq, qo + dc * 32, 0, 0));
   }
-
-  // a3: tile loads.  Thread t moves 16-byte chunks t, t+256, ... of the
-  // BC x D tile of K and of V (row-major).  Key rows past the end are
-  // clamped to the last row (finite values; their scores are masked).
-  u32x4 kreg[LOADS], vreg[LOADS];
-  auto gload = [&](int tile) {
-    const int kb = tile * BC;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int cid = tid + 256 * i;
-      const int r = cid / CPR, c = cid % CPR;
-      const long long off = (long long)min(kb + r, len - 1) * kv_rs_bytes + c * 16;
-      kreg[i] = *(const u32x4*)(kp + off);
-      vreg[i] = *(const u32x4*)(vp + off);
-    }
-  };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int cid = tid + 256 * i;
-      const int r = cid / CPR, c = cid % CPR;
-      *(u32x4*)(&smem[buf][0][k_off<D>(r, c)]) = kreg[i];
-      *(u32x4*)(&smem[buf][1][v_off<D>(r, c)]) = vreg[i];
-    }
-  };
 
   f32x16 oacc[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
   float m_run = -__builtin_inff();  // running max of scaled scores (log2 units)
   float ell = 0.0f;                 // this lane's part of the row sum
-
   const int qrow = row0 + l32;      // query index of this lane
 
-  gload(0);
-  swrite(0);
-  __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntiles) gload(j + 1);
-
-    if (j < wave_ntiles) {
-      const int kb = j * BC;
-      const char* ks = smem[buf][0];
-      const char* vs = smem[buf][1];
-
-      // a4: S^T = K Q^T, block nb covers keys kb + 32*nb .. +31.
-      f32x16 s[NB];
+  auto compute = [&](int j, const char* ks, const char* vs) {
+    const int kb = j * BC;
+    // a4: S^T = K Q^T, block nb covers keys kb + 32*nb .. +31.
+    f32x16 s[NB];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        s[nb] = f32x16{};
-        const int kr = 32 * nb + l32;
+    for (int nb = 0; nb < NB; ++nb) {
+      s[nb] = f32x16{};
+      const int kr = 32 * nb + l32;
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc) {
-          const vec8 kf = *(const vec8*)(ks + k_off<D>(kr, 2 * dc + hf));
-          s[nb] = Ops<T>::mfma(kf, qf[dc], s[nb]);
-        }
-      }
-
-      // a5: masks, only on tiles that cross the diagonal or the end.
-      const bool need_mask = (CAUSAL && kb + BC - 1 > row0) || (kb + BC > len);
-      if (need_mask) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kb + 32 * nb + 8 * (i >> 2) + 4 * hf + (i & 3);
-            const bool dead = (CAUSAL && key > qrow) || key >= len;
-            if (dead) s[nb][i] = -__builtin_inff();
-          }
-      }
-
-      // a6: online softmax.
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[nb][i]);
-      mx = fmaxf(mx, wave_swap_halves(mx));
-      const float mt = mx * p.scale_log2;
-      if (__any(mt > m_run + kRescaleSlack)) {
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
-        ell *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-        m_run = m_new;
-      }
-      const float neg_m = -m_run;
-      uint32_t pk[NB][8];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][i], p.scale_log2, neg_m));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][i + 1], p.scale_log2, neg_m));
-          ell += p0 + p1;
-          pk[nb][i >> 1] = Ops<T>::pack(p0, p1);
-        }
-
-      // a7: O^T += V^T P^T over the 16-key chunks of the tile.
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const int nb = kc >> 1, half = kc & 1;
-        u32x4 pb = {pk[nb][4 * half + 0], pk[nb][4 * half + 1],
-                    pk[nb][4 * half + 2], pk[nb][4 * half + 3]};
-        const vec8 pf = __builtin_bit_cast(vec8, pb);
-        // Transposed reads: lane i of each 16-lane group receives, for its
-        // output column d, the 4 keys held by lanes 4e + i/4 (e = 0..3).
-        const int g = lane >> 4, li = lane & 15;
-        const int vr0 = kc * 16 + 4 * hf + (li >> 2);   // first 4-key group
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int dcol = 32 * db + 16 * (g & 1) + 4 * (li & 3);
-          const int c = dcol >> 3, within = (dcol & 7) * 2;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(vs + v_off<D>(vr0, c) + within));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(vs + v_off<D>(vr0 + 8, c) + within));
-          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-          u32x4 vv = {lo2[0], lo2[1], hi2[0], hi2[1]};
-          oacc[db] = Ops<T>::mfma(__builtin_bit_cast(vec8, vv), pf, oacc[db]);
-        }
+      for (int dc = 0; dc < DC; ++dc) {
+        const vec8 kf = *(const vec8*)(ks + k_off<D>(kr, 2 * dc + hf));
+        s[nb] = Ops<T>::mfma(kf, qf[dc], s[nb]);
       }
     }
 
-    if (j + 1 < ntiles) swrite(buf ^ 1);
+    // a5: masks, only on tiles that cross the diagonal or the end.
+    const bool need_mask = (CAUSAL && kb + BC - 1 > row0) || (kb + BC > len);
+    if (need_mask) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kb + 32 * nb + 8 * (i >> 2) + 4 * hf + (i & 3);
+          const bool dead = (CAUSAL && key > qrow) || key >= len;
+          if (dead) s[nb][i] = -__builtin_inff();
+        }
+    }
+
+    // a6: online softmax.
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[nb][i]);
+    mx = halves_max(mx);
+    const float mt = mx * p.scale_log2;
+    if (__any(mt > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
+      ell *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = -m_run;
+    uint32_t pk[NB][8];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][i], p.scale_log2, neg_m));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][i + 1], p.scale_log2, neg_m));
+        ell += p0 + p1;
+        pk[nb][i >> 1] = Ops<T>::pack(p0, p1);
+      }
+
+    // a7: O^T += V^T P^T over the 16-key chunks of the tile.
+    const int g = lane >> 4, li = lane & 15;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const int nb = kc >> 1, half = kc & 1;
+      u32x4 pb = {pk[nb][4 * half + 0], pk[nb][4 * half + 1],
+                  pk[nb][4 * half + 2], pk[nb][4 * half + 3]};
+      const vec8 pf = __builtin_bit_cast(vec8, pb);
+      // Transposed reads: lane i of each 16-lane group receives, for its
+      // output column d, the 4 keys held by lanes 4e + i/4 (e = 0..3).
+      const int vr0 = kc * 16 + 4 * hf + (li >> 2);   // first 4-key group
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int dcol = 32 * db + 16 * (g & 1) + 4 * (li & 3);
+        const int c = dcol >> 3, within = (dcol & 7) * 2;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vs + v_off<D>(vr0, c) + within));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vs + v_off<D>(vr0 + 8, c) + within));
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+        u32x4 vv = {lo2[0], lo2[1], hi2[0], hi2[1]};
+        oacc[db] = Ops<T>::mfma(__builtin_bit_cast(vec8, vv), pf, oacc[db]);
+      }
+    }
+  };
+
+  // Main loop, unrolled by two so each step's buffers are fixed: step j reads
+  // buffer j % 2 while tile j + 1 streams into the other one.  One barrier per
+  // tile: it follows both this step's reads and the wait for the next tile.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile 0 and Q have landed
+  __syncthreads();
+  for (int j = 0; j < ntiles; j += 2) {
+    if (j + 1 < ntiles) gload(j + 1, k_lds1, v_lds1);
+    if (j < wave_ntiles) compute(j, k_lds0, v_lds0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (j + 1 >= ntiles) break;
+    if (j + 2 < ntiles) gload(j + 2, k_lds0, v_lds0);
+    if (j + 1 < wave_ntiles) compute(j + 1, k_lds1, v_lds1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
 
   if (!active) return;
 
   // a8: epilogue.  O = acc / ell, L = (m + log2 ell) * ln 2.
-  const float ell_t = ell + wave_swap_halves(ell);
+  const float ell_t = halves_sum(ell);
   const float inv = 1.0f / ell_t;
   if (qrow < len) {
     const long long orow = qbase + (long long)qrow * p.q_rs;

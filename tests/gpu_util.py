@@ -65,3 +65,18 @@ def o_bar(dtype: str, out_dtype: str, ref: np.ndarray):
     if out_dtype == "fp16":
         return bar + np.abs(ref) * 2.0 ** -11
     return bar
+
+
+def o_bar_derived(dtype: str, abs_weighted: np.ndarray):
+    """Bar for inputs outside the five workloads (e.g. very peaked softmax).
+
+    The kernel rounds P to the input precision for the P.V contraction, so
+    |dO_rj| <= u * sum_c P_rc |V_cj| / l_r, with u the unit roundoff (2^-8
+    bf16, 2^-11 fp16, 0 for fp32 where P stays fp32); ``abs_weighted`` is that
+    weighted sum, i.e. the oracle's output for values |V|.  1e-3 is added for
+    the fp32 score, exp2 and accumulation errors at large score magnitudes.
+    The stated bar still applies wherever it is larger.
+    """
+    u = {"bf16": 2.0 ** -8, "fp16": 2.0 ** -11, "fp32": 0.0}[dtype]
+    return np.maximum(O_TOL[dtype], u * abs_weighted + 1e-3)
+
