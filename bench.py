@@ -38,6 +38,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=64,
                     help="query heads (from the first sequences) the oracle is timed on")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB "
+                         "(reads and writes that many bytes once), to scale memory "
+                         "counters such as FETCH_SIZE / WRITE_SIZE")
     return ap.parse_args()
 
 
@@ -161,6 +165,14 @@ def main():
         "timing": {"launch_ms_min": round(min(per), 4), "launch_ms_median":
                    round(sorted(per)[len(per) // 2], 4), "wall_s": round(wall, 4)},
     }
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["copy_calibration_bytes"] = n * 4
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_heads)
     print(json.dumps(rec), flush=True)

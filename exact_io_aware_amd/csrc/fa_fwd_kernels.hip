@@ -62,9 +62,12 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-// Largest increase of a row maximum (log2 units) tolerated before the
-// running maximum is moved and the accumulators rescaled.
-constexpr float kRescaleSlack = 8.0f;
+// Largest partial row sum of P tolerated before the running maximum is
+// moved and the accumulators rescaled: every P is then <= 2^15, inside the
+// fp16 range, and the sums stay far from fp32 overflow.
+constexpr float kSumLimit = 32768.0f;
+// Immediate of s_waitcnt vmcnt(n) with the other counters left alone.
+constexpr int waitcnt_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 struct FwdParams {
   const void* q; const void* k; const void* v; void* o; float* lse;
@@ -105,11 +108,6 @@ template <> struct Ops<_Float16> {
   }
 };
 
-__device__ __forceinline__ float wave_swap_halves(float x) {
-  // value of lane l ^ 32
-  return __shfl_xor(x, 32, 64);
-}
-
 // Combine a value with the one held by lane l ^ 32 (v_permlane32_swap: the
 // two results hold, in every lane, the values of lanes l and l ^ 32).
 __device__ __forceinline__ float halves_max(float x) {
@@ -143,33 +141,49 @@ __device__ __forceinline__ void lds_load16(rsrc_t r, char* lds_dst, uint32_t vof
 #endif
 }
 
-// LDS byte offset of 16-byte chunk c of tile row r.
-//  K tiles: chunk ^ (row % 8) — the 8 rows read together by one
-//  ds_read_b128 phase hit 8 different bank groups.
-//  V tiles: chunk ^ 2*(row % 4) — the 4 rows x 32 bytes read together by a
-//  16-lane group of ds_read_b64_tr_b16 hit 8 different bank groups.
+// LDS tile layouts.  A tile is BC rows (keys) x D columns of 16-bit values,
+// row-major (2*D bytes per row), cut into 16-byte chunks.  gfx950 LDS serves
+// 256 bytes per cycle (64 four-byte banks): a ds_read_b128 takes 16 lanes per
+// cycle and a ds_read_b64_tr_b16 32 lanes.  Chunk c of row r is stored at
+// chunk position c ^ swizzle(r), chosen so that those lane groups always
+// touch 16 different 16-byte bank groups:
+//  K (lanes read one chunk of 16 consecutive rows):
+//    D = 128: c ^ (r % 16);          D = 64: c ^ ((r / 2) % 8)
+//  V (32 lanes read 4 consecutive chunks of 4 consecutive rows):
+//    D = 128: c ^ 4 * (r % 4);       D = 64: c ^ 4 * ((r / 2) % 2)
+template <bool B> struct BoolTag { static constexpr bool value = B; };
+
 template <int D>
-__device__ __forceinline__ int k_off(int r, int c) {
-  return r * (D * 2) + ((c ^ (r & 7)) << 4);
+__device__ __forceinline__ int k_swz(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
 }
 template <int D>
-__device__ __forceinline__ int v_off(int r, int c) {
-  return r * (D * 2) + ((c ^ ((r & 3) << 1)) << 4);
+__device__ __forceinline__ int v_swz(int r) {
+  return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
 }
 
 // ---------------------------------------------------------------------------
 // 16-bit (bf16 / fp16) inputs: MFMA kernel.
+//
+// Each wave owns QB blocks of 32 query rows of one head; every K or V operand
+// it reads from LDS feeds the MFMAs of all QB blocks.  Keys are processed in
+// 32-key blocks; K/V tiles of 64 keys (two blocks) are double-buffered in LDS.
+// Step i of a wave masks block i if needed, issues the MFMAs of block i+1's
+// scores, forms block i's probabilities (independent work, so the matrix
+// cores and the vector ALUs overlap), then accumulates P.V of block i.
 template <typename T, int D, bool CAUSAL, bool VARLEN, bool OUT_F32>
 __global__ __launch_bounds__(256, 2) void fa_fwd_mfma(FwdParams p) {
   using vec8 = typename Ops<T>::vec8;
-  constexpr int BC = (D == 128) ? 64 : 128;  // keys per K/V tile
-  constexpr int NB = BC / 32;                // 32-key score blocks per tile
-  constexpr int KC = BC / 16;                // 16-key chunks (P.V k-steps)
+  constexpr int QB = rows_per_wave(FA_BF16) / 32;  // 32-row query blocks per wave
+  constexpr int WR = 32 * QB;                // query rows per wave
+  constexpr int BC = 64;                     // keys per K/V tile (two 32-key blocks)
   constexpr int DB = D / 32;                 // 32-wide blocks of the output
   constexpr int DC = D / 16;                 // 16-wide chunks of Q.K
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int RB = D * 2;                  // bytes per tile row
   constexpr int LOADS = BC * CPR / 256;      // 16-byte loads per thread per tile
-  constexpr int TILE_BYTES = BC * D * 2;
+  constexpr int TILE_BYTES = BC * RB;
+  constexpr int HALF = 32 * RB;              // bytes of one 32-key block in a tile
 
   // Two LDS buffers per operand, as separate objects so that reads of one
   // are known not to alias the direct-to-LDS loads landing in the other.
@@ -201,13 +215,12 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_mfma(FwdParams p) {
   }
   const int wg_row0 = rb * p.rows_per_wg;
   if (wg_row0 >= len) return;                 // uniform over the workgroup
-  const int row0 = wg_row0 + (wave / p.hp) * 32;
+  const int row0 = wg_row0 + (wave / p.hp) * WR;
   const int wg_rows_end = min(wg_row0 + p.rows_per_wg, len);
   const int kv_end = CAUSAL ? wg_rows_end : len;
-  const int ntiles = (kv_end + BC - 1) / BC;
   const bool active = row0 < len;
-  const int wave_kv_end = CAUSAL ? min(row0 + 32, len) : len;
-  const int wave_ntiles = active ? (wave_kv_end + BC - 1) / BC : 0;
+  const int wave_kv_end = CAUSAL ? min(row0 + WR, len) : len;
+  const int wave_nblk = active ? (wave_kv_end + 31) / 32 : 0;  // blocks this wave needs
 
   const long long qbase = (VARLEN ? (long long)seq0 * p.q_rs : (long long)b * p.q_bs) +
                           (long long)h * p.q_hs;
@@ -218,178 +231,282 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_mfma(FwdParams p) {
   const uint32_t kv_rs_bytes = (uint32_t)p.kv_rs * 2;
 
   // a3: tile loads go straight from memory into LDS (buffer_load ... lds):
-  // lane L of wave w in load i fills 16-byte LDS chunk p = 256*i + 64*w + L of
-  // the tile, i.e. row p / CPR, stored chunk p % CPR, which holds the row's
-  // chunk (p % CPR) ^ swizzle(row).  Rows past the sequence end read zeros.
+  // lane L of wave w in load i fills 16-byte LDS chunk position
+  // q = 256*i + 64*w + L of the tile, i.e. row q / CPR, position q % CPR,
+  // which holds the row's chunk (q % CPR) ^ swizzle(row).  Rows past the
+  // sequence end (and whole tiles past it) read zeros.
   uint32_t koff[LOADS], voff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int pch = tid + 256 * i;
     const int r = pch / CPR, pc = pch % CPR;
-    koff[i] = r * kv_rs_bytes + ((pc ^ (r & 7)) << 4);
-    voff[i] = r * kv_rs_bytes + ((pc ^ ((r & 3) << 1)) << 4);
+    koff[i] = r * kv_rs_bytes + ((pc ^ k_swz<D>(r)) << 4);
+    voff[i] = r * kv_rs_bytes + ((pc ^ v_swz<D>(r)) << 4);
   }
-  auto gload = [&](int tile, char* kdst, char* vdst) {
+  auto gload = [&](const char* src, const uint32_t (&off)[LOADS], int tile, char* dst_base)
+      __attribute__((always_inline)) {
     const int kb = tile * BC;
-    const long long off = (long long)kb * kv_rs_bytes;
-    const uint32_t bytes = (uint32_t)min(len - kb, BC) * kv_rs_bytes;
-    const rsrc_t rk = make_rsrc(kp + off, bytes), rv = make_rsrc(vp + off, bytes);
+    // readfirstlane keeps the clamp (a VALU med3) in a scalar register: the
+    // resource of a buffer load must be wave-uniform.
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(len - kb, BC)));
+    const rsrc_t r = make_rsrc(src + (long long)min(kb, len) * kv_rs_bytes,
+                               (uint32_t)rows * kv_rs_bytes);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int dst = (256 * i + 64 * wave) * 16;
-      lds_load16(rk, kdst + dst, koff[i]);
-      lds_load16(rv, vdst + dst, voff[i]);
-    }
+    for (int i = 0; i < LOADS; ++i) lds_load16(r, dst_base + (256 * i + 64 * wave) * 16, off[i]);
   };
 
-  gload(0, k_lds0, v_lds0);
+  // Prologue loads: K_0, K_1 and V_0 (K runs ahead of V).
+  gload(kp, koff, 0, k_lds0);
+  gload(vp, voff, 0, v_lds0);
+  gload(kp, koff, 1, k_lds1);
 
-  // a2: this wave's Q rows as MFMA B operands (d-chunk dc, 8 values per lane:
-  // Q[row0 + l32][16*dc + 8*hf .. +7]).  Rows past the end read zeros; their
-  // results are never stored.
-  vec8 qf[DC];
+  // a2: this wave's Q rows as MFMA B operands (query block qb, d-chunk dc,
+  // 8 values per lane: Q[row0 + 32*qb + l32][16*dc + 8*hf .. +7]).  Rows past
+  // the end read zeros; their results are never stored.
+  vec8 qf[QB][DC];
   {
-    const int qrows = active ? min(32, len - row0) : 0;
+    const int qrows = __builtin_amdgcn_readfirstlane(active ? min(WR, len - row0) : 0);
     const rsrc_t rq = make_rsrc((const T*)p.q + qbase + (long long)(active ? row0 : 0) * p.q_rs,
                                 (uint32_t)qrows * (uint32_t)p.q_rs * 2);
-    const uint32_t qo = (uint32_t)(l32 * p.q_rs + hf * 8) * 2;
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc)
-      qf[dc] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(rq, qo + dc * 32, 0, 0));
+    for (int qb = 0; qb < QB; ++qb) {
+      const uint32_t qo = (uint32_t)((32 * qb + l32) * p.q_rs + hf * 8) * 2;
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+        qf[qb][dc] = __builtin_bit_cast(
+            vec8, __builtin_amdgcn_raw_buffer_load_b128(rq, qo + dc * 32, 0, 0));
+    }
   }
 
-  f32x16 oacc[DB];
+  // Per-lane LDS byte offsets of the MFMA operand reads; everything else in
+  // those addresses is a compile-time constant (an instruction offset).
+  //  K (A operand of S^T = K Q^T): block row l32, chunk 2*dc + hf.
+  int kaddr[DC];
 #pragma unroll
-  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
-  float m_run = -__builtin_inff();  // running max of scaled scores (log2 units)
-  float ell = 0.0f;                 // this lane's part of the row sum
-  const int qrow = row0 + l32;      // query index of this lane
-
-  auto compute = [&](int j, const char* ks, const char* vs) {
-    const int kb = j * BC;
-    // a4: S^T = K Q^T, block nb covers keys kb + 32*nb .. +31.
-    f32x16 s[NB];
+  for (int dc = 0; dc < DC; ++dc) kaddr[dc] = l32 * RB + (((2 * dc + hf) ^ k_swz<D>(l32)) << 4);
+  //  V (A operand of O^T = V^T P^T, transposed read): for 16-key chunk kc,
+  //  half e (keys +0 / +8) and output block db, lane (g = lane/16, i = lane%16)
+  //  points at row 16*kc + 8*e + 4*hf + i/4, columns 32*db + 16*(g%2) + 4*(i%4)
+  //  .. +3.  Lane i of each 16-lane group then receives, for its column, the 4
+  //  keys held by lanes 4*t + i/4 (t = 0..3): the keys of P^T's B-operand
+  //  layout (0-3, 8-11 in lanes 0-31; 4-7, 12-15 in lanes 32-63).
+  int vaddr[DB];
+  {
+    const int g = lane >> 4, li = lane & 15;
+    const int vr = 4 * hf + (li >> 2);   // row within the 16-key chunk (+8 for e = 1)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      s[nb] = f32x16{};
-      const int kr = 32 * nb + l32;
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-        const vec8 kf = *(const vec8*)(ks + k_off<D>(kr, 2 * dc + hf));
-        s[nb] = Ops<T>::mfma(kf, qf[dc], s[nb]);
-      }
+    for (int db = 0; db < DB; ++db) {
+      const int dcol = 32 * db + 16 * (g & 1) + 4 * (li & 3);
+      vaddr[db] = vr * RB + (((dcol >> 3) ^ v_swz<D>(vr)) << 4) + (dcol & 7) * 2;
     }
+  }
 
-    // a5: masks, only on tiles that cross the diagonal or the end.
-    const bool need_mask = (CAUSAL && kb + BC - 1 > row0) || (kb + BC > len);
-    if (need_mask) {
+  f32x16 oacc[QB][DB];
+  float m_run[QB], ell[QB];         // reference maximum (log2 units), partial row sum
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+  for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kb + 32 * nb + 8 * (i >> 2) + 4 * hf + (i & 3);
-          const bool dead = (CAUSAL && key > qrow) || key >= len;
-          if (dead) s[nb][i] = -__builtin_inff();
+    for (int i = 0; i < DB; ++i) oacc[qb][i] = f32x16{};
+    m_run[qb] = -__builtin_inff();
+    ell[qb] = 0.0f;
+  }
+  const float sl2 = p.scale_log2;
+
+  // a4: S^T = K Q^T for one 32-key block (rows of `ks`), every query block.
+  auto qk = [&](const char* ks, f32x16 (&s)[QB]) __attribute__((always_inline)) {
+    vec8 kf[DC];
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) kf[dc] = *(const vec8*)(ks + kaddr[dc]);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[qb] = Ops<T>::mfma(kf[dc], qf[qb][dc], s[qb]);
+  };
+
+  // a5: masks of block i (keys 32i .. 32i+31), only where it crosses the
+  // diagonal or the end of the sequence.
+  auto mask = [&](int i, f32x16 (&s)[QB]) __attribute__((always_inline)) {
+    const int kb = i * 32;
+    if ((CAUSAL && kb + 31 > row0) || (kb + 32 > len)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kb + 8 * (e >> 2) + 4 * hf + (e & 3);
+          if ((CAUSAL && key > row0 + 32 * qb + l32) || key >= len) s[qb][e] = -__builtin_inff();
         }
     }
+  };
 
-    // a6: online softmax.
-    float mx = -__builtin_inff();
+  // a6: online softmax of one block.  P is formed against the reference
+  // maximum m (form_p); if a lane's partial sum leaves [0, 2^15] (a score far
+  // above m, or the first block, where m = -inf), m moves to the true running
+  // maximum, O and ell are rescaled by exp2(m_old - m_new) and P is formed
+  // again (settle).  The rescale is exact, so the result does not depend on
+  // when m moves.
+  auto form_p = [&](const f32x16 (&s)[QB], uint32_t (&pk)[QB][8], float (&lsum)[QB],
+                    bool live) __attribute__((always_inline)) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int qb = 0; qb < QB; ++qb) {
+      // A block past the wave's last one gets m = +inf: P = 0 and sum 0.
+      const float m = live ? m_run[qb] : __builtin_inff();
+      float acc = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[nb][i]);
-    mx = halves_max(mx);
-    const float mt = mx * p.scale_log2;
-    if (__any(mt > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
-      ell *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-      m_run = m_new;
-    }
-    const float neg_m = -m_run;
-    uint32_t pk[NB][8];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][i], p.scale_log2, neg_m));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][i + 1], p.scale_log2, neg_m));
-        ell += p0 + p1;
-        pk[nb][i >> 1] = Ops<T>::pack(p0, p1);
+      for (int e = 0; e < 16; e += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][e], sl2, -m));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][e + 1], sl2, -m));
+        acc += p0 + p1;
+        pk[qb][e >> 1] = Ops<T>::pack(p0, p1);
       }
-
-    // a7: O^T += V^T P^T over the 16-key chunks of the tile.
-    const int g = lane >> 4, li = lane & 15;
+      lsum[qb] = acc;
+    }
+  };
+  auto settle = [&](const f32x16 (&s)[QB], uint32_t (&pk)[QB][8], float (&lsum)[QB])
+      __attribute__((always_inline)) {
+    bool ok = true;
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      const int nb = kc >> 1, half = kc & 1;
-      u32x4 pb = {pk[nb][4 * half + 0], pk[nb][4 * half + 1],
-                  pk[nb][4 * half + 2], pk[nb][4 * half + 3]};
-      const vec8 pf = __builtin_bit_cast(vec8, pb);
-      // Transposed reads: lane i of each 16-lane group receives, for its
-      // output column d, the 4 keys held by lanes 4e + i/4 (e = 0..3).
-      const int vr0 = kc * 16 + 4 * hf + (li >> 2);   // first 4-key group
+    for (int qb = 0; qb < QB; ++qb) ok = ok && (lsum[qb] <= kSumLimit);
+    if (__any(!ok)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[qb][e]);
+        // -inf only for rows with no visible key yet, which keep m = -inf.
+        const float m_new = fmaxf(m_run[qb], halves_max(mx) * sl2);
+        const float alpha = m_new == m_run[qb] ? 1.0f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        ell[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[qb][db][e] *= alpha;
+        m_run[qb] = m_new;
+      }
+      form_p(s, pk, lsum, true);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) ell[qb] += lsum[qb];
+  };
+
+  // a7: O^T += V^T P^T over the two 16-key chunks of one block (V rows at vs).
+  auto pv = [&](const char* vs, const uint32_t (&pk)[QB][8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      vec8 pf[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        u32x4 pb = {pk[qb][4 * kc + 0], pk[qb][4 * kc + 1], pk[qb][4 * kc + 2], pk[qb][4 * kc + 3]};
+        pf[qb] = __builtin_bit_cast(vec8, pb);
+      }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int dcol = 32 * db + 16 * (g & 1) + 4 * (li & 3);
-        const int c = dcol >> 3, within = (dcol & 7) * 2;
+        const char* va = vs + vaddr[db] + kc * 16 * RB;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(vs + v_off<D>(vr0, c) + within));
+            (__attribute__((address_space(3))) s16x4*)(va));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(vs + v_off<D>(vr0 + 8, c) + within));
+            (__attribute__((address_space(3))) s16x4*)(va + 8 * RB));
         const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-        u32x4 vv = {lo2[0], lo2[1], hi2[0], hi2[1]};
-        oacc[db] = Ops<T>::mfma(__builtin_bit_cast(vec8, vv), pf, oacc[db]);
+        const u32x4 vv = {lo2[0], lo2[1], hi2[0], hi2[1]};
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          oacc[qb][db] = Ops<T>::mfma(__builtin_bit_cast(vec8, vv), pf[qb], oacc[qb][db]);
       }
     }
   };
 
-  // Main loop, unrolled by two so each step's buffers are fixed: step j reads
-  // buffer j % 2 while tile j + 1 streams into the other one.  One barrier per
-  // tile: it follows both this step's reads and the wait for the next tile.
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile 0 and Q have landed
+  // Step s of the three-stage pipeline: scores of block s+1 (MFMA), softmax
+  // of block s (VALU) and P.V of block s-1 (MFMA) are independent, so they
+  // are issued together and the matrix cores and vector ALUs overlap.  The
+  // same straight-line code serves every step: past a wave's last block its
+  // P is zero (and its scores, reads of loaded or zero-filled LDS, unused),
+  // so the step after the last one just drains P.V.
+  auto step = [&](int st, f32x16 (&s_cur)[QB], f32x16 (&s_nxt)[QB], uint32_t (&pk_cur)[QB][8],
+                  const uint32_t (&pk_prev)[QB][8], const char* ks_nxt, const char* vs_prev)
+      __attribute__((always_inline)) {
+    const bool live = st < wave_nblk;
+    mask(st, s_cur);
+    float lsum[QB];
+    qk(ks_nxt, s_nxt);
+    form_p(s_cur, pk_cur, lsum, live);
+    pv(vs_prev, pk_prev);
+    settle(s_cur, pk_cur, lsum);
+  };
+
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // K_0, K_1, V_0 and Q have landed
   __syncthreads();
-  for (int j = 0; j < ntiles; j += 2) {
-    if (j + 1 < ntiles) gload(j + 1, k_lds1, v_lds1);
-    if (j < wave_ntiles) compute(j, k_lds0, v_lds0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    if (j + 1 >= ntiles) break;
-    if (j + 2 < ntiles) gload(j + 2, k_lds0, v_lds0);
-    if (j + 1 < wave_ntiles) compute(j + 1, k_lds1, v_lds1);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
+  f32x16 sA[QB], sB[QB];
+  uint32_t pkA[QB][8], pkB[QB][8];
+  qk(k_lds0, sA);
+  {                                  // step 0: no P.V yet
+    float lsum[QB];
+    mask(0, sA);
+    qk(k_lds0 + HALF, sB);
+    form_p(sA, pkA, lsum, wave_nblk > 0);
+    settle(sA, pkA, lsum);
   }
+  // Barrier B_t follows step 2t: all of K_t and V_{t-1} have been read, so
+  // K_{t+2} and V_{t+1} start streaming into their buffers; every step reads
+  // data that landed at least one barrier earlier.  Loads past the last tile
+  // fetch nothing and write zeros.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();
+  gload(kp, koff, 2, k_lds0);
+  gload(vp, voff, 1, v_lds1);
+
+  // Steps 1 .. nblk (the last one drains P.V), four per iteration so that
+  // every buffer is a fixed object: K_t sits in k_lds[t % 2], V_t in
+  // v_lds[t % 2]; step s reads K of block s+1 and V of block s-1.
+  const int last_step = (kv_end + 31) / 32;
+  for (int u = 0; 4 * u + 1 <= last_step; ++u) {
+    const int s1 = 4 * u + 1;
+    step(s1, sB, sA, pkB, pkA, k_lds1, v_lds0);
+    if (s1 + 1 > last_step) break;
+    step(s1 + 1, sA, sB, pkA, pkB, k_lds1 + HALF, v_lds0 + HALF);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    gload(kp, koff, 2 * u + 3, k_lds1);
+    gload(vp, voff, 2 * u + 2, v_lds0);
+    if (s1 + 2 > last_step) break;
+    step(s1 + 2, sB, sA, pkB, pkA, k_lds0, v_lds1);
+    if (s1 + 3 > last_step) break;
+    step(s1 + 3, sA, sB, pkA, pkB, k_lds0 + HALF, v_lds1 + HALF);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    gload(kp, koff, 2 * u + 4, k_lds0);
+    gload(vp, voff, 2 * u + 3, v_lds1);
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // no load left in flight
 
   if (!active) return;
 
   // a8: epilogue.  O = acc / ell, L = (m + log2 ell) * ln 2.
-  const float ell_t = halves_sum(ell);
-  const float inv = 1.0f / ell_t;
-  if (qrow < len) {
-    const long long orow = qbase + (long long)qrow * p.q_rs;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qrow = row0 + 32 * qb + l32;
+    const float ell_t = halves_sum(ell[qb]);
+    const float inv = 1.0f / ell_t;
+    if (qrow < len) {
+      const long long orow = qbase + (long long)qrow * p.q_rs;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * db + 8 * g4 + 4 * hf;
-        const float a0 = oacc[db][4 * g4 + 0] * inv, a1 = oacc[db][4 * g4 + 1] * inv;
-        const float a2 = oacc[db][4 * g4 + 2] * inv, a3 = oacc[db][4 * g4 + 3] * inv;
-        if (OUT_F32) {
-          *(f32x4*)((float*)p.o + orow + d0) = f32x4{a0, a1, a2, a3};
-        } else {
-          u32x2 w = {Ops<T>::pack(a0, a1), Ops<T>::pack(a2, a3)};
-          *(u32x2*)((T*)p.o + orow + d0) = w;
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = 32 * db + 8 * g4 + 4 * hf;
+          const float a0 = oacc[qb][db][4 * g4 + 0] * inv, a1 = oacc[qb][db][4 * g4 + 1] * inv;
+          const float a2 = oacc[qb][db][4 * g4 + 2] * inv, a3 = oacc[qb][db][4 * g4 + 3] * inv;
+          if (OUT_F32) {
+            *(f32x4*)((float*)p.o + orow + d0) = f32x4{a0, a1, a2, a3};
+          } else {
+            u32x2 w = {Ops<T>::pack(a0, a1), Ops<T>::pack(a2, a3)};
+            *(u32x2*)((T*)p.o + orow + d0) = w;
+          }
         }
+      if (hf == 0) {
+        const long long li = ((long long)b * p.Hq + h) * p.N + qrow;
+        p.lse[li] = (m_run[qb] + __builtin_amdgcn_logf(ell_t)) * kLn2;
       }
-    if (hf == 0) {
-      const long long li = ((long long)b * p.Hq + h) * p.N + qrow;
-      p.lse[li] = (m_run + __builtin_amdgcn_logf(ell_t)) * kLn2;
     }
   }
 }
@@ -472,13 +589,19 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_f32(FwdParams p) {
           if ((CAUSAL && key > qrow) || key >= len) s[i] = -__builtin_inff();
         }
       }
-      float mx = -__builtin_inff();
+      // Online softmax against the reference maximum, moved (with an exact
+      // rescale) when a partial sum leaves [0, 2^15]; see the 16-bit kernel.
+      float pr[16], lsum = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
-      mx = fmaxf(mx, wave_swap_halves(mx));
-      const float mt = mx * p.scale_log2;
-      if (__any(mt > m_run + kRescaleSlack)) {
-        const float m_new = fmaxf(m_run, mt);
+      for (int i = 0; i < 16; ++i) {
+        pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.scale_log2, -m_run));
+        lsum += pr[i];
+      }
+      if (__any(!(lsum <= kSumLimit))) {
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
+        const float m_new = fmaxf(m_run, halves_max(mx) * p.scale_log2);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         ell *= alpha;
 #pragma unroll
@@ -486,13 +609,14 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_f32(FwdParams p) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
         m_run = m_new;
-      }
-      float pr[16];
+        lsum = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.scale_log2, -m_run));
-        ell += pr[i];
+        for (int i = 0; i < 16; ++i) {
+          pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.scale_log2, -m_run));
+          lsum += pr[i];
+        }
       }
+      ell += lsum;
       // O^T += V^T P^T: step i pairs key(i, half 0) and key(i, half 1).
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -506,7 +630,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_f32(FwdParams p) {
     __syncthreads();
   }
   if (!active) return;
-  const float ell_t = ell + wave_swap_halves(ell);
+  const float ell_t = halves_sum(ell);
   const float inv = 1.0f / ell_t;
   if (qrow < len) {
     float* orow = (float*)p.o + qbase + (long long)qrow * p.q_rs;
