@@ -172,8 +172,10 @@ __device__ __forceinline__ int v_swz(int r) {
 // scores, forms block i's probabilities (independent work, so the matrix
 // cores and the vector ALUs overlap), then accumulates P.V of block i.
 template <typename T, int D, bool CAUSAL, bool VARLEN, bool OUT_F32>
-__global__ __launch_bounds__(256, 2) void fa_fwd_mfma(FwdParams p) {
+__global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(FwdParams p) {
   using vec8 = typename Ops<T>::vec8;
+  constexpr int NW = waves_per_wg(FA_BF16);        // waves per workgroup
+  constexpr int NT = 64 * NW;                      // threads per workgroup
   constexpr int QB = rows_per_wave(FA_BF16) / 32;  // 32-row query blocks per wave
   constexpr int WR = 32 * QB;                // query rows per wave
   constexpr int BC = 64;                     // keys per K/V tile (two 32-key blocks)
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_mfma(FwdParams p) {
   constexpr int DC = D / 16;                 // 16-wide chunks of Q.K
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int RB = D * 2;                  // bytes per tile row
-  constexpr int LOADS = BC * CPR / 256;      // 16-byte loads per thread per tile
+  constexpr int LOADS = BC * CPR / NT;       // 16-byte loads per thread per tile
   constexpr int TILE_BYTES = BC * RB;
   constexpr int HALF = 32 * RB;              // bytes of one 32-key block in a tile
 
@@ -232,13 +234,13 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_mfma(FwdParams p) {
 
   // a3: tile loads go straight from memory into LDS (buffer_load ... lds):
   // lane L of wave w in load i fills 16-byte LDS chunk position
-  // q = 256*i + 64*w + L of the tile, i.e. row q / CPR, position q % CPR,
+  // q = NT*i + 64*w + L of the tile, i.e. row q / CPR, position q % CPR,
   // which holds the row's chunk (q % CPR) ^ swizzle(row).  Rows past the
   // sequence end (and whole tiles past it) read zeros.
   uint32_t koff[LOADS], voff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    const int pch = tid + 256 * i;
+    const int pch = tid + NT * i;
     const int r = pch / CPR, pc = pch % CPR;
     koff[i] = r * kv_rs_bytes + ((pc ^ k_swz<D>(r)) << 4);
     voff[i] = r * kv_rs_bytes + ((pc ^ v_swz<D>(r)) << 4);
@@ -252,7 +254,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_mfma(FwdParams p) {
     const rsrc_t r = make_rsrc(src + (long long)min(kb, len) * kv_rs_bytes,
                                (uint32_t)rows * kv_rs_bytes);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) lds_load16(r, dst_base + (256 * i + 64 * wave) * 16, off[i]);
+    for (int i = 0; i < LOADS; ++i) lds_load16(r, dst_base + (NT * i + 64 * wave) * 16, off[i]);
   };
 
   // Prologue loads: K_0, K_1 and V_0 (K runs ahead of V).
@@ -723,7 +725,8 @@ int launch_fwd(const LaunchArgs& a, void* stream) {
   }
   void* args[] = {&p};
   const hipError_t e = hipLaunchKernel((const void*)var->fn, dim3((unsigned)plan.total_wg),
-                                       dim3(256), args, 0, (hipStream_t)stream);
+                                       dim3(64 * waves_per_wg(a.in_dtype)), args, 0,
+                                       (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -13,11 +13,15 @@ namespace fa {
 // share every K/V operand read from LDS).
 constexpr int rows_per_wave(int in_dtype) { return in_dtype == FA_F32 ? 32 : 32; }
 
-// How the launch covers the work.  A workgroup is 4 waves; each wave owns
-// rows_per_wave() query rows of one query head.  `hp` query heads that share
+// Waves per workgroup: 8 for 16-bit inputs (two per SIMD; all eight share
+// each K/V tile in LDS), 4 for fp32 inputs.
+constexpr int waves_per_wg(int in_dtype) { return in_dtype == FA_F32 ? 4 : 8; }
+
+// How the launch covers the work.  A workgroup is waves_per_wg() waves; each
+// wave owns rows_per_wave() query rows of one query head.  `hp` query heads that share
 // one K/V head are packed into a workgroup (GQA), so one K/V tile in LDS
-// serves them all; the workgroup then covers 4 * rows_per_wave / hp rows of
-// each of those heads.
+// serves them all; the workgroup then covers waves_per_wg * rows_per_wave / hp
+// rows of each of those heads.
 struct Plan {
   int hp;            // query heads per workgroup (1, 2 or 4)
   int rows_per_wg;   // query rows per head per workgroup
@@ -32,7 +36,7 @@ inline Plan make_plan(int B, int Hq, int Hkv, int N, int d, int in_dtype) {
   const int G = Hq / Hkv;
   if (in_dtype == FA_F32) p.hp = 1;
   else p.hp = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
-  p.rows_per_wg = 4 * rows_per_wave(in_dtype) / p.hp;
+  p.rows_per_wg = waves_per_wg(in_dtype) * rows_per_wave(in_dtype) / p.hp;
   p.n_rblocks = (N + p.rows_per_wg - 1) / p.rows_per_wg;
   p.n_hgroups = Hq / p.hp;
   p.total_wg = (uint64_t)B * (uint64_t)p.n_hgroups * (uint64_t)p.n_rblocks;
