@@ -12,6 +12,7 @@ STATUS = {
     "FA_OK": 0, "FA_ERR_NULL": -1, "FA_ERR_SHAPE": -2, "FA_ERR_HEADDIM": -3,
     "FA_ERR_GQA": -4, "FA_ERR_DTYPE": -5, "FA_ERR_ALIGN": -6, "FA_ERR_ALIAS": -7,
     "FA_ERR_SCALE": -8, "FA_ERR_DEVICE": -9, "FA_ERR_LAUNCH": -10,
+    "FA_ERR_WORKSPACE": -11, "FA_ERR_ALLOC": -12,
 }
 
 _lib = None
@@ -30,6 +31,13 @@ def load() -> ctypes.CDLL:
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, i, i]
     lib.fa_fwd.restype = i
+    z = ctypes.c_size_t
+    lib.fa_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa_workspace_bytes.restype = z
+    lib.fa_pack_v.argtypes = [vp, vp, z, i, i, i, i, vp, vp, i]
+    lib.fa_pack_v.restype = i
+    lib.fa_fwd_packed.argtypes = [vp, vp, vp, z, vp, vp, i, i, i, i, i, i, f, vp, vp, i, i]
+    lib.fa_fwd_packed.restype = i
     lib.fa_fwd_check.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i, i]
     lib.fa_fwd_check.restype = i
     lib.fa_kernel_name.argtypes = [i, i, i, i, i]
@@ -73,3 +81,20 @@ def fwd_raw(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, cu_seqlens,
     """fa_fwd with raw integer device addresses and a raw hipStream_t."""
     return load().fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, int(causal), scale,
                          cu_seqlens, stream, in_dtype, out_dtype)
+
+
+def workspace_bytes(B, Hkv, N, d, in_dtype) -> int:
+    """fa_workspace_bytes: size of the packed-V workspace (0 if none)."""
+    return load().fa_workspace_bytes(B, Hkv, N, d, in_dtype)
+
+
+def pack_v_raw(v, vt, vt_bytes, B, Hkv, N, d, cu_seqlens, stream, in_dtype) -> int:
+    """fa_pack_v with raw integer device addresses and a raw hipStream_t."""
+    return load().fa_pack_v(v, vt, vt_bytes, B, Hkv, N, d, cu_seqlens, stream, in_dtype)
+
+
+def fwd_packed_raw(q, k, vt, vt_bytes, o, lse, B, Hq, Hkv, N, d, causal, scale,
+                   cu_seqlens, stream, in_dtype, out_dtype) -> int:
+    """fa_fwd_packed with raw integer device addresses and a raw hipStream_t."""
+    return load().fa_fwd_packed(q, k, vt, vt_bytes, o, lse, B, Hq, Hkv, N, d, int(causal),
+                                scale, cu_seqlens, stream, in_dtype, out_dtype)

@@ -1,6 +1,7 @@
 // C ABI of libfa (declared and documented in include/fa.h).
 #include <hip/hip_runtime.h>
 
+#include <cstdint>
 #include <cstring>
 #include <mutex>
 
@@ -39,6 +40,34 @@ int fa_fwd_check(const void* q, const void* k, const void* v, const void* o,
                         cu_seqlens, in_dtype, out_dtype);
 }
 
+size_t fa_workspace_bytes(int B, int Hkv, int N, int d, int in_dtype) {
+  if ((d != 64 && d != 128) || (in_dtype != FA_F16 && in_dtype != FA_BF16)) return 0;
+  const uint64_t n = fa::workspace_bytes(B, Hkv, N, d, in_dtype);
+  return n > (uint64_t)SIZE_MAX ? SIZE_MAX : (size_t)n;
+}
+
+int fa_pack_v(const void* v, void* vt, size_t vt_bytes, int B, int Hkv, int N, int d,
+              const int* cu_seqlens, void* stream, int in_dtype) {
+  int st = fa::check_pack_args(v, vt, vt_bytes, B, Hkv, N, d, cu_seqlens, in_dtype);
+  if (st != FA_OK) return st;
+  st = device_status();
+  if (st != FA_OK) return st;
+  return fa::launch_vt_pack(v, vt, B, Hkv, N, d, cu_seqlens, in_dtype, stream);
+}
+
+int fa_fwd_packed(const void* q, const void* k, const void* vt, size_t vt_bytes, void* o,
+                  float* lse, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                  const int* cu_seqlens, void* stream, int in_dtype, int out_dtype) {
+  int st = fa::check_packed_args(q, k, vt, vt_bytes, o, lse, B, Hq, Hkv, N, d, causal, scale,
+                                 cu_seqlens, in_dtype, out_dtype);
+  if (st != FA_OK) return st;
+  st = device_status();
+  if (st != FA_OK) return st;
+  fa::LaunchArgs a{q, k, nullptr, o, lse, vt, cu_seqlens, B, Hq, Hkv, N, d, causal,
+                   scale, in_dtype, out_dtype};
+  return fa::launch_fwd(a, stream);
+}
+
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int Hq, int Hkv, int N, int d, int causal, float scale,
            const int* cu_seqlens, void* stream, int in_dtype, int out_dtype) {
@@ -47,9 +76,23 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   if (st != FA_OK) return st;
   st = device_status();
   if (st != FA_OK) return st;
-  fa::LaunchArgs a{q, k, v, o, lse, cu_seqlens, B, Hq, Hkv, N, d, causal,
+  fa::LaunchArgs a{q, k, v, o, lse, nullptr, cu_seqlens, B, Hq, Hkv, N, d, causal,
                    scale, in_dtype, out_dtype};
-  return fa::launch_fwd(a, stream);
+  if (in_dtype == FA_F32) return fa::launch_fwd(a, stream);
+  // 16-bit inputs: pack V^T into a stream-ordered workspace, run, release.
+  const uint64_t need = fa::workspace_bytes(B, Hkv, N, d, in_dtype);
+  if (need / (128ull * (uint64_t)d) > (uint64_t)INT32_MAX || need > (uint64_t)SIZE_MAX)
+    return FA_ERR_SHAPE;
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, (size_t)need, (hipStream_t)stream) != hipSuccess || !ws)
+    return FA_ERR_ALLOC;
+  st = fa::launch_vt_pack(v, ws, B, Hkv, N, d, cu_seqlens, in_dtype, stream);
+  if (st == FA_OK) {
+    a.vt = ws;
+    st = fa::launch_fwd(a, stream);
+  }
+  if (hipFreeAsync(ws, (hipStream_t)stream) != hipSuccess && st == FA_OK) st = FA_ERR_LAUNCH;
+  return st;
 }
 
 const char* fa_kernel_name(int in_dtype, int d, int causal, int varlen,
@@ -75,10 +118,12 @@ const char* fa_status_string(int status) {
     case FA_ERR_SCALE: return "scale must be finite and > 0";
     case FA_ERR_DEVICE: return "no usable device: the current HIP device is not gfx950";
     case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_WORKSPACE: return "workspace too small: see fa_workspace_bytes";
+    case FA_ERR_ALLOC: return "could not allocate the device workspace";
     default: return "unknown status";
   }
 }
 
-int fa_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+int fa_version(void) { return 1 * 10000 + 1 * 100 + 0; }
 
 }  // extern "C"

@@ -75,6 +75,8 @@ struct FwdParams {
   int N, Hq, G;            // max length, query heads, Hq / Hkv
   int hp, rows_per_wg, n_rblocks, n_hgroups, total_wg, xcd_remap;
   float scale_log2;        // scale * log2(e)
+  const void* vt;          // packed V^T tiles (16-bit inputs), see fa_vt_pack
+  int Hkv, vt_ntiles;      // K/V heads; V^T tiles per (sequence, K/V head)
   long long q_bs, q_hs, q_rs;    // element strides of q (and o): batch, head, row
   long long kv_bs, kv_hs, kv_rs; // element strides of k and v
 };
@@ -141,25 +143,84 @@ __device__ __forceinline__ void lds_load16(rsrc_t r, char* lds_dst, uint32_t vof
 #endif
 }
 
-// LDS tile layouts.  A tile is BC rows (keys) x D columns of 16-bit values,
-// row-major (2*D bytes per row), cut into 16-byte chunks.  gfx950 LDS serves
-// 256 bytes per cycle (64 four-byte banks): a ds_read_b128 takes 16 lanes per
-// cycle and a ds_read_b64_tr_b16 32 lanes.  Chunk c of row r is stored at
-// chunk position c ^ swizzle(r), chosen so that those lane groups always
-// touch 16 different 16-byte bank groups:
-//  K (lanes read one chunk of 16 consecutive rows):
+// LDS tile layouts, cut into 16-byte chunks.  gfx950 LDS serves 256 bytes per
+// cycle (64 four-byte banks); a ds_read_b128 takes 16 lanes per cycle.  Chunk
+// c of row r is stored at chunk position c ^ swizzle(r), chosen so that the 16
+// lanes of one cycle (one chunk of 16 consecutive rows) hit 16 different
+// 16-byte bank groups.
+//  K tile: 64 key rows x D values (2*D bytes per row):
 //    D = 128: c ^ (r % 16);          D = 64: c ^ ((r / 2) % 8)
-//  V (32 lanes read 4 consecutive chunks of 4 consecutive rows):
-//    D = 128: c ^ 4 * (r % 4);       D = 64: c ^ 4 * ((r / 2) % 2)
+//  V^T tile: D rows (one per output column) x 64 keys (128 bytes per row):
+//    c ^ ((r / 2) % 8)
 template <bool B> struct BoolTag { static constexpr bool value = B; };
 
 template <int D>
 __device__ __forceinline__ int k_swz(int r) {
   return D == 128 ? (r & 15) : ((r >> 1) & 7);
 }
-template <int D>
-__device__ __forceinline__ int v_swz(int r) {
-  return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+__device__ __forceinline__ int vt_swz(int r) { return (r >> 1) & 7; }
+
+// Key stored at position j (0..15) of a 16-key group of a V^T row: the
+// order of P^T's B-operand fragment (lanes 0-31 hold keys 0-3 and 8-11,
+// lanes 32-63 keys 4-7 and 12-15), so one 16-byte read per lane is the A
+// operand of O^T = V^T P^T.
+__device__ __forceinline__ int vt_key(int j) {
+  return (j & 3) | ((j & 4) << 1) | ((j & 8) >> 1);
+}
+
+// ---------------------------------------------------------------------------
+// V^T packing: for every (sequence, K/V head, 64-key tile), write the tile
+// transposed, D rows x 64 keys, keys in vt_key order, to the workspace:
+// tile (b, kvh, t) at byte ((b * Hkv + kvh) * ntiles + t) * 128 * D.  Keys
+// past the sequence end are zero.  Tiles wholly past it are not written (the
+// attention kernel never reads them).
+struct VtParams {
+  const void* v; void* ws; const int* cu_seqlens;
+  int N, Hkv, ntiles;
+  long long kv_bs, kv_hs, kv_rs;
+};
+
+template <typename T, int D, bool VARLEN>
+__global__ __launch_bounds__(256) void fa_vt_pack(VtParams p) {
+  // One workgroup per tile: blockIdx.x = (b * Hkv + kvh) * ntiles + t.
+  const int t = blockIdx.x % p.ntiles;
+  const int kvh = (blockIdx.x / p.ntiles) % p.Hkv;
+  const int b = blockIdx.x / p.ntiles / p.Hkv;
+  int seq0 = 0, len = p.N;
+  if (VARLEN) {
+    seq0 = p.cu_seqlens[b];
+    len = p.cu_seqlens[b + 1] - seq0;
+  }
+  const int kb = t * 64;
+  if (kb >= len) return;
+  __shared__ __attribute__((aligned(16))) T vt[64 * D];   // V rows of the tile
+  const T* src = (const T*)p.v + (VARLEN ? (long long)seq0 * p.kv_rs : (long long)b * p.kv_bs) +
+                 (long long)kvh * p.kv_hs;
+  constexpr int CPR = D / 8;
+#pragma unroll
+  for (int i = 0; i < 64 * CPR / 256; ++i) {
+    const int q = threadIdx.x + 256 * i;
+    const int r = q / CPR, c = q % CPR;
+    u32x4 x = {0, 0, 0, 0};
+    if (kb + r < len) x = *(const u32x4*)(src + (long long)(kb + r) * p.kv_rs + c * 8);
+    *(u32x4*)(vt + r * D + c * 8) = x;
+  }
+  __syncthreads();
+  char* dst = (char*)p.ws + (long long)blockIdx.x * (128LL * D);
+#pragma unroll
+  for (int i = 0; i < 8 * D / 256; ++i) {
+    const int q = threadIdx.x + 256 * i;
+    const int d = q % D, c = q / D;             // output row d, 16-byte chunk c
+    uint16_t v8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int key = 16 * (c >> 1) + vt_key(8 * (c & 1) + j);
+      v8[j] = __builtin_bit_cast(uint16_t, vt[key * D + d]);
+    }
+    u32x4 w = {v8[0] | (uint32_t)v8[1] << 16, v8[2] | (uint32_t)v8[3] << 16,
+               v8[4] | (uint32_t)v8[5] << 16, v8[6] | (uint32_t)v8[7] << 16};
+    *(u32x4*)(dst + d * 128 + c * 16) = w;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -229,7 +290,6 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
   const long long kvbase = (VARLEN ? (long long)seq0 * p.kv_rs : (long long)b * p.kv_bs) +
                            (long long)kvh * p.kv_hs;
   const char* kp = (const char*)((const T*)p.k + kvbase);
-  const char* vp = (const char*)((const T*)p.v + kvbase);
   const uint32_t kv_rs_bytes = (uint32_t)p.kv_rs * 2;
 
   // a3: tile loads go straight from memory into LDS (buffer_load ... lds):
@@ -243,24 +303,33 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
     const int pch = tid + NT * i;
     const int r = pch / CPR, pc = pch % CPR;
     koff[i] = r * kv_rs_bytes + ((pc ^ k_swz<D>(r)) << 4);
-    voff[i] = r * kv_rs_bytes + ((pc ^ v_swz<D>(r)) << 4);
+    const int vr = pch / 8, vc = pch % 8;       // V^T tile: 8 chunks per row
+    voff[i] = vr * 128 + ((vc ^ vt_swz(vr)) << 4);
   }
-  auto gload = [&](const char* src, const uint32_t (&off)[LOADS], int tile, char* dst_base)
-      __attribute__((always_inline)) {
+  auto gload = [&](int tile, char* dst_base) __attribute__((always_inline)) {
     const int kb = tile * BC;
     // readfirstlane keeps the clamp (a VALU med3) in a scalar register: the
     // resource of a buffer load must be wave-uniform.
     const int rows = __builtin_amdgcn_readfirstlane(max(0, min(len - kb, BC)));
-    const rsrc_t r = make_rsrc(src + (long long)min(kb, len) * kv_rs_bytes,
+    const rsrc_t r = make_rsrc(kp + (long long)min(kb, len) * kv_rs_bytes,
                                (uint32_t)rows * kv_rs_bytes);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) lds_load16(r, dst_base + (NT * i + 64 * wave) * 16, off[i]);
+    for (int i = 0; i < LOADS; ++i) lds_load16(r, dst_base + (NT * i + 64 * wave) * 16, koff[i]);
+  };
+  const char* vtp = (const char*)p.vt + (long long)(b * p.Hkv + kvh) * p.vt_ntiles * TILE_BYTES;
+  auto gload_vt = [&](int tile, char* dst_base) __attribute__((always_inline)) {
+    // A V^T tile is contiguous; tiles past the sequence end read zeros.
+    const int live_tile = __builtin_amdgcn_readfirstlane(tile * BC < len ? 1 : 0);
+    const rsrc_t r = make_rsrc(vtp + (long long)min(tile, p.vt_ntiles) * TILE_BYTES,
+                               live_tile ? (uint32_t)TILE_BYTES : 0u);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) lds_load16(r, dst_base + (NT * i + 64 * wave) * 16, voff[i]);
   };
 
   // Prologue loads: K_0, K_1 and V_0 (K runs ahead of V).
-  gload(kp, koff, 0, k_lds0);
-  gload(vp, voff, 0, v_lds0);
-  gload(kp, koff, 1, k_lds1);
+  gload(0, k_lds0);
+  gload_vt(0, v_lds0);
+  gload(1, k_lds1);
 
   // a2: this wave's Q rows as MFMA B operands (query block qb, d-chunk dc,
   // 8 values per lane: Q[row0 + 32*qb + l32][16*dc + 8*hf .. +7]).  Rows past
@@ -286,22 +355,12 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
   int kaddr[DC];
 #pragma unroll
   for (int dc = 0; dc < DC; ++dc) kaddr[dc] = l32 * RB + (((2 * dc + hf) ^ k_swz<D>(l32)) << 4);
-  //  V (A operand of O^T = V^T P^T, transposed read): for 16-key chunk kc,
-  //  half e (keys +0 / +8) and output block db, lane (g = lane/16, i = lane%16)
-  //  points at row 16*kc + 8*e + 4*hf + i/4, columns 32*db + 16*(g%2) + 4*(i%4)
-  //  .. +3.  Lane i of each 16-lane group then receives, for its column, the 4
-  //  keys held by lanes 4*t + i/4 (t = 0..3): the keys of P^T's B-operand
-  //  layout (0-3, 8-11 in lanes 0-31; 4-7, 12-15 in lanes 32-63).
-  int vaddr[DB];
-  {
-    const int g = lane >> 4, li = lane & 15;
-    const int vr = 4 * hf + (li >> 2);   // row within the 16-key chunk (+8 for e = 1)
+  //  V^T (A operand of O^T = V^T P^T): output block db, row 32*db + l32; for
+  //  key half hb of the tile and 16-key chunk kc, logical chunk 4*hb + 2*kc + hf
+  //  (8 keys in vt_key order).  Index [2*hb + kc]; db is an instruction offset.
+  int vaddr[4];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int dcol = 32 * db + 16 * (g & 1) + 4 * (li & 3);
-      vaddr[db] = vr * RB + (((dcol >> 3) ^ v_swz<D>(vr)) << 4) + (dcol & 7) * 2;
-    }
-  }
+  for (int q = 0; q < 4; ++q) vaddr[q] = l32 * 128 + (((2 * q + hf) ^ vt_swz(l32)) << 4);
 
   f32x16 oacc[QB][DB];
   float m_run[QB], ell[QB];         // reference maximum (log2 units), partial row sum
@@ -392,8 +451,10 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
     for (int qb = 0; qb < QB; ++qb) ell[qb] += lsum[qb];
   };
 
-  // a7: O^T += V^T P^T over the two 16-key chunks of one block (V rows at vs).
-  auto pv = [&](const char* vs, const uint32_t (&pk)[QB][8]) __attribute__((always_inline)) {
+  // a7: O^T += V^T P^T over the two 16-key chunks of one block: key half hb
+  // of the V^T tile at vs.
+  auto pv = [&](const char* vs, int hb, const uint32_t (&pk)[QB][8])
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       vec8 pf[QB];
@@ -404,16 +465,9 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
       }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const char* va = vs + vaddr[db] + kc * 16 * RB;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(va));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(va + 8 * RB));
-        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-        const u32x4 vv = {lo2[0], lo2[1], hi2[0], hi2[1]};
+        const vec8 vf = *(const vec8*)(vs + vaddr[2 * hb + kc] + db * 32 * 128);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          oacc[qb][db] = Ops<T>::mfma(__builtin_bit_cast(vec8, vv), pf[qb], oacc[qb][db]);
+        for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = Ops<T>::mfma(vf, pf[qb], oacc[qb][db]);
       }
     }
   };
@@ -425,14 +479,32 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
   // P is zero (and its scores, reads of loaded or zero-filled LDS, unused),
   // so the step after the last one just drains P.V.
   auto step = [&](int st, f32x16 (&s_cur)[QB], f32x16 (&s_nxt)[QB], uint32_t (&pk_cur)[QB][8],
-                  const uint32_t (&pk_prev)[QB][8], const char* ks_nxt, const char* vs_prev)
+                  const uint32_t (&pk_prev)[QB][8], const char* ks_nxt, const char* vs_prev,
+                  int hb_prev)
       __attribute__((always_inline)) {
     const bool live = st < wave_nblk;
     mask(st, s_cur);
     float lsum[QB];
     qk(ks_nxt, s_nxt);
     form_p(s_cur, pk_cur, lsum, live);
-    pv(vs_prev, pk_prev);
+    pv(vs_prev, hb_prev, pk_prev);
+    // Issue order for the region above: a few operand reads ahead, then each
+    // MFMA (32 cycles in the matrix pipe) followed by a few independent
+    // softmax instructions and the next reads, so the wave's exp/FMA work
+    // runs while its own MFMAs execute.
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);       // 4 LDS reads
+#pragma unroll
+    for (int i = 0; i < DC * QB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // 1 MFMA (scores)
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);     // 3 VALU
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);     // 3 LDS reads
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * DB * QB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // 1 MFMA (P.V)
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);     // 4 VALU
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // 1 LDS read
+    }
     settle(s_cur, pk_cur, lsum);
   };
 
@@ -454,8 +526,8 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
   // fetch nothing and write zeros.
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
-  gload(kp, koff, 2, k_lds0);
-  gload(vp, voff, 1, v_lds1);
+  gload(2, k_lds0);
+  gload_vt(1, v_lds1);
 
   // Steps 1 .. nblk (the last one drains P.V), four per iteration so that
   // every buffer is a fixed object: K_t sits in k_lds[t % 2], V_t in
@@ -463,21 +535,21 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
   const int last_step = (kv_end + 31) / 32;
   for (int u = 0; 4 * u + 1 <= last_step; ++u) {
     const int s1 = 4 * u + 1;
-    step(s1, sB, sA, pkB, pkA, k_lds1, v_lds0);
+    step(s1, sB, sA, pkB, pkA, k_lds1, v_lds0, 0);
     if (s1 + 1 > last_step) break;
-    step(s1 + 1, sA, sB, pkA, pkB, k_lds1 + HALF, v_lds0 + HALF);
+    step(s1 + 1, sA, sB, pkA, pkB, k_lds1 + HALF, v_lds0, 1);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
-    gload(kp, koff, 2 * u + 3, k_lds1);
-    gload(vp, voff, 2 * u + 2, v_lds0);
+    gload(2 * u + 3, k_lds1);
+    gload_vt(2 * u + 2, v_lds0);
     if (s1 + 2 > last_step) break;
-    step(s1 + 2, sB, sA, pkB, pkA, k_lds0, v_lds1);
+    step(s1 + 2, sB, sA, pkB, pkA, k_lds0, v_lds1, 0);
     if (s1 + 3 > last_step) break;
-    step(s1 + 3, sA, sB, pkA, pkB, k_lds0 + HALF, v_lds1 + HALF);
+    step(s1 + 3, sA, sB, pkA, pkB, k_lds0 + HALF, v_lds1, 1);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
-    gload(kp, koff, 2 * u + 4, k_lds0);
-    gload(vp, voff, 2 * u + 3, v_lds1);
+    gload(2 * u + 4, k_lds0);
+    gload_vt(2 * u + 3, v_lds1);
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // no load left in flight
 
@@ -696,6 +768,18 @@ const Variant* find_variant(int in_dtype, int d, int causal, int varlen, int out
 
 }  // namespace
 
+typedef void (*PackFn)(VtParams);
+struct PackVariant {
+  int in_dtype, d, varlen;
+  PackFn fn;
+};
+const PackVariant kPackVariants[] = {
+    {FA_BF16, 64, 0, fa_vt_pack<__bf16, 64, false>}, {FA_BF16, 64, 1, fa_vt_pack<__bf16, 64, true>},
+    {FA_BF16, 128, 0, fa_vt_pack<__bf16, 128, false>}, {FA_BF16, 128, 1, fa_vt_pack<__bf16, 128, true>},
+    {FA_F16, 64, 0, fa_vt_pack<_Float16, 64, false>}, {FA_F16, 64, 1, fa_vt_pack<_Float16, 64, true>},
+    {FA_F16, 128, 0, fa_vt_pack<_Float16, 128, false>}, {FA_F16, 128, 1, fa_vt_pack<_Float16, 128, true>},
+};
+
 const char* kernel_name(int in_dtype, int d, int causal, int varlen, int out_dtype) {
   const Variant* v = find_variant(in_dtype, d, causal != 0, varlen != 0, out_dtype);
   return v ? v->name : nullptr;
@@ -715,6 +799,7 @@ int launch_fwd(const LaunchArgs& a, void* stream) {
   p.n_hgroups = plan.n_hgroups; p.total_wg = (int)plan.total_wg;
   p.xcd_remap = (a.in_dtype != FA_F32) && (plan.total_wg % 8 == 0);
   p.scale_log2 = a.scale * kLog2e;
+  p.vt = a.vt; p.Hkv = a.Hkv; p.vt_ntiles = vt_tiles(a.N);
   const long long d = a.d;
   if (varlen) {
     p.q_bs = 0; p.q_hs = d; p.q_rs = (long long)a.Hq * d;
@@ -727,6 +812,28 @@ int launch_fwd(const LaunchArgs& a, void* stream) {
   const hipError_t e = hipLaunchKernel((const void*)var->fn, dim3((unsigned)plan.total_wg),
                                        dim3(64 * waves_per_wg(a.in_dtype)), args, 0,
                                        (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int launch_vt_pack(const void* v, void* vt, int B, int Hkv, int N, int d, const int* cu_seqlens,
+                   int in_dtype, void* stream) {
+  const int varlen = cu_seqlens != nullptr;
+  const PackVariant* var = nullptr;
+  for (const PackVariant& pv : kPackVariants)
+    if (pv.in_dtype == in_dtype && pv.d == d && pv.varlen == varlen) var = &pv;
+  if (!var) return FA_ERR_DTYPE;
+  VtParams p;
+  p.v = v; p.ws = vt; p.cu_seqlens = cu_seqlens;
+  p.N = N; p.Hkv = Hkv; p.ntiles = vt_tiles(N);
+  if (varlen) {
+    p.kv_bs = 0; p.kv_hs = d; p.kv_rs = (long long)Hkv * d;
+  } else {
+    p.kv_rs = d; p.kv_hs = (long long)N * d; p.kv_bs = (long long)Hkv * N * d;
+  }
+  void* args[] = {&p};
+  const hipError_t e = hipLaunchKernel((const void*)var->fn,
+                                       dim3((unsigned)((long long)B * Hkv * p.ntiles)), dim3(256),
+                                       args, 0, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

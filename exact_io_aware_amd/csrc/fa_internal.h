@@ -43,17 +43,40 @@ inline Plan make_plan(int B, int Hq, int Hkv, int N, int d, int in_dtype) {
   return p;
 }
 
+// 64-key V^T tiles per (sequence, K/V head) in the packed-V workspace.
+inline int vt_tiles(int N) { return (N + 63) / 64; }
+
+// Bytes of the packed V^T workspace: B * Hkv * vt_tiles(N) tiles of d rows x
+// 64 keys in 16 bits.  fp32 inputs need none.  Saturates at UINT64_MAX.
+inline uint64_t workspace_bytes(int B, int Hkv, int N, int d, int in_dtype) {
+  if (in_dtype == FA_F32 || B < 1 || Hkv < 1 || N < 1 || d < 1) return 0;
+  const uint64_t tiles = (uint64_t)B * (uint64_t)Hkv * (uint64_t)vt_tiles(N);
+  const uint64_t per = 128ull * (uint64_t)d;
+  return tiles > UINT64_MAX / per ? UINT64_MAX : tiles * per;
+}
+
 inline uint64_t grid_size(int B, int Hq, int Hkv, int N, int d, int in_dtype) {
   return make_plan(B, Hq, Hkv, N, d, in_dtype).total_wg;
 }
 
+// Checks of fa_fwd's arguments.  v_bytes is the extent of v used for the
+// overlap test with o (0: the size of V itself).
 int check_args(const void* q, const void* k, const void* v, const void* o,
                const float* lse, int B, int Hq, int Hkv, int N, int d,
                int causal, float scale, const int* cu_seqlens, int in_dtype,
-               int out_dtype);
+               int out_dtype, uint64_t v_bytes = 0);
+
+// Checks of fa_fwd_packed's and fa_pack_v's arguments.
+int check_packed_args(const void* q, const void* k, const void* vt, uint64_t vt_bytes,
+                      const void* o, const float* lse, int B, int Hq, int Hkv, int N, int d,
+                      int causal, float scale, const int* cu_seqlens, int in_dtype,
+                      int out_dtype);
+int check_pack_args(const void* v, const void* vt, uint64_t vt_bytes, int B, int Hkv, int N,
+                    int d, const int* cu_seqlens, int in_dtype);
 
 struct LaunchArgs {
   const void* q; const void* k; const void* v; void* o; float* lse;
+  const void* vt;      // packed V^T (16-bit inputs; v is then unused)
   const int* cu_seqlens;
   int B, Hq, Hkv, N, d, causal;
   float scale;
@@ -63,6 +86,10 @@ struct LaunchArgs {
 // Enqueue the kernel for already-checked arguments.  Returns FA_OK or
 // FA_ERR_LAUNCH.  `stream` is a hipStream_t.
 int launch_fwd(const LaunchArgs& a, void* stream);
+
+// Enqueue the V^T packing kernel (16-bit inputs) for checked arguments.
+int launch_vt_pack(const void* v, void* vt, int B, int Hkv, int N, int d, const int* cu_seqlens,
+                   int in_dtype, void* stream);
 
 // Static name of the kernel instance for these settings, or nullptr.
 const char* kernel_name(int in_dtype, int d, int causal, int varlen, int out_dtype);

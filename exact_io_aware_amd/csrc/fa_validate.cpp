@@ -1,4 +1,4 @@
-// Argument checks of fa_fwd (include/fa.h).  Pure C++: no HIP call, so the
+// Argument checks of fa_fwd, fa_pack_v and fa_fwd_packed (include/fa.h).  Pure C++: no HIP call, so the
 // checks run, and are tested, on a machine without a GPU.
 #include <cmath>
 #include <cstdint>
@@ -27,7 +27,7 @@ bool overlap(uintptr_t a, uint64_t na, uintptr_t b, uint64_t nb) {
 int check_args(const void* q, const void* k, const void* v, const void* o,
                const float* lse, int B, int Hq, int Hkv, int N, int d,
                int causal, float scale, const int* cu_seqlens, int in_dtype,
-               int out_dtype) {
+               int out_dtype, uint64_t v_bytes) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || (causal != 0 && causal != 1))
     return FA_ERR_SHAPE;
@@ -44,6 +44,7 @@ int check_args(const void* q, const void* k, const void* v, const void* o,
   if (!mul_ok(rows, (uint64_t)Hq * (uint64_t)d, &qn)) return FA_ERR_SHAPE;
   if (!mul_ok(rows, (uint64_t)Hkv * (uint64_t)d, &kn)) return FA_ERR_SHAPE;
   if (!mul_ok(rows, (uint64_t)Hq, &ln)) return FA_ERR_SHAPE;
+  if (v_bytes == 0) v_bytes = kn * elem_size(in_dtype);
   // Kernel index arithmetic uses 64-bit element offsets and 32-bit row,
   // head and workgroup counts.
   if (qn > (uint64_t)INT64_MAX / 4 || ln > (uint64_t)INT32_MAX * 64)
@@ -67,10 +68,46 @@ int check_args(const void* q, const void* k, const void* v, const void* o,
     const uint64_t ob = qn * elem_size(out_dtype), ib = elem_size(in_dtype);
     if (overlap(po, ob, (uintptr_t)q, qn * ib) ||
         overlap(po, ob, (uintptr_t)k, kn * ib) ||
-        overlap(po, ob, (uintptr_t)v, kn * ib) ||
+        overlap(po, ob, (uintptr_t)v, v_bytes) ||
         overlap(po, ob, (uintptr_t)lse, ln * 4))
       return FA_ERR_ALIAS;
   }
+  return FA_OK;
+}
+
+int check_packed_args(const void* q, const void* k, const void* vt, uint64_t vt_bytes,
+                      const void* o, const float* lse, int B, int Hq, int Hkv, int N, int d,
+                      int causal, float scale, const int* cu_seqlens, int in_dtype,
+                      int out_dtype) {
+  if (in_dtype == FA_F32) return FA_ERR_DTYPE;   // fp32 inputs use V itself
+  const uint64_t need = workspace_bytes(B, Hkv, N, d, in_dtype);
+  const int st = check_args(q, k, vt, o, lse, B, Hq, Hkv, N, d, causal, scale, cu_seqlens,
+                            in_dtype, out_dtype, need);
+  if (st != FA_OK) return st;
+  if (vt_bytes < need) return FA_ERR_WORKSPACE;
+  if (need / (128ull * (uint64_t)d) > (uint64_t)INT32_MAX) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+int check_pack_args(const void* v, const void* vt, uint64_t vt_bytes, int B, int Hkv, int N,
+                    int d, const int* cu_seqlens, int in_dtype) {
+  if (!v || !vt) return FA_ERR_NULL;
+  if (B < 1 || Hkv < 1 || N < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (in_dtype != FA_F16 && in_dtype != FA_BF16) return FA_ERR_DTYPE;
+  uint64_t rows, vn;
+  if (!mul_ok((uint64_t)B, (uint64_t)N, &rows)) return FA_ERR_SHAPE;
+  if (!mul_ok(rows, (uint64_t)Hkv * (uint64_t)d, &vn)) return FA_ERR_SHAPE;
+  if (vn > (uint64_t)INT64_MAX / 4) return FA_ERR_SHAPE;
+  const uint64_t need = workspace_bytes(B, Hkv, N, d, in_dtype);
+  // One workgroup per tile, counted in 32 bits.
+  if (need / (128ull * (uint64_t)d) > (uint64_t)INT32_MAX) return FA_ERR_SHAPE;
+  auto mis = [](const void* p, uintptr_t a) { return ((uintptr_t)p) % a != 0; };
+  if (mis(v, 16) || mis(vt, 16) || (cu_seqlens && mis(cu_seqlens, 4))) return FA_ERR_ALIGN;
+  if (vt_bytes < need) return FA_ERR_WORKSPACE;
+  if ((uintptr_t)vt == (uintptr_t)v ||
+      (!cu_seqlens && overlap((uintptr_t)vt, need, (uintptr_t)v, vn * 2)))
+    return FA_ERR_ALIAS;
   return FA_OK;
 }
 

@@ -1,4 +1,5 @@
-"""``fwd``: torch front end of fa_fwd (memory, streams and argument marshalling)."""
+"""``fwd`` and ``pack_v``: torch front end of libfa (memory, streams and
+argument marshalling)."""
 from __future__ import annotations
 
 import math
@@ -12,11 +13,63 @@ _DT = {torch.float32: _lib.FA_F32, torch.float16: _lib.FA_F16,
        torch.bfloat16: _lib.FA_BF16}
 
 
-def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+def _max_seqlen(cu_seqlens: torch.Tensor, max_seqlen: Optional[int]) -> int:
+    if max_seqlen is not None:
+        return int(max_seqlen)
+    B = cu_seqlens.numel() - 1
+    return int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if B > 0 else 0
+
+
+def _check_cu(cu_seqlens: torch.Tensor) -> None:
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be an int32 device tensor [B+1]")
+    if not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be contiguous")
+
+
+def pack_v(v: torch.Tensor, *, cu_seqlens: Optional[torch.Tensor] = None,
+           max_seqlen: Optional[int] = None, out: Optional[torch.Tensor] = None,
+           stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """fa_pack_v: V (float16/bfloat16, layout as in ``fwd``) transposed into
+    64-key tiles, the form ``fwd(..., vt=...)`` reads.  Returns the packed
+    uint8 workspace (``out`` if given; it must hold fa_workspace_bytes)."""
+    if v.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("pack_v takes float16 or bfloat16 values")
+    if not v.is_cuda or not v.is_contiguous():
+        raise ValueError("v must be a contiguous device tensor")
+    if cu_seqlens is None:
+        if v.dim() != 4:
+            raise ValueError("fixed layout needs v [B,Hkv,N,d]")
+        B, Hkv, N, d = v.shape
+        cu_ptr = None
+    else:
+        _check_cu(cu_seqlens)
+        if v.dim() != 3:
+            raise ValueError("packed layout needs v [T,Hkv,d]")
+        _, Hkv, d = v.shape
+        B = cu_seqlens.numel() - 1
+        N = _max_seqlen(cu_seqlens, max_seqlen)
+        cu_ptr = cu_seqlens.data_ptr()
+    nbytes = _lib.workspace_bytes(B, Hkv, N, d, _DT[v.dtype])
+    if out is None:
+        out = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=v.device)
+    elif out.dtype != torch.uint8 or not out.is_cuda or not out.is_contiguous():
+        raise ValueError("out must be a contiguous uint8 device tensor")
+    st = (stream or torch.cuda.current_stream(v.device)).cuda_stream
+    with torch.cuda.device(v.device):
+        status = _lib.pack_v_raw(v.data_ptr(), out.data_ptr(), out.numel(), B, Hkv, N, d,
+                                 cu_ptr, st, _DT[v.dtype])
+    if status != _lib.FA_OK:
+        raise RuntimeError(f"fa_pack_v failed ({status}): {_lib.status_string(status)}")
+    return out
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor], *, causal: bool = False,
         scale: Optional[float] = None, cu_seqlens: Optional[torch.Tensor] = None,
         max_seqlen: Optional[int] = None, out_dtype: torch.dtype = torch.float32,
         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-        stream: Optional[torch.cuda.Stream] = None):
+        stream: Optional[torch.cuda.Stream] = None, vt: Optional[torch.Tensor] = None,
+        library_workspace: bool = False):
     """Exact attention forward on the GPU: returns ``(o, lse)``.
 
     Fixed length: q ``[B, Hq, N, d]``, k/v ``[B, Hkv, N, d]``.
@@ -26,8 +79,17 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
     which synchronises.
     ``lse`` is float32 ``[B, Hq, N]``.  ``scale`` defaults to 1/sqrt(d).
     ``out``/``lse`` may be given to write into existing buffers.
-    The kernel is enqueued on ``stream`` (default: the current stream).
+    The kernels are enqueued on ``stream`` (default: the current stream).
+
+    16-bit inputs: V is first packed (``pack_v``) into a workspace from
+    torch's allocator, then fa_fwd_packed runs.  ``vt`` passes V already
+    packed by ``pack_v`` (``v`` may then be None).  ``library_workspace``
+    calls fa_fwd instead, which allocates its own stream-ordered workspace.
     """
+    if v is None and vt is None:
+        raise ValueError("v is needed unless a packed vt is given")
+    if v is None:
+        v = k            # shapes and dtype only; V itself comes from vt
     if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share one dtype among float32/float16/bfloat16")
     if out_dtype not in (torch.float32, q.dtype):
@@ -48,18 +110,13 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
     else:
         if q.dim() != 3 or k.dim() != 3:
             raise ValueError("packed layout needs q [T,Hq,d] and k/v [T,Hkv,d]")
-        if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1:
-            raise ValueError("cu_seqlens must be an int32 device tensor [B+1]")
-        if not cu_seqlens.is_contiguous():
-            raise ValueError("cu_seqlens must be contiguous")
+        _check_cu(cu_seqlens)
         T, Hq, d = q.shape
         if k.shape[0] != T or k.shape[2] != d:
             raise ValueError("k/v shape does not match q")
         Hkv = k.shape[1]
         B = cu_seqlens.numel() - 1
-        if max_seqlen is None:
-            max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if B > 0 else 0
-        N = int(max_seqlen)
+        N = _max_seqlen(cu_seqlens, max_seqlen)
         cu_ptr = cu_seqlens.data_ptr()
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -71,13 +128,29 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     elif lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, N) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 tensor [B, Hq, N]")
-    st = (stream or torch.cuda.current_stream(q.device)).cuda_stream
+    stream = stream or torch.cuda.current_stream(q.device)
+    st = stream.cuda_stream
+    packed = q.dtype != torch.float32 and not library_workspace
+    if vt is not None and not packed:
+        raise ValueError("vt is used for 16-bit inputs without library_workspace only")
+    if packed and vt is None:
+        vt = pack_v(v, cu_seqlens=cu_seqlens, max_seqlen=N if cu_seqlens is not None else None,
+                    stream=stream)
+    if packed and (vt.dtype != torch.uint8 or not vt.is_cuda or not vt.is_contiguous()):
+        raise ValueError("vt must be the contiguous uint8 device tensor pack_v returns")
     with torch.cuda.device(q.device):
-        status = _lib.fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                              lse.data_ptr(), B, Hq, Hkv, N, d, causal, float(scale),
-                              cu_ptr, st, _DT[q.dtype], _DT[out_dtype])
+        if packed:
+            status = _lib.fwd_packed_raw(q.data_ptr(), k.data_ptr(), vt.data_ptr(), vt.numel(),
+                                         out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, N, d,
+                                         causal, float(scale), cu_ptr, st, _DT[q.dtype],
+                                         _DT[out_dtype])
+        else:
+            status = _lib.fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  lse.data_ptr(), B, Hq, Hkv, N, d, causal, float(scale),
+                                  cu_ptr, st, _DT[q.dtype], _DT[out_dtype])
     if status != _lib.FA_OK:
-        raise RuntimeError(f"fa_fwd failed ({status}): {_lib.status_string(status)}")
+        name = "fa_fwd_packed" if packed else "fa_fwd"
+        raise RuntimeError(f"{name} failed ({status}): {_lib.status_string(status)}")
     return out, lse
 
 

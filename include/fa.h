@@ -49,8 +49,12 @@
  * {0, 1}; scale finite and > 0.  No dropout, no arbitrary mask.
  *
  * Ownership and threading: every pointer is a device pointer owned by the
- * caller; the library allocates no device memory, keeps no per-call state,
- * and never synchronises.  The work is enqueued on `stream` (a hipStream_t;
+ * caller.  For 16-bit inputs fa_fwd takes a stream-ordered device workspace
+ * of fa_workspace_bytes() bytes (hipMallocAsync / hipFreeAsync on `stream`)
+ * for a transposed copy of V; callers that manage memory themselves call
+ * fa_pack_v and fa_fwd_packed with a workspace of their own instead, and the
+ * library then allocates nothing.  The library keeps no per-call state and
+ * never synchronises.  The work is enqueued on `stream` (a hipStream_t;
  * NULL is the default stream) and fa_fwd returns at once.  Calls are
  * thread-safe; calls on different streams may run concurrently.  o must not
  * overlap q, k, v or lse.
@@ -65,6 +69,8 @@
  */
 #ifndef FA_H
 #define FA_H
+
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -83,7 +89,9 @@ typedef enum {
   FA_ERR_ALIAS = -7,    /* o overlaps q, k, v or lse */
   FA_ERR_SCALE = -8,    /* scale not finite or not > 0 */
   FA_ERR_DEVICE = -9,   /* current device is not gfx950, or no device */
-  FA_ERR_LAUNCH = -10   /* the kernel launch failed */
+  FA_ERR_LAUNCH = -10,  /* the kernel launch failed */
+  FA_ERR_WORKSPACE = -11, /* vt_bytes below fa_workspace_bytes() */
+  FA_ERR_ALLOC = -12    /* fa_fwd could not allocate its workspace */
 } fa_status;
 
 /* Exact attention forward (see the header comment).  q, k, v: inputs in
@@ -92,6 +100,41 @@ typedef enum {
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int Hq, int Hkv, int N, int d, int causal, float scale,
            const int* cu_seqlens, void* stream, int in_dtype, int out_dtype);
+
+/* Bytes of the packed-V workspace that fa_pack_v fills and fa_fwd_packed
+ * reads, for 16-bit inputs: B * Hkv * ceil(N / 64) tiles of d * 64 values
+ * (d * 128 bytes each).  0 for fp32 inputs (which need none) and for
+ * unsupported d or dtype.
+ *
+ * Why (a gfx950 design choice, not from the pages): the P.V product of each
+ * key block takes V^T as its matrix operand.  Transposing V once per forward
+ * pass, in a streaming pre-pass that reads and writes V once, lets the
+ * attention kernel, which brings every V block on chip once per query
+ * block, read it with plain 16-byte LDS reads instead of slower transposing
+ * reads. */
+size_t fa_workspace_bytes(int B, int Hkv, int N, int d, int in_dtype);
+
+/* Pack V (layout as for fa_fwd, in_dtype FA_F16 or FA_BF16) into vt: for
+ * every sequence b, K/V head g and 64-key tile t, the tile transposed (d rows
+ * of 64 keys, 128 bytes per row; keys past the sequence end zero) at byte
+ * offset ((b * Hkv + g) * ceil(N/64) + t) * d * 128.  Within each group of
+ * 16 keys of a row, position j holds key (j % 4) + 8 * ((j / 4) % 2) +
+ * 4 * (j / 8) of the group (the order of the P.V operand's fragments).  Tiles wholly past a
+ * sequence's end are not written.  vt (16-byte aligned, vt_bytes >=
+ * fa_workspace_bytes) must not overlap v.  Enqueued on `stream`; returns
+ * FA_OK or a negative fa_status (FA_ERR_DTYPE for fp32 inputs) before
+ * anything is enqueued. */
+int fa_pack_v(const void* v, void* vt, size_t vt_bytes, int B, int Hkv, int N, int d,
+              const int* cu_seqlens, void* stream, int in_dtype);
+
+/* fa_fwd for 16-bit inputs with V given as fa_pack_v's output vt (packed
+ * with the same B, Hkv, N, d, cu_seqlens and in_dtype, and enqueued before
+ * this call on the same stream, or otherwise complete).  Same results as
+ * fa_fwd; allocates nothing.  Errors as fa_fwd, plus FA_ERR_WORKSPACE, and
+ * FA_ERR_DTYPE for fp32 inputs. */
+int fa_fwd_packed(const void* q, const void* k, const void* vt, size_t vt_bytes, void* o,
+                  float* lse, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                  const int* cu_seqlens, void* stream, int in_dtype, int out_dtype);
 
 /* The argument checks of fa_fwd alone: returns what fa_fwd would return
  * before touching the device (FA_OK if it would go on to launch).  Makes no

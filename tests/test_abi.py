@@ -25,7 +25,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     assert {"fa_fwd", "fa_fwd_check", "fa_kernel_name", "fa_supported",
-            "fa_status_string", "fa_version"} <= set(names)
+            "fa_status_string", "fa_version", "fa_workspace_bytes", "fa_pack_v",
+            "fa_fwd_packed"} <= set(names)
 
 
 def test_library_exports_every_declared_symbol():
@@ -48,7 +49,7 @@ def test_status_codes_match_header():
 
 
 def test_version_and_support():
-    assert fa.version() == 10000
+    assert fa.version() == 10100
     for dt in (fa.FA_F32, fa.FA_F16, fa.FA_BF16):
         for d in (64, 128):
             for c in (False, True):
@@ -134,3 +135,61 @@ def test_flops_convention():
     from workloads import WORKLOADS
     w = WORKLOADS["gqa_bf16"]
     assert abs(fa.flops(w.Hq, w.d, [w.N] * w.B, True) - 5.50e11) / 5.50e11 < 0.01
+
+
+def test_workspace_bytes():
+    # B * Hkv * ceil(N/64) tiles of d rows x 64 keys x 2 bytes; none for fp32.
+    assert fa.workspace_bytes(4, 8, 4096, 128, fa.FA_BF16) == 4 * 8 * 64 * 128 * 128
+    assert fa.workspace_bytes(2, 3, 65, 64, fa.FA_F16) == 2 * 3 * 2 * 64 * 128
+    assert fa.workspace_bytes(1, 1, 1, 128, fa.FA_BF16) == 128 * 128
+    assert fa.workspace_bytes(4, 8, 4096, 128, fa.FA_F32) == 0
+    assert fa.workspace_bytes(4, 8, 4096, 96, fa.FA_BF16) == 0
+    assert fa.workspace_bytes(0, 8, 4096, 128, fa.FA_BF16) == 0
+
+
+VT = 0x700000
+WS = 2 * 2 * 1 * 128 * 128       # workspace of BASE: B=2, Hkv=2, one 64-key tile, d=128
+
+
+def packed(**kw):
+    a = dict(BASE, vt=VT, vt_bytes=WS)
+    a.update(kw)
+    return _lib.fwd_packed_raw(a["q"], a["k"], a["vt"], a["vt_bytes"], a["o"], a["lse"],
+                               a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["causal"],
+                               a["scale"], a["cu_seqlens"], None, a["in_dtype"],
+                               a["out_dtype"])
+
+
+def pack(**kw):
+    a = dict(BASE, vt=VT, vt_bytes=WS)
+    a.update(kw)
+    return _lib.pack_v_raw(a["v"], a["vt"], a["vt_bytes"], a["B"], a["Hkv"], a["N"], a["d"],
+                           a["cu_seqlens"], None, a["in_dtype"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"vt": None}, "FA_ERR_NULL"), ({"q": None}, "FA_ERR_NULL"),
+    ({"vt_bytes": WS - 1}, "FA_ERR_WORKSPACE"), ({"vt_bytes": 0}, "FA_ERR_WORKSPACE"),
+    ({"vt": VT + 8}, "FA_ERR_ALIGN"),
+    ({"in_dtype": fa.FA_F32}, "FA_ERR_DTYPE"),
+    ({"d": 96}, "FA_ERR_HEADDIM"), ({"Hq": 6, "Hkv": 4}, "FA_ERR_GQA"),
+    ({"scale": 0.0}, "FA_ERR_SCALE"),
+    ({"o": VT}, "FA_ERR_ALIAS"), ({"o": VT + WS - 16}, "FA_ERR_ALIAS"),
+])
+def test_fwd_packed_rejects_before_any_device_call(kw, code):
+    assert packed(**kw) == S[code]
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"v": None}, "FA_ERR_NULL"), ({"vt": None}, "FA_ERR_NULL"),
+    ({"B": 0}, "FA_ERR_SHAPE"), ({"N": 0}, "FA_ERR_SHAPE"), ({"Hkv": 0}, "FA_ERR_SHAPE"),
+    ({"B": 1 << 20, "N": 1 << 30, "Hkv": 1 << 10}, "FA_ERR_SHAPE"),
+    ({"d": 32}, "FA_ERR_HEADDIM"),
+    ({"in_dtype": fa.FA_F32}, "FA_ERR_DTYPE"), ({"in_dtype": 5}, "FA_ERR_DTYPE"),
+    ({"v": 0x300004}, "FA_ERR_ALIGN"), ({"vt": VT + 4}, "FA_ERR_ALIGN"),
+    ({"cu_seqlens": 0x600002}, "FA_ERR_ALIGN"),
+    ({"vt_bytes": WS - 16}, "FA_ERR_WORKSPACE"),
+    ({"vt": 0x300000}, "FA_ERR_ALIAS"), ({"vt": 0x300000 + 4096}, "FA_ERR_ALIAS"),
+])
+def test_pack_v_rejects_before_any_device_call(kw, code):
+    assert pack(**kw) == S[code]

@@ -258,3 +258,92 @@ def test_kernel_reported():
     assert fa.kernel_name(fa.FA_BF16, 128, True, False, fa.FA_F32) == \
         "fa_fwd_mfma_bf16_d128_causal_of32"
     assert fa.kernel_name(fa.FA_F32, 64, False, True, fa.FA_F32) == "fa_fwd_f32_d64_varlen"
+
+
+# --- packed V (fa_pack_v / fa_fwd_packed / fa_fwd's own workspace) ----------
+
+def _vt_expected(v16: np.ndarray, lens, Hkv: int, d: int, ntiles: int):
+    """The packed layout fa.h documents, built with numpy from the uint16
+    bit patterns of V ([B, Hkv, N, d] views per sequence).  Returns
+    {(b, g, t): uint16 [d, 64]} for the tiles that hold keys."""
+    j = np.arange(16)
+    key_of_pos = (j % 4) + 8 * ((j // 4) % 2) + 4 * (j // 8)
+    order = (16 * (np.arange(64) // 16) + key_of_pos[np.arange(64) % 16])
+    out = {}
+    for b, n in enumerate(lens):
+        for g in range(Hkv):
+            for t in range((n + 63) // 64):
+                tile = np.zeros((64, d), np.uint16)
+                keys = np.arange(64 * t, min(64 * t + 64, n))
+                tile[keys - 64 * t] = v16[b][g][keys]
+                out[(b, g, t)] = tile[order].T
+    return out
+
+
+@pytest.mark.parametrize("dtype,d,lens,varlen", [
+    ("bf16", 128, [130, 130], False), ("fp16", 64, [70, 1, 130], True),
+    ("bf16", 64, [64, 200], True), ("fp16", 128, [1], False)])
+def test_pack_v_layout(dtype, d, lens, varlen):
+    import torch
+
+    import exact_io_aware_amd as fa
+    Hkv = 3
+    if varlen:
+        w = workloads.make_custom(len(lens), Hkv, Hkv, d, dtype, seed=7, lengths=lens)
+    else:
+        w = workloads.make_custom(len(lens), Hkv, Hkv, d, dtype, seed=7, N=lens[0])
+    N = max(lens)
+    v16 = np.ascontiguousarray(w["v"]).view(np.uint16)
+    if varlen:
+        cu = w["cu_seqlens"]
+        per = [v16[cu[b]:cu[b + 1]].transpose(1, 0, 2) for b in range(len(lens))]
+    else:
+        per = [v16[b] for b in range(len(lens))]
+    ntiles = (N + 63) // 64
+    want = _vt_expected(per, lens, Hkv, d, ntiles)
+    v = G.to_device(w["v"], dtype, "cuda:0")
+    cu_t = torch.from_numpy(w["cu_seqlens"]).to("cuda:0") if varlen else None
+    G.say(f"pack_v {dtype} d={d} lens={lens} varlen={varlen}")
+    ws = fa.pack_v(v, cu_seqlens=cu_t, max_seqlen=N if varlen else None)
+    torch.cuda.synchronize()
+    assert ws.numel() == fa.workspace_bytes(len(lens), Hkv, N, d,
+                                            fa.FA_BF16 if dtype == "bf16" else fa.FA_F16)
+    got = ws.cpu().numpy().view(np.uint16).reshape(len(lens), Hkv, ntiles, d, 64)
+    for (b, g, t), tile in want.items():
+        assert np.array_equal(got[b, g, t], tile), (b, g, t)
+
+
+def test_packed_reuse_and_library_workspace_agree():
+    import torch
+
+    import exact_io_aware_amd as fa
+    w = _make(("bf16", 128, 2, 8, 2, 333, True), seed=11)
+    q, k, v = (G.to_device(w[x], "bf16", "cuda:0") for x in "qkv")
+    G.say("packed vt reuse vs fa_fwd workspace")
+    o1, l1 = fa.fwd(q, k, v, causal=True)
+    vt = fa.pack_v(v)
+    o2, l2 = fa.fwd(q, k, None, causal=True, vt=vt)
+    o3, l3 = fa.fwd(q, k, None, causal=True, vt=vt)
+    o4, l4 = fa.fwd(q, k, v, causal=True, library_workspace=True)
+    torch.cuda.synchronize()
+    for o, l in ((o2, l2), (o3, l3), (o4, l4)):
+        assert torch.equal(o1, o) and torch.equal(l1, l)
+    Oref, Lref = _oracle(w)
+    _compare(w, o4.double().cpu().numpy(), l4.double().cpu().numpy(), Oref, Lref)
+
+
+def test_library_workspace_varlen_fp16():
+    w = _make(("fp16", 64, 3, 4, 2, [200, 7, 128], True), seed=12)
+    Oref, Lref = _oracle(w)
+    import torch
+
+    import exact_io_aware_amd as fa
+    q, k, v = (G.to_device(w[x], "fp16", "cuda:0") for x in "qkv")
+    cu = torch.from_numpy(w["cu_seqlens"]).to("cuda:0")
+    G.say("fa_fwd own workspace, varlen fp16")
+    o, l = fa.fwd(q, k, v, causal=True, cu_seqlens=cu, max_seqlen=200, library_workspace=True)
+    torch.cuda.synchronize()
+    L = l.double().cpu().numpy()
+    for b, n in enumerate(np.diff(w["cu_seqlens"])):
+        L[b, :, n:] = Lref[b, :, n:] = 0.0
+    _compare(w, o.double().cpu().numpy(), L, Oref, Lref)
