@@ -32,13 +32,14 @@ KERNEL_SRC = os.path.join(ROOT, "exact_io_aware_amd", "csrc", "fa_fwd_kernels.hi
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="gqa_bf16")
     ap.add_argument("--out-dtype", choices=["fp32", "in"], default="fp32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-heads", type=int, default=64,
-                    help="query heads (from the first sequences) the oracle is timed on")
+    ap.add_argument("--cpu-sample-heads", type=int, default=0,
+                    help="query heads (from the first sequences) the oracle is timed on; "
+                         "0 = the whole workload")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
                          "(reads and writes that many bytes once), to scale memory "
@@ -72,6 +73,8 @@ def cpu_baseline(w, heads: int):
     import oracle
     import workloads
     G = w["Hq"] // w["Hkv"]
+    if heads <= 0:
+        heads = w["B"] * w["Hq"]
     heads = max(G, (heads // G) * G)
     q, k, v = (workloads.to_f64(w[x], w["dtype"]) for x in "qkv")
     nb = max(1, heads // w["Hq"])
