@@ -14,34 +14,34 @@
 // leaves registers.
 //
 // gfx950 mapping (our design, not the pages'):
-//  * A workgroup is 4 waves.  Each wave owns 32 query rows of one query head.
-//    For GQA, up to 4 query heads sharing a K/V head share the workgroup, so
-//    one K/V tile in LDS feeds all of them.
+//  * A workgroup is 8 waves (two per SIMD).  Each wave owns 32 query rows of
+//    one query head.  For GQA, up to 4 query heads sharing a K/V head share
+//    the workgroup, so one K/V tile in LDS feeds all of them.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16:
 //    the 32x32 accumulator puts one query per lane column (lane l and l+32
 //    hold the same query), so the row max / row sum are in-lane except one
 //    exchange between the two half-waves.
 //  * The probabilities P^T stay in registers: the accumulator layout of
 //    S^T is exactly the B-operand layout of O^T = V^T P^T once the key order
-//    inside each 16-key chunk is permuted (0-3,8-11 | 4-7,12-15); the
-//    A operand V^T is read with the same permutation straight from the
-//    row-major V tile with ds_read_b64_tr_b16 (LDS transpose read).
-//  * K/V tiles are double-buffered in LDS (one barrier per tile); global
-//    loads of tile j+1 are in flight while tile j is computed.
+//    inside each 16-key chunk is permuted (0-3,8-11 | 4-7,12-15).  A small
+//    pre-pass (fa_vt_pack) writes V^T tiles with the keys already in that
+//    order, so the A operand is one 16-byte LDS read per lane.
+//  * K and V^T tiles are double-buffered in LDS (one barrier per tile) and
+//    filled straight from memory (buffer_load ... lds); loads of tile j+1
+//    are in flight while tile j is computed.
 //  * Online softmax in the log2 domain (scale*log2(e) folded into one FMA
-//    per score), with the running maximum only moved when a row's new
-//    maximum exceeds it by more than 8 (in log2 units).  The rescale is then
-//    exact as before, and P stays <= 2^8, so the result is the same
-//    mathematically; most tiles skip the O rescale.
+//    per score), with the running maximum moved lazily: only when a row's
+//    partial sum over a block leaves [0, 2^15].  The rescale is exact, so
+//    the result is the same mathematically; most blocks skip the O rescale.
 //  * Causal: tiles entirely above the diagonal are never visited; only
-//    diagonal and ragged-tail tiles take the per-element mask.
-//  * Workgroups are ordered longest-first within each (sequence, head group)
-//    and the units are laid out so that all workgroups of one K/V head land
-//    on the same XCD (workgroups are dealt round-robin over the 8 XCDs),
-//    keeping that head's K/V in one L2.
+//    diagonal and ragged-tail blocks take the per-element mask.
+//  * Row blocks run longest-first within each (sequence, head group), and
+//    each (sequence, head group) runs on one XCD (workgroups are dealt
+//    round-robin over the 8 XCDs), keeping its K/V in that XCD's L2.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "fa.h"
 #include "fa_internal.h"
@@ -260,11 +260,22 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hf = lane >> 5;
 
-  // a1: workgroup -> (sequence b, head group, row block).
-  int x = blockIdx.x;
-  if (p.xcd_remap) x = (x & 7) * (p.total_wg >> 3) + (x >> 3);
-  const int unit = x / p.n_rblocks;
-  int rb = x - unit * p.n_rblocks;
+  // a1: workgroup -> (unit = sequence b x head group, row block).
+  // Workgroups are dealt round-robin over the 8 XCDs (workgroup j on XCD
+  // j % 8).  With xcd_remap, XCD x takes the units u with u % 8 == x, each
+  // unit's row blocks consecutively: all row blocks of a unit (which share
+  // its K/V) stay in one XCD's L2, and every XCD gets an equal share of
+  // every sequence, whatever the sequence lengths.
+  int unit, rb;
+  if (p.xcd_remap) {
+    const int idx = blockIdx.x >> 3;
+    const int k = idx / p.n_rblocks;
+    rb = idx - k * p.n_rblocks;
+    unit = 8 * k + (blockIdx.x & 7);
+  } else {
+    unit = blockIdx.x / p.n_rblocks;
+    rb = blockIdx.x - unit * p.n_rblocks;
+  }
   if (CAUSAL) rb = p.n_rblocks - 1 - rb;     // longest row blocks first
   const int b = unit / p.n_hgroups;
   const int hgrp = unit - b * p.n_hgroups;
@@ -552,35 +563,73 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
     gload_vt(2 * u + 3, v_lds1);
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // no load left in flight
-
+  // Every wave has finished reading K/V from LDS: the tile buffers become
+  // the epilogue's staging area.
+  __syncthreads();
   if (!active) return;
 
   // a8: epilogue.  O = acc / ell, L = (m + log2 ell) * ln 2.
+  //
+  // The accumulator gives each lane one query row and scattered 16-byte
+  // pieces of it, so stores straight from registers would touch 32 rows per
+  // instruction.  Each wave instead stages its rows in its share of the four
+  // tile buffers (SLOT bytes: 8 KiB at d = 128, 4 KiB at d = 64), DBP
+  // output blocks of 32 columns at a time, and stores whole row segments
+  // (consecutive lanes write consecutive 16-byte chunks of a row).
+  using OT = typename std::conditional<OUT_F32, float, T>::type;
+  constexpr int OB = sizeof(OT);
+  constexpr int SLOT = 4 * TILE_BYTES / NW;          // staging bytes per wave
+  static_assert(NW == 8, "two staging slots per tile buffer");
+  constexpr int DBP = (DB < SLOT / (32 * 32 * OB)) ? DB : SLOT / (32 * 32 * OB);
+  constexpr int RP = DBP * 32 * OB;                  // staged bytes per row
+  constexpr int CPO = RP / 16;                       // 16-byte chunks per staged row
+  constexpr int RPI = 64 / CPO;                      // rows per store instruction
+  static_assert(DBP >= 1 && DB % DBP == 0 && 32 * RP <= SLOT, "staging slot size");
+  char* slot = (wave >> 1) == 0 ? k_lds0 : (wave >> 1) == 1 ? k_lds1
+             : (wave >> 1) == 2 ? v_lds0 : v_lds1;
+  slot += (wave & 1) * SLOT;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = row0 + 32 * qb + l32;
     const float ell_t = halves_sum(ell[qb]);
     const float inv = 1.0f / ell_t;
-    if (qrow < len) {
-      const long long orow = qbase + (long long)qrow * p.q_rs;
+    const int qrow = row0 + 32 * qb + l32;
+    if (hf == 0 && qrow < len) {
+      const long long li = ((long long)b * p.Hq + h) * p.N + qrow;
+      p.lse[li] = (m_run[qb] + __builtin_amdgcn_logf(ell_t)) * kLn2;
+    }
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int pass = 0; pass < DB / DBP; ++pass) {
+      // Stage: lane (l32, hf) holds row l32, columns 32*db + 8*g4 + 4*hf + 0..3.
+#pragma unroll
+      for (int j = 0; j < DBP; ++j) {
+        const int db = pass * DBP + j;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const int d0 = 32 * db + 8 * g4 + 4 * hf;
           const float a0 = oacc[qb][db][4 * g4 + 0] * inv, a1 = oacc[qb][db][4 * g4 + 1] * inv;
           const float a2 = oacc[qb][db][4 * g4 + 2] * inv, a3 = oacc[qb][db][4 * g4 + 3] * inv;
           if (OUT_F32) {
-            *(f32x4*)((float*)p.o + orow + d0) = f32x4{a0, a1, a2, a3};
+            const int c = 8 * j + 2 * g4 + hf;
+            *(f32x4*)(slot + l32 * RP + ((c ^ (l32 & (CPO - 1))) << 4)) = f32x4{a0, a1, a2, a3};
           } else {
+            const int c = 4 * j + g4;
             u32x2 w = {Ops<T>::pack(a0, a1), Ops<T>::pack(a2, a3)};
-            *(u32x2*)((T*)p.o + orow + d0) = w;
+            *(u32x2*)(slot + l32 * RP + ((c ^ (l32 & (CPO - 1))) << 4) + 8 * hf) = w;
           }
         }
-      if (hf == 0) {
-        const long long li = ((long long)b * p.Hq + h) * p.N + qrow;
-        p.lse[li] = (m_run[qb] + __builtin_amdgcn_logf(ell_t)) * kLn2;
       }
+      __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): the wave's own writes landed
+      // Store: lane L takes chunk L % CPO of row it*RPI + L / CPO.
+#pragma unroll
+      for (int it = 0; it < 32 / RPI; ++it) {
+        const int r = it * RPI + lane / CPO, c = lane % CPO;
+        const u32x4 v = *(const u32x4*)(slot + r * RP + ((c ^ (r & (CPO - 1))) << 4));
+        const int orow_i = row0 + 32 * qb + r;
+        if (orow_i < len) {
+          char* dst = (char*)((OT*)p.o + qbase + (long long)orow_i * p.q_rs) + pass * RP + c * 16;
+          *(u32x4*)dst = v;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);      // reads done before the slot is rewritten
     }
   }
 }
@@ -797,7 +846,7 @@ int launch_fwd(const LaunchArgs& a, void* stream) {
   p.N = a.N; p.Hq = a.Hq; p.G = a.Hq / a.Hkv;
   p.hp = plan.hp; p.rows_per_wg = plan.rows_per_wg; p.n_rblocks = plan.n_rblocks;
   p.n_hgroups = plan.n_hgroups; p.total_wg = (int)plan.total_wg;
-  p.xcd_remap = (a.in_dtype != FA_F32) && (plan.total_wg % 8 == 0);
+  p.xcd_remap = (a.in_dtype != FA_F32) && ((uint64_t)a.B * plan.n_hgroups) % 8 == 0;
   p.scale_log2 = a.scale * kLog2e;
   p.vt = a.vt; p.Hkv = a.Hkv; p.vt_ntiles = vt_tiles(a.N);
   const long long d = a.d;

@@ -347,3 +347,34 @@ def test_library_workspace_varlen_fp16():
     for b, n in enumerate(np.diff(w["cu_seqlens"])):
         L[b, :, n:] = Lref[b, :, n:] = 0.0
     _compare(w, o.double().cpu().numpy(), L, Oref, Lref)
+
+
+def test_no_score_matrix_in_device_memory():
+    """The O(N) memory claim: a call allocates no N x N scores.  With V
+    already packed the call allocates nothing beyond o and lse; the default
+    path adds only the packed-V workspace (the size of V)."""
+    import torch
+
+    import exact_io_aware_amd as fa
+    w = workloads.make_inputs("gqa_bf16")
+    q, k, v = (G.to_device(w[x], "bf16", "cuda:0") for x in "qkv")
+    o = torch.empty(q.shape, dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((w["B"], w["Hq"], w["N"]), dtype=torch.float32, device="cuda:0")
+    vt = fa.pack_v(v)
+    G.say("device memory during a call")
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    fa.fwd(q, k, None, causal=True, out=o, lse=lse, vt=vt)
+    torch.cuda.synchronize()
+    assert torch.cuda.max_memory_allocated() - base == 0
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    fa.fwd(q, k, v, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    delta = torch.cuda.max_memory_allocated() - base
+    ws = fa.workspace_bytes(w["B"], w["Hkv"], w["N"], w["d"], fa.FA_BF16)
+    assert ws == v.numel() * 2
+    assert delta <= ws + (2 << 20)
+    scores = w["B"] * w["Hq"] * w["N"] * w["N"] * 2          # one bf16 score matrix
+    assert delta * 100 < scores
