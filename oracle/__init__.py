@@ -15,6 +15,8 @@ from .exact import (  # noqa: F401
     attention_rows,
     attention_bruteforce,
     attention_tiled_online,
+    attention_qk,
+    pair_count,
     softmax_rows,
     visible_keys,
     unit_flops,

@@ -232,11 +232,14 @@ def attention_bruteforce(q, k, v, *, causal: bool, scale: float):
 
     No maximum is subtracted: every weight is ``exp(scale * q_r . k_c)``
     summed with ``math.fsum``, so it checks the stabilised oracle through a
-    different route.  Fixed layout only: q ``[B, Hq, N, d]``,
-    k/v ``[B, Hkv, N, d]``.  Returns nested lists O[b][h][r][j], L[b][h][r].
+    different route.  Fixed layout only: q ``[B, Hq, Nq, d]``,
+    k/v ``[B, Hkv, Nk, d]``; with Nq < Nk the queries are the last Nq
+    tokens (query r sees keys up to r + Nk - Nq when causal), and a row that
+    sees no key gets O = 0, L = -inf.  Returns nested lists O[b][h][r][j],
+    L[b][h][r].
     """
     B, Hq, N, d = (len(q), len(q[0]), len(q[0][0]), len(q[0][0][0]))
-    Hkv = len(k[0])
+    Hkv, Nk = len(k[0]), len(k[0][0])
     per_group = Hq // Hkv
     O, L = [], []
     for b in range(B):
@@ -247,7 +250,11 @@ def attention_bruteforce(q, k, v, *, causal: bool, scale: float):
                 g += 1
             Oh, Lh = [], []
             for r in range(N):
-                last = r if causal else N - 1
+                last = min(r + Nk - N, Nk - 1) if causal else Nk - 1
+                if last < 0:
+                    Oh.append([0.0] * d)
+                    Lh.append(-math.inf)
+                    continue
                 w = []
                 for c in range(last + 1):
                     dot = math.fsum(float(q[b][h][r][i]) * float(k[b][g][c][i])
@@ -320,6 +327,118 @@ def attention_tiled_online(q, k, v, *, causal: bool, scale: float,
     return O, L
 
 
+# ---------------------------------------------------------------------------
+# Queries against a longer key/value sequence (chunked prefill).
+
+def offset_mask(S: np.ndarray, rows: np.ndarray, cols: np.ndarray, offset: int) -> np.ndarray:
+    """Causal mask when the ``nq`` queries are the last tokens of an
+    ``nk``-token sequence: query row r is token ``r + offset`` of the
+    sequence (``offset = nk - nq``) and sees keys ``c <= r + offset``."""
+    return np.where(cols[None, :] > rows[:, None] + offset, -np.inf, S)
+
+
+def _head_rows_qk(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool,
+                  scale: float, rows: Optional[np.ndarray] = None):
+    """One head of one sequence, nq queries against nk keys, by the
+    definition.  Rows that see no key get O = 0 and L = -inf."""
+    nq, nk = q.shape[0], k.shape[0]
+    if rows is None:
+        rows = np.arange(nq)
+    rows = np.asarray(rows, dtype=np.int64)
+    O = np.zeros((rows.size, v.shape[1]), dtype=np.float64)
+    L = np.full(rows.size, -np.inf, dtype=np.float64)
+    offset = nk - nq
+    chunk = max(1, _CHUNK_BYTES // (8 * max(nk, 1)))
+    cols = np.arange(nk)
+    for s in range(0, rows.size, chunk):
+        r = rows[s:s + chunk]
+        seen = (np.minimum(r + offset, nk - 1) >= 0) if causal else np.full(r.size, nk > 0)
+        if not seen.any():
+            continue
+        r_seen = r[seen]
+        S = scores(q[r_seen], k, scale)                   # [R, nk]
+        if causal:
+            S = offset_mask(S, r_seen, cols, offset)
+        P, m, ell = softmax_rows(S)
+        idx = np.arange(s, s + r.size)[seen]
+        O[idx] = combine(P, v)
+        L[idx] = logsumexp_of(m, ell)
+    return O, L
+
+
+def _run_unit_qk(args):
+    qs, ks, vs, causal, scale = args
+    return _head_rows_qk(qs, ks, vs, causal, scale)
+
+
+def attention_qk(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, causal: bool,
+                 scale: float, cu_seqlens_q: Optional[np.ndarray] = None,
+                 cu_seqlens_k: Optional[np.ndarray] = None, workers: int = 1):
+    """Attention of nq queries against nk keys per sequence (chunked
+    prefill): returns ``(O, L)`` in float64.
+
+    The queries are the last nq tokens of an nk-token sequence, so with
+    ``causal`` query row r sees keys ``c <= r + nk - nq`` (bottom-right
+    alignment).  This is the manual chunking recipe of the French HolySheep
+    article ("Erreurs courantes", item 1): the query chunk ``[i, i+c)``
+    attends to the key prefix ``[0, i+c)``.  When nq = nk it is
+    :func:`attention`.  Rows that see no key (causal with nq > nk, or
+    nk = 0) get O = 0 and L = -inf.
+
+    Fixed layout: q ``[B, Hq, Nq, d]``, k/v ``[B, Hkv, Nk, d]``; L is
+    ``[B, Hq, Nq]``.  Varlen (both offset arrays given): q ``[Tq, Hq, d]``,
+    k/v ``[Tk, Hkv, d]``; L is ``[B, Hq, max nq]`` with NaN past each
+    sequence's query count.
+    """
+    if (cu_seqlens_q is None) != (cu_seqlens_k is None):
+        raise ValueError("give both cu_seqlens_q and cu_seqlens_k, or neither")
+    Hq, Hkv = q.shape[1], k.shape[1]
+    if cu_seqlens_q is None:
+        B = q.shape[0]
+        units = [(b, h) for b in range(B) for h in range(Hq)]
+        jobs = [(q[b, h], k[b, _group(h, Hq, Hkv)], v[b, _group(h, Hq, Hkv)], causal, scale)
+                for b, h in units]
+    else:
+        B = len(cu_seqlens_q) - 1
+        if len(cu_seqlens_k) != B + 1:
+            raise ValueError("cu_seqlens_q and cu_seqlens_k differ in length")
+        units = [(b, h) for b in range(B) for h in range(Hq)]
+        jobs = []
+        for b, h in units:
+            sq, eq = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])
+            sk, ek = int(cu_seqlens_k[b]), int(cu_seqlens_k[b + 1])
+            g = _group(h, Hq, Hkv)
+            jobs.append((q[sq:eq, h], k[sk:ek, g], v[sk:ek, g], causal, scale))
+    if workers <= 1:
+        results = [_run_unit_qk(j) for j in jobs]
+    else:
+        with ProcessPoolExecutor(max_workers=workers, initializer=_one_blas_thread) as ex:
+            results = list(ex.map(_run_unit_qk, jobs, chunksize=1))
+    O = np.empty(q.shape, dtype=np.float64)
+    if cu_seqlens_q is None:
+        L = np.empty(q.shape[:3], dtype=np.float64)
+        for (b, h), (o, l) in zip(units, results):
+            O[b, h] = o
+            L[b, h] = l
+        return O, L
+    lens = np.diff(np.asarray(cu_seqlens_q, dtype=np.int64))
+    L = np.full((B, Hq, int(lens.max()) if B else 0), np.nan)
+    for (b, h), (o, l) in zip(units, results):
+        s = int(cu_seqlens_q[b])
+        O[s:s + o.shape[0], h] = o
+        L[b, h, :o.shape[0]] = l
+    return O, L
+
+
+def pair_count(nq: int, nk: int, causal: bool) -> int:
+    """Visible (query, key) pairs of one head of one sequence with nq
+    queries at the end of an nk-token sequence."""
+    if not causal:
+        return nq * nk
+    off = nk - nq
+    return sum(max(0, min(r + off + 1, nk)) for r in range(nq))
+
+
 def unit_flops(n: int, d: int, causal: bool) -> float:
     """Algorithmic FLOP of one head of one sequence: the two contractions
     over the visible (query, key) pairs, 2*d each."""
@@ -336,6 +455,6 @@ def default_workers() -> int:
 
 __all__ = [
     "attention", "attention_rows", "attention_bruteforce",
-    "attention_tiled_online", "softmax_rows", "visible_keys",
-    "unit_flops", "default_workers",
+    "attention_tiled_online", "attention_qk", "pair_count", "softmax_rows",
+    "visible_keys", "unit_flops", "default_workers",
 ]

@@ -253,3 +253,114 @@ CHECKS = [
     check_shift, check_gqa_equals_repeated, check_varlen_equals_fixed,
     check_large_scale, check_convex,
 ]
+
+
+# ---------------------------------------------------------------------------
+# Queries against a longer key/value sequence (chunked prefill).  Each check
+# takes ``attn_qk(q, k, v, *, causal, scale, cu_seqlens_q=None,
+# cu_seqlens_k=None) -> (O, L)``.
+
+def _rand_qk(seed, B=2, Hq=4, Hkv=2, Nq=5, Nk=11, d=6):
+    r = _rng(seed)
+    return (r.standard_normal((B, Hq, Nq, d)), r.standard_normal((B, Hkv, Nk, d)),
+            r.standard_normal((B, Hkv, Nk, d)))
+
+
+def check_qk_chunk_recipe(attn_qk):
+    """The manual chunking recipe (French HolySheep article, "Erreurs
+    courantes", item 1): the query chunk [i, i+c) of a sequence, attending to
+    the key prefix [0, i+c), gives rows i .. i+c-1 of attention over the
+    whole sequence (computed by the pinned full-sequence oracle)."""
+    from oracle import attention
+    q, k, v = _rand(61, B=2, Hq=4, Hkv=2, N=13, d=5)
+    worst = 0.0
+    for causal in (True, False):
+        Of, Lf = attention(q, k, v, causal=causal, scale=0.37)
+        for i, c in ((0, 13), (0, 4), (4, 5), (9, 4), (12, 1)):
+            end = i + c if causal else 13
+            O, L = attn_qk(q[:, :, i:i + c], k[:, :, :end], v[:, :, :end],
+                           causal=causal, scale=0.37)
+            worst = max(worst, _err(O, Of[:, :, i:i + c]), _err(L, Lf[:, :, i:i + c]))
+    return worst
+
+
+def check_qk_bruteforce(attn_qk):
+    """Pure-Python sums (no max subtraction) with the queries at the end of
+    a longer key sequence."""
+    from oracle import attention_bruteforce
+    worst = 0.0
+    for causal in (False, True):
+        q, k, v = _rand_qk(63 + causal)
+        O, L = attn_qk(q, k, v, causal=causal, scale=0.52)
+        Ob, Lb = attention_bruteforce(q.tolist(), k.tolist(), v.tolist(),
+                                      causal=causal, scale=0.52)
+        worst = max(worst, _err(O, Ob), _err(L, Lb))
+    return worst
+
+
+def check_qk_library(attn_qk):
+    """torch's scaled_dot_product_attention with an explicit boolean mask
+    (key c visible to query r iff c <= r + Nk - Nq), float64 on the CPU."""
+    import torch
+    import torch.nn.functional as F
+    worst = 0.0
+    for causal in (False, True):
+        q, k, v = _rand_qk(65 + causal, B=2, Hq=6, Hkv=3, Nq=19, Nk=45, d=16)
+        O, L = attn_qk(q, k, v, causal=causal, scale=0.19)
+        tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+        Nq, Nk = q.shape[2], k.shape[2]
+        vis = torch.arange(Nk)[None, :] <= torch.arange(Nq)[:, None] + (Nk - Nq)
+        mask = vis if causal else None
+        kr = tk.repeat_interleave(2, dim=1)
+        vr = tv.repeat_interleave(2, dim=1)
+        To = F.scaled_dot_product_attention(tq, kr, vr, attn_mask=mask, scale=0.19)
+        S = 0.19 * torch.matmul(tq, kr.transpose(-1, -2))
+        if causal:
+            S = S.masked_fill(~vis, -math.inf)
+        worst = max(worst, _err(O, To.numpy()), _err(L, torch.logsumexp(S, -1).numpy()))
+    return worst
+
+
+def check_qk_no_visible_key(attn_qk):
+    """Causal with more queries than keys: query r sees keys up to
+    r + Nk - Nq, so the first Nq - Nk rows see none (O = 0, L = -inf) and
+    the rest are the Nk-token causal attention (pinned full oracle)."""
+    from oracle import attention
+    q, k, v = _rand_qk(67, Nq=9, Nk=4)
+    O, L = attn_qk(q, k, v, causal=True, scale=0.8)
+    worst = 0.0
+    if not (np.isneginf(L[:, :, :5]).all()):
+        return math.inf
+    worst = max(worst, float(np.abs(O[:, :, :5]).max()))
+    Of, Lf = attention(q[:, :, 5:], k, v, causal=True, scale=0.8)
+    return max(worst, _err(O[:, :, 5:], Of), _err(L[:, :, 5:], Lf))
+
+
+def check_qk_varlen(attn_qk):
+    """Packed sequences with their own query and key counts = each sequence
+    alone; L rows past a sequence's query count stay NaN."""
+    r = _rng(69)
+    Hq, Hkv, d = 4, 2, 5
+    nq, nk = [3, 1, 6], [7, 1, 6]
+    cq = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    ck = np.concatenate([[0], np.cumsum(nk)]).astype(np.int32)
+    q = r.standard_normal((cq[-1], Hq, d))
+    k = r.standard_normal((ck[-1], Hkv, d))
+    v = r.standard_normal((ck[-1], Hkv, d))
+    worst = 0.0
+    for causal in (False, True):
+        O, L = attn_qk(q, k, v, causal=causal, scale=0.6, cu_seqlens_q=cq, cu_seqlens_k=ck)
+        for b in range(3):
+            qs = q[cq[b]:cq[b + 1]].transpose(1, 0, 2)[None]
+            ks = k[ck[b]:ck[b + 1]].transpose(1, 0, 2)[None]
+            vs = v[ck[b]:ck[b + 1]].transpose(1, 0, 2)[None]
+            Ob, Lb = attn_qk(qs, ks, vs, causal=causal, scale=0.6)
+            worst = max(worst, _err(O[cq[b]:cq[b + 1]], Ob[0].transpose(1, 0, 2)),
+                        _err(L[b, :, :nq[b]], Lb[0]))
+            if not np.isnan(L[b, :, nq[b]:]).all():
+                return math.inf
+    return worst
+
+
+QK_CHECKS = [check_qk_chunk_recipe, check_qk_bruteforce, check_qk_library,
+             check_qk_no_visible_key, check_qk_varlen]

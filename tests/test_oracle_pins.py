@@ -127,3 +127,59 @@ def test_workload_shapes():
         x = workloads.make_inputs(name)
         assert x["q"].shape == (wl.B, wl.Hq, wl.N, wl.d)
         assert x["k"].shape == (wl.B, wl.Hkv, wl.N, wl.d)
+
+
+# ---------------------------------------------------------------------------
+# Queries against a longer key/value sequence (chunked prefill).
+
+@pytest.mark.parametrize("check", C.QK_CHECKS, ids=lambda f: f.__name__)
+def test_oracle_qk_pin(check):
+    assert check(oracle.attention_qk) <= C.TOL
+
+
+def _qk_mutants():
+    return {
+        "top_left": ("offset_mask", lambda S, r, c, off: np.where(
+            c[None, :] > r[:, None], -np.inf, S)),
+        "offset_plus_one": ("offset_mask", lambda S, r, c, off: np.where(
+            c[None, :] > r[:, None] + off + 1, -np.inf, S)),
+        "offset_reversed": ("offset_mask", lambda S, r, c, off: np.where(
+            c[None, :] > r[:, None] - off, -np.inf, S)),
+        "unseen_rows_zero_lse": ("_head_rows_qk", None),
+        "scores_of_prefix_only": ("scores", None),
+    }
+
+
+@pytest.mark.parametrize("name", sorted(_qk_mutants()))
+def test_qk_pins_catch_planted_mistake(name, monkeypatch):
+    attr, fn = _qk_mutants()[name]
+    if name == "unseen_rows_zero_lse":
+        orig = exact._head_rows_qk
+
+        def fn(q, k, v, causal, scale, rows=None):
+            O, L = orig(q, k, v, causal, scale, rows)
+            return O, np.where(np.isneginf(L), 0.0, L)
+    elif name == "scores_of_prefix_only":
+        orig_s = exact.scores
+
+        def fn(q, k, scale):          # keys past the query count ignored
+            S = orig_s(q, k, scale)
+            S[:, q.shape[0]:] = -np.inf if q.shape[0] < k.shape[0] else S[:, q.shape[0]:]
+            return S
+    monkeypatch.setattr(exact, attr, fn)
+    worst = 0.0
+    for check in C.QK_CHECKS:
+        try:
+            worst = max(worst, check(oracle.attention_qk))
+        except Exception:
+            worst = np.inf
+        if worst > C.TOL:
+            break
+    assert worst > C.TOL, f"no pin caught the planted mistake {name}"
+
+
+def test_pair_count():
+    for nq, nk in ((5, 5), (3, 9), (9, 4), (1, 7), (7, 0)):
+        brute = sum(1 for r in range(nq) for c in range(nk) if c <= r + nk - nq)
+        assert oracle.pair_count(nq, nk, True) == brute
+        assert oracle.pair_count(nq, nk, False) == nq * nk
