@@ -38,6 +38,11 @@ def load() -> ctypes.CDLL:
     lib.fa_pack_v.restype = i
     lib.fa_fwd_packed.argtypes = [vp, vp, vp, z, vp, vp, i, i, i, i, i, i, f, vp, vp, i, i]
     lib.fa_fwd_packed.restype = i
+    lib.fa_fwd_kv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, vp, i, i]
+    lib.fa_fwd_kv.restype = i
+    lib.fa_fwd_kv_packed.argtypes = [vp, vp, vp, z, vp, vp, i, i, i, i, i, i, i, f, vp, vp, vp,
+                                     i, i]
+    lib.fa_fwd_kv_packed.restype = i
     lib.fa_fwd_check.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i, i]
     lib.fa_fwd_check.restype = i
     lib.fa_kernel_name.argtypes = [i, i, i, i, i]
@@ -98,3 +103,17 @@ def fwd_packed_raw(q, k, vt, vt_bytes, o, lse, B, Hq, Hkv, N, d, causal, scale,
     """fa_fwd_packed with raw integer device addresses and a raw hipStream_t."""
     return load().fa_fwd_packed(q, k, vt, vt_bytes, o, lse, B, Hq, Hkv, N, d, int(causal),
                                 scale, cu_seqlens, stream, in_dtype, out_dtype)
+
+
+def fwd_kv_raw(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, cu_q, cu_k,
+               stream, in_dtype, out_dtype) -> int:
+    """fa_fwd_kv with raw integer device addresses and a raw hipStream_t."""
+    return load().fa_fwd_kv(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, int(causal), scale,
+                            cu_q, cu_k, stream, in_dtype, out_dtype)
+
+
+def fwd_kv_packed_raw(q, k, vt, vt_bytes, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale,
+                      cu_q, cu_k, stream, in_dtype, out_dtype) -> int:
+    """fa_fwd_kv_packed with raw integer device addresses and a raw hipStream_t."""
+    return load().fa_fwd_kv_packed(q, k, vt, vt_bytes, o, lse, B, Hq, Hkv, Nq, Nk, d,
+                                   int(causal), scale, cu_q, cu_k, stream, in_dtype, out_dtype)

@@ -36,8 +36,8 @@ int fa_fwd_check(const void* q, const void* k, const void* v, const void* o,
                  const float* lse, int B, int Hq, int Hkv, int N, int d,
                  int causal, float scale, const int* cu_seqlens, int in_dtype,
                  int out_dtype) {
-  return fa::check_args(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale,
-                        cu_seqlens, in_dtype, out_dtype);
+  return fa::check_args(q, k, v, o, lse, B, Hq, Hkv, N, N, d, causal, scale,
+                        cu_seqlens, cu_seqlens, in_dtype, out_dtype);
 }
 
 size_t fa_workspace_bytes(int B, int Hkv, int N, int d, int in_dtype) {
@@ -55,44 +55,60 @@ int fa_pack_v(const void* v, void* vt, size_t vt_bytes, int B, int Hkv, int N, i
   return fa::launch_vt_pack(v, vt, B, Hkv, N, d, cu_seqlens, in_dtype, stream);
 }
 
-int fa_fwd_packed(const void* q, const void* k, const void* vt, size_t vt_bytes, void* o,
-                  float* lse, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
-                  const int* cu_seqlens, void* stream, int in_dtype, int out_dtype) {
-  int st = fa::check_packed_args(q, k, vt, vt_bytes, o, lse, B, Hq, Hkv, N, d, causal, scale,
-                                 cu_seqlens, in_dtype, out_dtype);
+int fa_fwd_kv_packed(const void* q, const void* k, const void* vt, size_t vt_bytes, void* o,
+                     float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                     float scale, const int* cu_seqlens_q, const int* cu_seqlens_k,
+                     void* stream, int in_dtype, int out_dtype) {
+  int st = fa::check_packed_args(q, k, vt, vt_bytes, o, lse, B, Hq, Hkv, Nq, Nk, d, causal,
+                                 scale, cu_seqlens_q, cu_seqlens_k, in_dtype, out_dtype);
   if (st != FA_OK) return st;
   st = device_status();
   if (st != FA_OK) return st;
-  fa::LaunchArgs a{q, k, nullptr, o, lse, vt, cu_seqlens, B, Hq, Hkv, N, d, causal,
-                   scale, in_dtype, out_dtype};
+  fa::LaunchArgs a{q, k, nullptr, o, lse, vt, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, Nq, Nk,
+                   d, causal, scale, in_dtype, out_dtype};
   return fa::launch_fwd(a, stream);
 }
 
-int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-           int B, int Hq, int Hkv, int N, int d, int causal, float scale,
-           const int* cu_seqlens, void* stream, int in_dtype, int out_dtype) {
-  int st = fa::check_args(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale,
-                          cu_seqlens, in_dtype, out_dtype);
+int fa_fwd_packed(const void* q, const void* k, const void* vt, size_t vt_bytes, void* o,
+                  float* lse, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                  const int* cu_seqlens, void* stream, int in_dtype, int out_dtype) {
+  return fa_fwd_kv_packed(q, k, vt, vt_bytes, o, lse, B, Hq, Hkv, N, N, d, causal, scale,
+                          cu_seqlens, cu_seqlens, stream, in_dtype, out_dtype);
+}
+
+int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+              const int* cu_seqlens_q, const int* cu_seqlens_k, void* stream,
+              int in_dtype, int out_dtype) {
+  int st = fa::check_args(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale,
+                          cu_seqlens_q, cu_seqlens_k, in_dtype, out_dtype);
   if (st != FA_OK) return st;
   st = device_status();
   if (st != FA_OK) return st;
-  fa::LaunchArgs a{q, k, v, o, lse, nullptr, cu_seqlens, B, Hq, Hkv, N, d, causal,
-                   scale, in_dtype, out_dtype};
+  fa::LaunchArgs a{q, k, v, o, lse, nullptr, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, Nq, Nk,
+                   d, causal, scale, in_dtype, out_dtype};
   if (in_dtype == FA_F32) return fa::launch_fwd(a, stream);
   // 16-bit inputs: pack V^T into a stream-ordered workspace, run, release.
-  const uint64_t need = fa::workspace_bytes(B, Hkv, N, d, in_dtype);
+  const uint64_t need = fa::workspace_bytes(B, Hkv, Nk, d, in_dtype);
   if (need / (128ull * (uint64_t)d) > (uint64_t)INT32_MAX || need > (uint64_t)SIZE_MAX)
     return FA_ERR_SHAPE;
   void* ws = nullptr;
   if (hipMallocAsync(&ws, (size_t)need, (hipStream_t)stream) != hipSuccess || !ws)
     return FA_ERR_ALLOC;
-  st = fa::launch_vt_pack(v, ws, B, Hkv, N, d, cu_seqlens, in_dtype, stream);
+  st = fa::launch_vt_pack(v, ws, B, Hkv, Nk, d, cu_seqlens_k, in_dtype, stream);
   if (st == FA_OK) {
     a.vt = ws;
     st = fa::launch_fwd(a, stream);
   }
   if (hipFreeAsync(ws, (hipStream_t)stream) != hipSuccess && st == FA_OK) st = FA_ERR_LAUNCH;
   return st;
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+           const int* cu_seqlens, void* stream, int in_dtype, int out_dtype) {
+  return fa_fwd_kv(q, k, v, o, lse, B, Hq, Hkv, N, N, d, causal, scale, cu_seqlens,
+                   cu_seqlens, stream, in_dtype, out_dtype);
 }
 
 const char* fa_kernel_name(int in_dtype, int d, int causal, int varlen,

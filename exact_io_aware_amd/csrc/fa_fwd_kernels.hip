@@ -66,13 +66,18 @@ constexpr float kLn2 = 0.6931471805599453f;
 // moved and the accumulators rescaled: every P is then <= 2^15, inside the
 // fp16 range, and the sums stay far from fp32 overflow.
 constexpr float kSumLimit = 32768.0f;
+// Running maximum before any key has been seen.  Finite, so that a masked
+// score (-inf) minus it stays -inf (P = 0) instead of becoming NaN, while any
+// visible score minus it overflows and forces the first real maximum in.
+constexpr float kNoMax = -3.402823466e38f;
 // Immediate of s_waitcnt vmcnt(n) with the other counters left alone.
 constexpr int waitcnt_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 struct FwdParams {
   const void* q; const void* k; const void* v; void* o; float* lse;
-  const int* cu_seqlens;
-  int N, Hq, G;            // max length, query heads, Hq / Hkv
+  const int* cu_seqlens;   // query offsets (varlen)
+  const int* cu_seqlens_k; // key/value offsets (varlen)
+  int N, Nk, Hq, G;        // max query count, max key count, query heads, Hq / Hkv
   int hp, rows_per_wg, n_rblocks, n_hgroups, total_wg, xcd_remap;
   float scale_log2;        // scale * log2(e)
   const void* vt;          // packed V^T tiles (16-bit inputs), see fa_vt_pack
@@ -282,23 +287,29 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
   const int h = hgrp * p.hp + (wave % p.hp);
   const int kvh = (hgrp * p.hp) / p.G;
 
-  int seq0 = 0, len = p.N;
+  // Query rows [0, len) and keys [0, len_k) of sequence b.  The queries are
+  // the last len tokens of the sequence: with the causal mask, row r sees
+  // keys c <= r + off, off = len_k - len.
+  int seq0 = 0, len = p.N, seq0_k = 0, len_k = p.Nk;
   if (VARLEN) {
     seq0 = p.cu_seqlens[b];
     len = p.cu_seqlens[b + 1] - seq0;
+    seq0_k = p.cu_seqlens_k[b];
+    len_k = p.cu_seqlens_k[b + 1] - seq0_k;
   }
+  const int off = len_k - len;
   const int wg_row0 = rb * p.rows_per_wg;
   if (wg_row0 >= len) return;                 // uniform over the workgroup
   const int row0 = wg_row0 + (wave / p.hp) * WR;
   const int wg_rows_end = min(wg_row0 + p.rows_per_wg, len);
-  const int kv_end = CAUSAL ? wg_rows_end : len;
+  const int kv_end = CAUSAL ? max(0, min(wg_rows_end + off, len_k)) : len_k;
   const bool active = row0 < len;
-  const int wave_kv_end = CAUSAL ? min(row0 + WR, len) : len;
+  const int wave_kv_end = CAUSAL ? max(0, min(min(row0 + WR, len) + off, len_k)) : len_k;
   const int wave_nblk = active ? (wave_kv_end + 31) / 32 : 0;  // blocks this wave needs
 
   const long long qbase = (VARLEN ? (long long)seq0 * p.q_rs : (long long)b * p.q_bs) +
                           (long long)h * p.q_hs;
-  const long long kvbase = (VARLEN ? (long long)seq0 * p.kv_rs : (long long)b * p.kv_bs) +
+  const long long kvbase = (VARLEN ? (long long)seq0_k * p.kv_rs : (long long)b * p.kv_bs) +
                            (long long)kvh * p.kv_hs;
   const char* kp = (const char*)((const T*)p.k + kvbase);
   const uint32_t kv_rs_bytes = (uint32_t)p.kv_rs * 2;
@@ -321,8 +332,8 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
     const int kb = tile * BC;
     // readfirstlane keeps the clamp (a VALU med3) in a scalar register: the
     // resource of a buffer load must be wave-uniform.
-    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(len - kb, BC)));
-    const rsrc_t r = make_rsrc(kp + (long long)min(kb, len) * kv_rs_bytes,
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(len_k - kb, BC)));
+    const rsrc_t r = make_rsrc(kp + (long long)min(kb, len_k) * kv_rs_bytes,
                                (uint32_t)rows * kv_rs_bytes);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) lds_load16(r, dst_base + (NT * i + 64 * wave) * 16, koff[i]);
@@ -330,7 +341,7 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
   const char* vtp = (const char*)p.vt + (long long)(b * p.Hkv + kvh) * p.vt_ntiles * TILE_BYTES;
   auto gload_vt = [&](int tile, char* dst_base) __attribute__((always_inline)) {
     // A V^T tile is contiguous; tiles past the sequence end read zeros.
-    const int live_tile = __builtin_amdgcn_readfirstlane(tile * BC < len ? 1 : 0);
+    const int live_tile = __builtin_amdgcn_readfirstlane(tile * BC < len_k ? 1 : 0);
     const rsrc_t r = make_rsrc(vtp + (long long)min(tile, p.vt_ntiles) * TILE_BYTES,
                                live_tile ? (uint32_t)TILE_BYTES : 0u);
 #pragma unroll
@@ -379,7 +390,7 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
   for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
     for (int i = 0; i < DB; ++i) oacc[qb][i] = f32x16{};
-    m_run[qb] = -__builtin_inff();
+    m_run[qb] = kNoMax;
     ell[qb] = 0.0f;
   }
   const float sl2 = p.scale_log2;
@@ -401,13 +412,14 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
   // diagonal or the end of the sequence.
   auto mask = [&](int i, f32x16 (&s)[QB]) __attribute__((always_inline)) {
     const int kb = i * 32;
-    if ((CAUSAL && kb + 31 > row0) || (kb + 32 > len)) {
+    if ((CAUSAL && kb + 31 > row0 + off) || (kb + 32 > len_k)) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = kb + 8 * (e >> 2) + 4 * hf + (e & 3);
-          if ((CAUSAL && key > row0 + 32 * qb + l32) || key >= len) s[qb][e] = -__builtin_inff();
+          if ((CAUSAL && key > row0 + 32 * qb + l32 + off) || key >= len_k)
+            s[qb][e] = -__builtin_inff();
         }
     }
   };
@@ -446,7 +458,7 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
         float mx = -__builtin_inff();
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[qb][e]);
-        // -inf only for rows with no visible key yet, which keep m = -inf.
+        // mx = -inf only for rows with no visible key yet, which keep kNoMax.
         const float m_new = fmaxf(m_run[qb], halves_max(mx) * sl2);
         const float alpha = m_new == m_run[qb] ? 1.0f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
         ell[qb] *= alpha;
@@ -591,7 +603,9 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float ell_t = halves_sum(ell[qb]);
-    const float inv = 1.0f / ell_t;
+    // A row that sees no key (causal, more queries than keys) has ell = 0:
+    // O = 0 and L = -inf.
+    const float inv = ell_t > 0.0f ? 1.0f / ell_t : 0.0f;
     const int qrow = row0 + 32 * qb + l32;
     if (hf == 0 && qrow < len) {
       const long long li = ((long long)b * p.Hq + h) * p.N + qrow;
@@ -657,22 +671,26 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_f32(FwdParams p) {
   const int b = unit / p.Hq;
   const int h = unit - b * p.Hq;
   const int kvh = h / p.G;
-  int seq0 = 0, len = p.N;
+  int seq0 = 0, len = p.N, seq0_k = 0, len_k = p.Nk;
   if (VARLEN) {
     seq0 = p.cu_seqlens[b];
     len = p.cu_seqlens[b + 1] - seq0;
+    seq0_k = p.cu_seqlens_k[b];
+    len_k = p.cu_seqlens_k[b + 1] - seq0_k;
   }
+  const int off = len_k - len;                // row r sees keys c <= r + off (causal)
   const int wg_row0 = rb * 128;
   if (wg_row0 >= len) return;
   const int row0 = wg_row0 + wave * 32;
-  const int kv_end = CAUSAL ? min(wg_row0 + 128, len) : len;
+  const int kv_end = CAUSAL ? max(0, min(min(wg_row0 + 128, len) + off, len_k)) : len_k;
   const int ntiles = (kv_end + BC - 1) / BC;
   const bool active = row0 < len;
-  const int wave_ntiles = active ? ((CAUSAL ? min(row0 + 32, len) : len) + BC - 1) / BC : 0;
+  const int wave_kv_end = CAUSAL ? max(0, min(min(row0 + 32, len) + off, len_k)) : len_k;
+  const int wave_ntiles = active ? (wave_kv_end + BC - 1) / BC : 0;
 
   const long long qbase = (VARLEN ? (long long)seq0 * p.q_rs : (long long)b * p.q_bs) +
                           (long long)h * p.q_hs;
-  const long long kvbase = (VARLEN ? (long long)seq0 * p.kv_rs : (long long)b * p.kv_bs) +
+  const long long kvbase = (VARLEN ? (long long)seq0_k * p.kv_rs : (long long)b * p.kv_bs) +
                            (long long)kvh * p.kv_hs;
   const float* qp = (const float*)p.q + qbase;
   const float* kp = (const float*)p.k + kvbase;
@@ -688,13 +706,13 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_f32(FwdParams p) {
   f32x16 oacc[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
-  float m_run = -__builtin_inff(), ell = 0.0f;
+  float m_run = kNoMax, ell = 0.0f;
 
   for (int j = 0; j < ntiles; ++j) {
     const int kb = j * BC;
     for (int e = tid; e < BC * D; e += 256) {
       const int r = e / D, c = e % D;
-      const long long row = (long long)min(kb + r, len - 1) * p.kv_rs;
+      const long long row = (long long)min(kb + r, len_k - 1) * p.kv_rs;
       ks[r * KP + c] = kp[row + c];
       vs[r * D + c] = vp[row + c];
     }
@@ -704,12 +722,12 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_f32(FwdParams p) {
 #pragma unroll
       for (int t = 0; t < DK; ++t)
         s = __builtin_amdgcn_mfma_f32_32x32x2f32(ks[l32 * KP + 2 * t + hf], qf[t], s, 0, 0, 0);
-      const bool need_mask = (CAUSAL && kb + BC - 1 > row0) || (kb + BC > len);
+      const bool need_mask = (CAUSAL && kb + BC - 1 > row0 + off) || (kb + BC > len_k);
       if (need_mask) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = kb + 8 * (i >> 2) + 4 * hf + (i & 3);
-          if ((CAUSAL && key > qrow) || key >= len) s[i] = -__builtin_inff();
+          if ((CAUSAL && key > qrow + off) || key >= len_k) s[i] = -__builtin_inff();
         }
       }
       // Online softmax against the reference maximum, moved (with an exact
@@ -754,7 +772,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_f32(FwdParams p) {
   }
   if (!active) return;
   const float ell_t = halves_sum(ell);
-  const float inv = 1.0f / ell_t;
+  const float inv = ell_t > 0.0f ? 1.0f / ell_t : 0.0f;   // no visible key: O = 0
   if (qrow < len) {
     float* orow = (float*)p.o + qbase + (long long)qrow * p.q_rs;
 #pragma unroll
@@ -842,20 +860,20 @@ int launch_fwd(const LaunchArgs& a, void* stream) {
 
   FwdParams p;
   p.q = a.q; p.k = a.k; p.v = a.v; p.o = a.o; p.lse = a.lse;
-  p.cu_seqlens = a.cu_seqlens;
-  p.N = a.N; p.Hq = a.Hq; p.G = a.Hq / a.Hkv;
+  p.cu_seqlens = a.cu_seqlens; p.cu_seqlens_k = a.cu_seqlens_k;
+  p.N = a.N; p.Nk = a.Nk; p.Hq = a.Hq; p.G = a.Hq / a.Hkv;
   p.hp = plan.hp; p.rows_per_wg = plan.rows_per_wg; p.n_rblocks = plan.n_rblocks;
   p.n_hgroups = plan.n_hgroups; p.total_wg = (int)plan.total_wg;
   p.xcd_remap = (a.in_dtype != FA_F32) && ((uint64_t)a.B * plan.n_hgroups) % 8 == 0;
   p.scale_log2 = a.scale * kLog2e;
-  p.vt = a.vt; p.Hkv = a.Hkv; p.vt_ntiles = vt_tiles(a.N);
+  p.vt = a.vt; p.Hkv = a.Hkv; p.vt_ntiles = vt_tiles(a.Nk);
   const long long d = a.d;
   if (varlen) {
     p.q_bs = 0; p.q_hs = d; p.q_rs = (long long)a.Hq * d;
     p.kv_bs = 0; p.kv_hs = d; p.kv_rs = (long long)a.Hkv * d;
   } else {
     p.q_rs = d; p.q_hs = (long long)a.N * d; p.q_bs = (long long)a.Hq * a.N * d;
-    p.kv_rs = d; p.kv_hs = (long long)a.N * d; p.kv_bs = (long long)a.Hkv * a.N * d;
+    p.kv_rs = d; p.kv_hs = (long long)a.Nk * d; p.kv_bs = (long long)a.Hkv * a.Nk * d;
   }
   void* args[] = {&p};
   const hipError_t e = hipLaunchKernel((const void*)var->fn, dim3((unsigned)plan.total_wg),

@@ -59,26 +59,28 @@ inline uint64_t grid_size(int B, int Hq, int Hkv, int N, int d, int in_dtype) {
   return make_plan(B, Hq, Hkv, N, d, in_dtype).total_wg;
 }
 
-// Checks of fa_fwd's arguments.  v_bytes is the extent of v used for the
-// overlap test with o (0: the size of V itself).
+// Checks of the attention arguments (Nq queries, Nk keys per sequence; the
+// fa_fwd form has Nq = Nk and one offset array).  v_bytes is the extent of
+// v used for the overlap test with o (0: the size of V itself).
 int check_args(const void* q, const void* k, const void* v, const void* o,
-               const float* lse, int B, int Hq, int Hkv, int N, int d,
-               int causal, float scale, const int* cu_seqlens, int in_dtype,
-               int out_dtype, uint64_t v_bytes = 0);
+               const float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+               int causal, float scale, const int* cu_seqlens_q, const int* cu_seqlens_k,
+               int in_dtype, int out_dtype, uint64_t v_bytes = 0);
 
-// Checks of fa_fwd_packed's and fa_pack_v's arguments.
+// Checks of the packed-V attention arguments (vt from fa_pack_v).
 int check_packed_args(const void* q, const void* k, const void* vt, uint64_t vt_bytes,
-                      const void* o, const float* lse, int B, int Hq, int Hkv, int N, int d,
-                      int causal, float scale, const int* cu_seqlens, int in_dtype,
-                      int out_dtype);
+                      const void* o, const float* lse, int B, int Hq, int Hkv, int Nq, int Nk,
+                      int d, int causal, float scale, const int* cu_seqlens_q,
+                      const int* cu_seqlens_k, int in_dtype, int out_dtype);
 int check_pack_args(const void* v, const void* vt, uint64_t vt_bytes, int B, int Hkv, int N,
                     int d, const int* cu_seqlens, int in_dtype);
 
 struct LaunchArgs {
   const void* q; const void* k; const void* v; void* o; float* lse;
   const void* vt;      // packed V^T (16-bit inputs; v is then unused)
-  const int* cu_seqlens;
-  int B, Hq, Hkv, N, d, causal;
+  const int* cu_seqlens;    // query offsets (varlen), or nullptr
+  const int* cu_seqlens_k;  // key/value offsets (varlen), or nullptr
+  int B, Hq, Hkv, N, Nk, d, causal;   // N: max query count, Nk: max key count
   float scale;
   int in_dtype, out_dtype;
 };

@@ -1,4 +1,4 @@
-// Argument checks of fa_fwd, fa_pack_v and fa_fwd_packed (include/fa.h).  Pure C++: no HIP call, so the
+// Argument checks of the attention entry points and fa_pack_v (include/fa.h).  Pure C++: no HIP call, so the
 // checks run, and are tested, on a machine without a GPU.
 #include <cmath>
 #include <cstdint>
@@ -25,11 +25,12 @@ bool overlap(uintptr_t a, uint64_t na, uintptr_t b, uint64_t nb) {
 }  // namespace
 
 int check_args(const void* q, const void* k, const void* v, const void* o,
-               const float* lse, int B, int Hq, int Hkv, int N, int d,
-               int causal, float scale, const int* cu_seqlens, int in_dtype,
-               int out_dtype, uint64_t v_bytes) {
+               const float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+               int causal, float scale, const int* cu_seqlens_q, const int* cu_seqlens_k,
+               int in_dtype, int out_dtype, uint64_t v_bytes) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || (causal != 0 && causal != 1))
+  if ((cu_seqlens_q == nullptr) != (cu_seqlens_k == nullptr)) return FA_ERR_NULL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || (causal != 0 && causal != 1))
     return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
   if (Hq % Hkv != 0) return FA_ERR_GQA;
@@ -38,23 +39,26 @@ int check_args(const void* q, const void* k, const void* v, const void* o,
   if (out_dtype != FA_F32 && out_dtype != in_dtype) return FA_ERR_DTYPE;
   if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_SCALE;
 
-  // Element counts; the packed layout's token count is bounded by B * N.
-  uint64_t rows, qn, kn, ln;
-  if (!mul_ok((uint64_t)B, (uint64_t)N, &rows)) return FA_ERR_SHAPE;
+  // Element counts; the packed layout's token counts are bounded by B * Nq
+  // and B * Nk.
+  uint64_t rows, krows, qn, kn, ln;
+  if (!mul_ok((uint64_t)B, (uint64_t)Nq, &rows)) return FA_ERR_SHAPE;
+  if (!mul_ok((uint64_t)B, (uint64_t)Nk, &krows)) return FA_ERR_SHAPE;
   if (!mul_ok(rows, (uint64_t)Hq * (uint64_t)d, &qn)) return FA_ERR_SHAPE;
-  if (!mul_ok(rows, (uint64_t)Hkv * (uint64_t)d, &kn)) return FA_ERR_SHAPE;
+  if (!mul_ok(krows, (uint64_t)Hkv * (uint64_t)d, &kn)) return FA_ERR_SHAPE;
   if (!mul_ok(rows, (uint64_t)Hq, &ln)) return FA_ERR_SHAPE;
   if (v_bytes == 0) v_bytes = kn * elem_size(in_dtype);
   // Kernel index arithmetic uses 64-bit element offsets and 32-bit row,
   // head and workgroup counts.
-  if (qn > (uint64_t)INT64_MAX / 4 || ln > (uint64_t)INT32_MAX * 64)
+  if (qn > (uint64_t)INT64_MAX / 4 || kn > (uint64_t)INT64_MAX / 4 ||
+      ln > (uint64_t)INT32_MAX * 64)
     return FA_ERR_SHAPE;
-  if (grid_size(B, Hq, Hkv, N, d, in_dtype) > (uint64_t)INT32_MAX)
+  if (grid_size(B, Hq, Hkv, Nq, d, in_dtype) > (uint64_t)INT32_MAX)
     return FA_ERR_SHAPE;
 
   auto mis = [](const void* p, uintptr_t a) { return ((uintptr_t)p) % a != 0; };
   if (mis(q, 16) || mis(k, 16) || mis(v, 16) || mis(o, 16) || mis(lse, 4) ||
-      (cu_seqlens && mis(cu_seqlens, 4)))
+      (cu_seqlens_q && mis(cu_seqlens_q, 4)) || (cu_seqlens_k && mis(cu_seqlens_k, 4)))
     return FA_ERR_ALIGN;
 
   // o must not overlap any input or lse.  For the packed layout the true
@@ -64,7 +68,7 @@ int check_args(const void* q, const void* k, const void* v, const void* o,
   if (po == (uintptr_t)q || po == (uintptr_t)k || po == (uintptr_t)v ||
       po == (uintptr_t)lse)
     return FA_ERR_ALIAS;
-  if (!cu_seqlens) {
+  if (!cu_seqlens_q) {
     const uint64_t ob = qn * elem_size(out_dtype), ib = elem_size(in_dtype);
     if (overlap(po, ob, (uintptr_t)q, qn * ib) ||
         overlap(po, ob, (uintptr_t)k, kn * ib) ||
@@ -76,13 +80,13 @@ int check_args(const void* q, const void* k, const void* v, const void* o,
 }
 
 int check_packed_args(const void* q, const void* k, const void* vt, uint64_t vt_bytes,
-                      const void* o, const float* lse, int B, int Hq, int Hkv, int N, int d,
-                      int causal, float scale, const int* cu_seqlens, int in_dtype,
-                      int out_dtype) {
+                      const void* o, const float* lse, int B, int Hq, int Hkv, int Nq, int Nk,
+                      int d, int causal, float scale, const int* cu_seqlens_q,
+                      const int* cu_seqlens_k, int in_dtype, int out_dtype) {
   if (in_dtype == FA_F32) return FA_ERR_DTYPE;   // fp32 inputs use V itself
-  const uint64_t need = workspace_bytes(B, Hkv, N, d, in_dtype);
-  const int st = check_args(q, k, vt, o, lse, B, Hq, Hkv, N, d, causal, scale, cu_seqlens,
-                            in_dtype, out_dtype, need);
+  const uint64_t need = workspace_bytes(B, Hkv, Nk, d, in_dtype);
+  const int st = check_args(q, k, vt, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale,
+                            cu_seqlens_q, cu_seqlens_k, in_dtype, out_dtype, need);
   if (st != FA_OK) return st;
   if (vt_bytes < need) return FA_ERR_WORKSPACE;
   if (need / (128ull * (uint64_t)d) > (uint64_t)INT32_MAX) return FA_ERR_SHAPE;

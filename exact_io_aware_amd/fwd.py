@@ -69,22 +69,29 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor], *, causal: 
         max_seqlen: Optional[int] = None, out_dtype: torch.dtype = torch.float32,
         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
         stream: Optional[torch.cuda.Stream] = None, vt: Optional[torch.Tensor] = None,
-        library_workspace: bool = False):
+        library_workspace: bool = False, cu_seqlens_k: Optional[torch.Tensor] = None,
+        max_seqlen_k: Optional[int] = None):
     """Exact attention forward on the GPU: returns ``(o, lse)``.
 
-    Fixed length: q ``[B, Hq, N, d]``, k/v ``[B, Hkv, N, d]``.
-    Packed varlen: q ``[T, Hq, d]``, k/v ``[T, Hkv, d]`` and ``cu_seqlens``
-    (int32 device tensor ``[B+1]``); ``max_seqlen`` (>= the longest
-    sequence) sizes the launch; if omitted it is read from ``cu_seqlens``,
-    which synchronises.
-    ``lse`` is float32 ``[B, Hq, N]``.  ``scale`` defaults to 1/sqrt(d).
+    Fixed length: q ``[B, Hq, Nq, d]``, k/v ``[B, Hkv, Nk, d]``.
+    Packed varlen: q ``[Tq, Hq, d]``, k/v ``[Tk, Hkv, d]`` and ``cu_seqlens``
+    (int32 device tensor ``[B+1]``, query offsets); ``cu_seqlens_k`` gives
+    separate key/value offsets (default: the same as the queries).
+    ``max_seqlen`` / ``max_seqlen_k`` (>= the longest query / key count)
+    size the launch; if omitted they are read from the offsets, which
+    synchronises.
+    When a sequence has fewer queries than keys, the queries are its last
+    tokens (chunked prefill): with ``causal`` query row r sees keys
+    ``c <= r + nk - nq``.
+    ``lse`` is float32 ``[B, Hq, Nq]``.  ``scale`` defaults to 1/sqrt(d).
     ``out``/``lse`` may be given to write into existing buffers.
     The kernels are enqueued on ``stream`` (default: the current stream).
 
     16-bit inputs: V is first packed (``pack_v``) into a workspace from
-    torch's allocator, then fa_fwd_packed runs.  ``vt`` passes V already
-    packed by ``pack_v`` (``v`` may then be None).  ``library_workspace``
-    calls fa_fwd instead, which allocates its own stream-ordered workspace.
+    torch's allocator, then fa_fwd_packed (fa_fwd_kv_packed) runs.  ``vt``
+    passes V already packed by ``pack_v`` (``v`` may then be None).
+    ``library_workspace`` calls fa_fwd (fa_fwd_kv) instead, which allocates
+    its own stream-ordered workspace.
     """
     if v is None and vt is None:
         raise ValueError("v is needed unless a packed vt is given")
@@ -100,24 +107,37 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor], *, causal: 
     if k.shape != v.shape:
         raise ValueError("k and v must have the same shape")
     if cu_seqlens is None:
+        if cu_seqlens_k is not None:
+            raise ValueError("cu_seqlens_k needs cu_seqlens")
         if q.dim() != 4 or k.dim() != 4:
-            raise ValueError("fixed layout needs q [B,Hq,N,d] and k/v [B,Hkv,N,d]")
+            raise ValueError("fixed layout needs q [B,Hq,Nq,d] and k/v [B,Hkv,Nk,d]")
         B, Hq, N, d = q.shape
-        if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        if k.shape[0] != B or k.shape[3] != d:
             raise ValueError("k/v shape does not match q")
-        Hkv = k.shape[1]
-        cu_ptr = None
+        Hkv, Nk = k.shape[1], k.shape[2]
+        cu_ptr = cuk_ptr = None
     else:
         if q.dim() != 3 or k.dim() != 3:
-            raise ValueError("packed layout needs q [T,Hq,d] and k/v [T,Hkv,d]")
+            raise ValueError("packed layout needs q [Tq,Hq,d] and k/v [Tk,Hkv,d]")
         _check_cu(cu_seqlens)
         T, Hq, d = q.shape
-        if k.shape[0] != T or k.shape[2] != d:
+        if k.shape[2] != d:
             raise ValueError("k/v shape does not match q")
         Hkv = k.shape[1]
         B = cu_seqlens.numel() - 1
         N = _max_seqlen(cu_seqlens, max_seqlen)
         cu_ptr = cu_seqlens.data_ptr()
+        if cu_seqlens_k is None:
+            if k.shape[0] != T:
+                raise ValueError("k/v token count differs from q: pass cu_seqlens_k")
+            Nk, cuk_ptr = N, cu_ptr
+        else:
+            _check_cu(cu_seqlens_k)
+            if cu_seqlens_k.numel() != B + 1:
+                raise ValueError("cu_seqlens_k must have as many entries as cu_seqlens")
+            Nk = _max_seqlen(cu_seqlens_k, max_seqlen_k)
+            cuk_ptr = cu_seqlens_k.data_ptr()
+    same = Nk == N and cuk_ptr == cu_ptr
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -127,34 +147,61 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor], *, causal: 
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     elif lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, N) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor [B, Hq, N]")
+        raise ValueError("lse must be a contiguous float32 tensor [B, Hq, Nq]")
     stream = stream or torch.cuda.current_stream(q.device)
     st = stream.cuda_stream
     packed = q.dtype != torch.float32 and not library_workspace
     if vt is not None and not packed:
         raise ValueError("vt is used for 16-bit inputs without library_workspace only")
     if packed and vt is None:
-        vt = pack_v(v, cu_seqlens=cu_seqlens, max_seqlen=N if cu_seqlens is not None else None,
-                    stream=stream)
+        vt = pack_v(v, cu_seqlens=cu_seqlens_k if cu_seqlens_k is not None else cu_seqlens,
+                    max_seqlen=Nk if cu_seqlens is not None else None, stream=stream)
     if packed and (vt.dtype != torch.uint8 or not vt.is_cuda or not vt.is_contiguous()):
         raise ValueError("vt must be the contiguous uint8 device tensor pack_v returns")
+    dt, odt = _DT[q.dtype], _DT[out_dtype]
     with torch.cuda.device(q.device):
-        if packed:
+        if packed and same:
+            name = "fa_fwd_packed"
             status = _lib.fwd_packed_raw(q.data_ptr(), k.data_ptr(), vt.data_ptr(), vt.numel(),
                                          out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, N, d,
-                                         causal, float(scale), cu_ptr, st, _DT[q.dtype],
-                                         _DT[out_dtype])
-        else:
+                                         causal, float(scale), cu_ptr, st, dt, odt)
+        elif packed:
+            name = "fa_fwd_kv_packed"
+            status = _lib.fwd_kv_packed_raw(q.data_ptr(), k.data_ptr(), vt.data_ptr(),
+                                            vt.numel(), out.data_ptr(), lse.data_ptr(), B, Hq,
+                                            Hkv, N, Nk, d, causal, float(scale), cu_ptr,
+                                            cuk_ptr, st, dt, odt)
+        elif same:
+            name = "fa_fwd"
             status = _lib.fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                   lse.data_ptr(), B, Hq, Hkv, N, d, causal, float(scale),
-                                  cu_ptr, st, _DT[q.dtype], _DT[out_dtype])
+                                  cu_ptr, st, dt, odt)
+        else:
+            name = "fa_fwd_kv"
+            status = _lib.fwd_kv_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                     lse.data_ptr(), B, Hq, Hkv, N, Nk, d, causal,
+                                     float(scale), cu_ptr, cuk_ptr, st, dt, odt)
     if status != _lib.FA_OK:
-        name = "fa_fwd_packed" if packed else "fa_fwd"
         raise RuntimeError(f"{name} failed ({status}): {_lib.status_string(status)}")
     return out, lse
 
 
-def flops(Hq: int, d: int, lengths: Sequence[int], causal: bool) -> float:
-    """Algorithmic FLOP of one forward: 4*d*Hq per visible (query, key) pair."""
-    pairs = sum(n * (n + 1) // 2 if causal else n * n for n in lengths)
+def flops(Hq: int, d: int, lengths: Sequence[int], causal: bool,
+          lengths_k: Optional[Sequence[int]] = None) -> float:
+    """Algorithmic FLOP of one forward: 4*d*Hq per visible (query, key) pair.
+    ``lengths_k`` gives per-sequence key counts when they differ from the
+    query counts (the queries are then the last tokens of each sequence)."""
+    if lengths_k is None:
+        pairs = sum(n * (n + 1) // 2 if causal else n * n for n in lengths)
+    else:
+        pairs = 0
+        for nq, nk in zip(lengths, lengths_k):
+            nq, nk = int(nq), int(nk)
+            if not causal:
+                pairs += nq * nk
+                continue
+            # row r sees r + nk - nq + 1 keys when that is positive (never
+            # more than nk, since r < nq)
+            lo = max(0, nq - nk)
+            pairs += sum(range(lo + nk - nq + 1, nk + 1)) if lo < nq else 0
     return 4.0 * d * Hq * pairs

@@ -136,6 +136,34 @@ int fa_fwd_packed(const void* q, const void* k, const void* vt, size_t vt_bytes,
                   float* lse, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                   const int* cu_seqlens, void* stream, int in_dtype, int out_dtype);
 
+/* Queries against a longer key/value sequence (chunked prefill).  As
+ * fa_fwd, but each sequence has nq query rows and nk key/value rows, and the
+ * queries are the LAST nq tokens of the sequence: with causal = 1, query
+ * row r sees keys c <= r + nk - nq (bottom-right alignment).  This is the
+ * manual chunking recipe of the French HolySheep article ("Erreurs
+ * courantes", item 1): the query chunk [i, i+c) attends to the key prefix
+ * [0, i+c).  nq = nk gives fa_fwd.  A row that sees no key (causal with
+ * nq > nk, or nk = 0 in a packed batch) gets O = 0 and L = -inf.
+ *
+ * Layouts: fixed (both offset arrays NULL): q, o [B][Hq][Nq][d],
+ * k, v [B][Hkv][Nk][d], lse [B][Hq][Nq].  Packed: cu_seqlens_q and
+ * cu_seqlens_k are DEVICE int32 arrays [B+1] (both given, or neither),
+ * q, o [Tq][Hq][d], k, v [Tk][Hkv][d]; Nq and Nk bound the longest query
+ * and key counts; lse [B][Hq][Nq] with rows past a sequence's nq untouched.
+ * Errors as fa_fwd (FA_ERR_NULL if only one offset array is given; Nq, Nk
+ * must be >= 1). */
+int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+              const int* cu_seqlens_q, const int* cu_seqlens_k, void* stream,
+              int in_dtype, int out_dtype);
+
+/* fa_fwd_kv for 16-bit inputs with V packed by fa_pack_v (called with N = Nk
+ * and cu_seqlens = cu_seqlens_k).  Allocates nothing. */
+int fa_fwd_kv_packed(const void* q, const void* k, const void* vt, size_t vt_bytes, void* o,
+                     float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                     float scale, const int* cu_seqlens_q, const int* cu_seqlens_k,
+                     void* stream, int in_dtype, int out_dtype);
+
 /* The argument checks of fa_fwd alone: returns what fa_fwd would return
  * before touching the device (FA_OK if it would go on to launch).  Makes no
  * HIP call, so it is usable without a GPU. */

@@ -193,3 +193,23 @@ def test_fwd_packed_rejects_before_any_device_call(kw, code):
 ])
 def test_pack_v_rejects_before_any_device_call(kw, code):
     assert pack(**kw) == S[code]
+
+
+def kv(**kw):
+    a = dict(BASE, Nk=96, cu_k=None)
+    a.update(kw)
+    return _lib.fwd_kv_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"],
+                           a["Hkv"], a["N"], a["Nk"], a["d"], a["causal"], a["scale"],
+                           a["cu_seqlens"], a["cu_k"], None, a["in_dtype"], a["out_dtype"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"cu_seqlens": 0x600000}, "FA_ERR_NULL"),            # query offsets without key offsets
+    ({"cu_k": 0x600100}, "FA_ERR_NULL"),
+    ({"Nk": 0}, "FA_ERR_SHAPE"), ({"N": 0}, "FA_ERR_SHAPE"),
+    ({"cu_seqlens": 0x600000, "cu_k": 0x600102}, "FA_ERR_ALIGN"),
+    ({"d": 96}, "FA_ERR_HEADDIM"),
+    ({"o": 0x200000 + 2 * 96 * 2 * 128 * 2 - 16}, "FA_ERR_ALIAS"),   # runs into k (Nk rows)
+])
+def test_fwd_kv_rejects_before_any_device_call(kw, code):
+    assert kv(**kw) == S[code]

@@ -126,7 +126,8 @@ def test_workload_shapes():
             continue
         x = workloads.make_inputs(name)
         assert x["q"].shape == (wl.B, wl.Hq, wl.N, wl.d)
-        assert x["k"].shape == (wl.B, wl.Hkv, wl.N, wl.d)
+        assert x["k"].shape == (wl.B, wl.Hkv, wl.Nk or wl.N, wl.d)
+        assert x["v"].shape == x["k"].shape
 
 
 # ---------------------------------------------------------------------------

@@ -14,6 +14,11 @@ storage precision with round-to-nearest-even.  The five named workloads are:
 * ``long_bf16``   B=1, Hq=32, Hkv=8, N=32768, d=128, bf16, causal
 * ``varlen_bf16`` 16 packed sequences, lengths uniform in [1024, 8192],
                   Hq=32, Hkv=8, d=128, bf16, causal
+* ``prefill_bf16`` chunked prefill: the last 1024 queries of 8192-token
+                  sequences, B=4, Hq=32, Hkv=8, d=128, bf16, causal
+
+When a workload has more keys than queries (``Nk``), k and v are drawn with
+the key count and the queries are the last tokens of each sequence.
 
 Storage formats returned by :func:`make_inputs`:
 
@@ -33,7 +38,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 __all__ = [
-    "Workload", "WORKLOADS", "HEADLINE", "make_inputs", "make_custom",
+    "Workload", "WORKLOADS", "HEADLINE", "make_inputs", "make_custom", "make_custom_qk",
     "round_to_bf16_bits", "bf16_bits_to_f32", "to_f64", "varlen_lengths",
 ]
 
@@ -52,6 +57,7 @@ class Workload:
     varlen: bool = False
     len_lo: int = 0      # varlen: inclusive range of the uniform lengths
     len_hi: int = 0
+    Nk: int = 0          # keys per sequence when more than the queries (0: = N)
 
     @property
     def scale(self) -> float:
@@ -66,6 +72,7 @@ WORKLOADS = {
         Workload("long_bf16", 1, 32, 8, 32768, 128, "bf16", True, 1004),
         Workload("varlen_bf16", 16, 32, 8, 8192, 128, "bf16", True, 1005,
                  varlen=True, len_lo=1024, len_hi=8192),
+        Workload("prefill_bf16", 4, 32, 8, 1024, 128, "bf16", True, 1006, Nk=8192),
     ]
 }
 
@@ -124,25 +131,51 @@ def make_custom(B: int, Hq: int, Hkv: int, d: int, dtype: str, seed: int,
     return _draw(rng, B, Hq, Hkv, d, dtype, N, lengths)
 
 
-def _draw(rng, B, Hq, Hkv, d, dtype, N, lengths):
+def _offsets(lengths, B):
+    lengths = np.asarray(lengths, dtype=np.int64)
+    assert lengths.shape == (B,)
+    cu = np.zeros(B + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    return lengths, cu
+
+
+def _draw(rng, B, Hq, Hkv, d, dtype, N, lengths, Nk=None, lengths_k=None):
+    cu_k = None
     if lengths is not None:
-        lengths = np.asarray(lengths, dtype=np.int64)
-        assert lengths.shape == (B,)
-        cu = np.zeros(B + 1, dtype=np.int32)
-        cu[1:] = np.cumsum(lengths)
-        T = int(cu[-1])
-        qs, ks = (T, Hq, d), (T, Hkv, d)
+        lengths, cu = _offsets(lengths, B)
+        qs = (int(cu[-1]), Hq, d)
         nmax = int(lengths.max()) if B > 0 else 0
+        if lengths_k is not None:
+            lengths_k, cu_k = _offsets(lengths_k, B)
+            ks = (int(cu_k[-1]), Hkv, d)
+            nkmax = int(lengths_k.max()) if B > 0 else 0
+        else:
+            ks, nkmax = (int(cu[-1]), Hkv, d), nmax
     else:
         cu = None
-        qs, ks = (B, Hq, N, d), (B, Hkv, N, d)
-        nmax = N
+        nk = N if Nk is None else Nk
+        qs, ks = (B, Hq, N, d), (B, Hkv, nk, d)
+        nmax, nkmax = N, nk
     q = _round(rng.standard_normal(qs, dtype=np.float32), dtype)
     k = _round(rng.standard_normal(ks, dtype=np.float32), dtype)
     v = _round(rng.standard_normal(ks, dtype=np.float32), dtype)
     return dict(q=q, k=k, v=v, cu_seqlens=cu, N=nmax, dtype=dtype,
                 lengths=None if lengths is None else lengths.tolist(),
-                B=B, Hq=Hq, Hkv=Hkv, d=d)
+                B=B, Hq=Hq, Hkv=Hkv, d=d, Nk=nkmax, cu_seqlens_k=cu_k,
+                lengths_k=None if lengths_k is None else lengths_k.tolist())
+
+
+def make_custom_qk(B: int, Hq: int, Hkv: int, d: int, dtype: str, seed: int,
+                   Nq: Optional[int] = None, Nk: Optional[int] = None,
+                   lengths_q: Optional[Sequence[int]] = None,
+                   lengths_k: Optional[Sequence[int]] = None) -> dict:
+    """Draw q, k, v with separate query and key counts.
+
+    Fixed layout: ``Nq``, ``Nk``.  Varlen: ``lengths_q`` and ``lengths_k``
+    (both), giving ``cu_seqlens`` (queries) and ``cu_seqlens_k``.
+    """
+    rng = np.random.default_rng(seed)
+    return _draw(rng, B, Hq, Hkv, d, dtype, Nq, lengths_q, Nk, lengths_k)
 
 
 def make_inputs(w: Workload | str) -> dict:
@@ -154,7 +187,7 @@ def make_inputs(w: Workload | str) -> dict:
     if w.varlen:
         lengths = varlen_lengths(rng, w.B, w.len_lo, w.len_hi)
     out = _draw(rng, w.B, w.Hq, w.Hkv, w.d, w.dtype,
-                None if w.varlen else w.N, lengths)
+                None if w.varlen else w.N, lengths, Nk=w.Nk or None)
     out["causal"] = w.causal
     out["scale"] = w.scale
     out["name"] = w.name
