@@ -77,16 +77,33 @@ def cpu_baseline(w, heads: int):
         heads = w["B"] * w["Hq"]
     heads = max(G, (heads // G) * G)
     q, k, v = (workloads.to_f64(w[x], w["dtype"]) for x in "qkv")
-    nb = max(1, heads // w["Hq"])
+    nb = min(w["B"], max(1, heads // w["Hq"]))
     hq = min(heads, w["Hq"])
-    qs = np.ascontiguousarray(q[:nb, :hq])
-    ks = np.ascontiguousarray(k[:nb, :hq // G])
-    vs = np.ascontiguousarray(v[:nb, :hq // G])
     workers = oracle.default_workers()
-    t0 = time.perf_counter()
-    oracle.attention(qs, ks, vs, causal=w["causal"], scale=w["scale"], workers=workers)
-    dt = time.perf_counter() - t0
-    fl = nb * hq * oracle.unit_flops(w["N"], w["d"], w["causal"])
+    if w["cu_seqlens"] is not None:
+        cu = w["cu_seqlens"][:nb + 1]
+        T = int(cu[-1])
+        qs = np.ascontiguousarray(q[:T, :hq])
+        ks = np.ascontiguousarray(k[:T, :hq // G])
+        vs = np.ascontiguousarray(v[:T, :hq // G])
+        t0 = time.perf_counter()
+        oracle.attention(qs, ks, vs, causal=w["causal"], scale=w["scale"], cu_seqlens=cu,
+                         workers=workers)
+        dt = time.perf_counter() - t0
+        fl = hq * sum(oracle.unit_flops(int(n), w["d"], w["causal"]) for n in np.diff(cu))
+    else:
+        qs = np.ascontiguousarray(q[:nb, :hq])
+        ks = np.ascontiguousarray(k[:nb, :hq // G])
+        vs = np.ascontiguousarray(v[:nb, :hq // G])
+        t0 = time.perf_counter()
+        if w["Nk"] != w["N"]:
+            oracle.attention_qk(qs, ks, vs, causal=w["causal"], scale=w["scale"],
+                                workers=workers)
+            fl = nb * hq * 4.0 * w["d"] * oracle.pair_count(w["N"], w["Nk"], w["causal"])
+        else:
+            oracle.attention(qs, ks, vs, causal=w["causal"], scale=w["scale"], workers=workers)
+            fl = nb * hq * oracle.unit_flops(w["N"], w["d"], w["causal"])
+        dt = time.perf_counter() - t0
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
             "sample": f"{nb} sequence(s) x {hq} query heads of {w['name']} "
                       f"({nb * hq} of {w['B'] * w['Hq']} head-sequences), float64 numpy, "
@@ -115,11 +132,16 @@ def main():
 
     q, k, v = (up(w[x]) for x in "qkv")
     cu = None if w["cu_seqlens"] is None else torch.from_numpy(w["cu_seqlens"]).to(dev)
+    cuk = None if w["cu_seqlens_k"] is None else torch.from_numpy(w["cu_seqlens_k"]).to(dev)
+    Nk = w["Nk"]
     out_dtype = torch.float32 if args.out_dtype == "fp32" else q.dtype
     o = torch.empty(q.shape, dtype=out_dtype, device=dev)
     lse = torch.empty((w["B"], w["Hq"], w["N"]), dtype=torch.float32, device=dev)
     lengths = [w["N"]] * w["B"] if cu is None else list(np.diff(w["cu_seqlens"]))
-    flop = fa.flops(w["Hq"], w["d"], lengths, w["causal"])
+    lengths_k = None
+    if Nk != w["N"] or cuk is not None:
+        lengths_k = [Nk] * w["B"] if cuk is None else list(np.diff(w["cu_seqlens_k"]))
+    flop = fa.flops(w["Hq"], w["d"], lengths, w["causal"], lengths_k)
     dt_code = {"fp32": fa.FA_F32, "fp16": fa.FA_F16, "bf16": fa.FA_BF16}[w["dtype"]]
     kname = fa.kernel_name(dt_code, w["d"], w["causal"], cu is not None,
                            fa.FA_F32 if args.out_dtype == "fp32" else dt_code)
@@ -128,17 +150,19 @@ def main():
     max_seqlen = w["N"] if cu is not None else None
     vt = None
     if packed:
-        vt = torch.empty(fa.workspace_bytes(w["B"], w["Hkv"], w["N"], w["d"], dt_code),
+        vt = torch.empty(fa.workspace_bytes(w["B"], w["Hkv"], Nk, w["d"], dt_code),
                          dtype=torch.uint8, device=dev)
 
     def step(mark=None):
         if packed:
-            fa.pack_v(v, cu_seqlens=cu, max_seqlen=max_seqlen, out=vt, stream=stream)
+            fa.pack_v(v, cu_seqlens=cuk if cuk is not None else cu,
+                      max_seqlen=Nk if cu is not None else None, out=vt, stream=stream)
         if mark is not None:
             mark[0].record(stream)
         fa.fwd(q, k, None if packed else v, causal=w["causal"], scale=w["scale"],
                cu_seqlens=cu, max_seqlen=max_seqlen, out_dtype=out_dtype, out=o, lse=lse,
-               stream=stream, vt=vt)
+               stream=stream, vt=vt, cu_seqlens_k=cuk,
+               max_seqlen_k=Nk if cu is not None else None)
         if mark is not None:
             mark[1].record(stream)
 
@@ -177,7 +201,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w["dtype"], "data": "synthetic",
         "config": {"workload": w["name"], "B": w["B"], "Hq": w["Hq"], "Hkv": w["Hkv"],
-                   "N": w["N"], "d": w["d"], "causal": w["causal"],
+                   "N": w["N"], "Nk": Nk, "d": w["d"], "causal": w["causal"],
                    "out_dtype": args.out_dtype, "kernel": kname,
                    "algorithmic_flop_per_step": flop},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),

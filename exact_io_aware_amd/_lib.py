@@ -43,6 +43,13 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_kv_packed.argtypes = [vp, vp, vp, z, vp, vp, i, i, i, i, i, i, i, f, vp, vp, vp,
                                      i, i]
     lib.fa_fwd_kv_packed.restype = i
+    lib.fa_num_splits.argtypes = [i, i, i, i, i, i, i]
+    lib.fa_num_splits.restype = i
+    lib.fa_split_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa_split_workspace_bytes.restype = z
+    lib.fa_fwd_kv_split_packed.argtypes = [vp, vp, vp, z, vp, vp, i, i, i, i, i, i, i, f, vp,
+                                           vp, i, vp, z, vp, i, i]
+    lib.fa_fwd_kv_split_packed.restype = i
     lib.fa_fwd_check.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i, i]
     lib.fa_fwd_check.restype = i
     lib.fa_kernel_name.argtypes = [i, i, i, i, i]
@@ -117,3 +124,22 @@ def fwd_kv_packed_raw(q, k, vt, vt_bytes, o, lse, B, Hq, Hkv, Nq, Nk, d, causal,
     """fa_fwd_kv_packed with raw integer device addresses and a raw hipStream_t."""
     return load().fa_fwd_kv_packed(q, k, vt, vt_bytes, o, lse, B, Hq, Hkv, Nq, Nk, d,
                                    int(causal), scale, cu_q, cu_k, stream, in_dtype, out_dtype)
+
+
+def num_splits(B, Hq, Hkv, Nq, Nk, d, in_dtype) -> int:
+    """fa_num_splits: split-KV count for these sizes on the current device."""
+    return load().fa_num_splits(B, Hq, Hkv, Nq, Nk, d, in_dtype)
+
+
+def split_workspace_bytes(B, Hq, Nq, d, n_splits) -> int:
+    """fa_split_workspace_bytes: bytes of the split-KV partials."""
+    return load().fa_split_workspace_bytes(B, Hq, Nq, d, n_splits)
+
+
+def fwd_kv_split_packed_raw(q, k, vt, vt_bytes, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale,
+                            cu_q, cu_k, n_splits, part, part_bytes, stream, in_dtype,
+                            out_dtype) -> int:
+    """fa_fwd_kv_split_packed with raw integer device addresses."""
+    return load().fa_fwd_kv_split_packed(q, k, vt, vt_bytes, o, lse, B, Hq, Hkv, Nq, Nk, d,
+                                         int(causal), scale, cu_q, cu_k, n_splits, part,
+                                         part_bytes, stream, in_dtype, out_dtype)

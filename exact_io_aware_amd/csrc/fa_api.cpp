@@ -16,6 +16,14 @@ constexpr int kMaxDevices = 64;
 std::once_flag g_dev_once[kMaxDevices];
 int g_dev_ok[kMaxDevices];
 
+// Compute units of the current device, 0 if unknown.
+int device_cus() {
+  int dev = -1, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
+
 int device_status() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
@@ -69,6 +77,42 @@ int fa_fwd_kv_packed(const void* q, const void* k, const void* vt, size_t vt_byt
   return fa::launch_fwd(a, stream);
 }
 
+int fa_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int in_dtype) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || Hq % Hkv != 0 ||
+      (d != 64 && d != 128))
+    return 1;
+  return fa::suggest_splits(B, Hq, Hkv, Nq, Nk, d, in_dtype, device_cus());
+}
+
+size_t fa_split_workspace_bytes(int B, int Hq, int Nq, int d, int num_splits) {
+  if (num_splits < 2) return 0;
+  const uint64_t n = fa::split_workspace_bytes(B, Hq, Nq, d, num_splits);
+  return n > (uint64_t)SIZE_MAX ? SIZE_MAX : (size_t)n;
+}
+
+int fa_fwd_kv_split_packed(const void* q, const void* k, const void* vt, size_t vt_bytes,
+                           void* o, float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                           int causal, float scale, const int* cu_seqlens_q,
+                           const int* cu_seqlens_k, int num_splits, void* part,
+                           size_t part_bytes, void* stream, int in_dtype, int out_dtype) {
+  int st = fa::check_packed_args(q, k, vt, vt_bytes, o, lse, B, Hq, Hkv, Nq, Nk, d, causal,
+                                 scale, cu_seqlens_q, cu_seqlens_k, in_dtype, out_dtype);
+  if (st != FA_OK) return st;
+  st = fa::check_split_args(part, part_bytes, o, lse, B, Hq, Hkv, Nq, Nk, d, num_splits,
+                            in_dtype, out_dtype, cu_seqlens_q != nullptr);
+  if (st != FA_OK) return st;
+  st = device_status();
+  if (st != FA_OK) return st;
+  fa::LaunchArgs a{q, k, nullptr, o, lse, vt, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, Nq, Nk,
+                   d, causal, scale, in_dtype, out_dtype};
+  if (num_splits > 1) {
+    a.n_splits = num_splits;
+    a.o_part = (float*)part;
+    a.lse_part = (float*)((char*)part + (size_t)num_splits * B * Hq * Nq * d * 4);
+  }
+  return fa::launch_fwd(a, stream);
+}
+
 int fa_fwd_packed(const void* q, const void* k, const void* vt, size_t vt_bytes, void* o,
                   float* lse, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                   const int* cu_seqlens, void* stream, int in_dtype, int out_dtype) {
@@ -88,16 +132,26 @@ int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
   fa::LaunchArgs a{q, k, v, o, lse, nullptr, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, Nq, Nk,
                    d, causal, scale, in_dtype, out_dtype};
   if (in_dtype == FA_F32) return fa::launch_fwd(a, stream);
-  // 16-bit inputs: pack V^T into a stream-ordered workspace, run, release.
+  // 16-bit inputs: pack V^T into a stream-ordered workspace (plus split-KV
+  // partials for decode-like shapes), run, release.
   const uint64_t need = fa::workspace_bytes(B, Hkv, Nk, d, in_dtype);
   if (need / (128ull * (uint64_t)d) > (uint64_t)INT32_MAX || need > (uint64_t)SIZE_MAX)
     return FA_ERR_SHAPE;
+  const int n_splits = fa::suggest_splits(B, Hq, Hkv, Nq, Nk, d, in_dtype, device_cus());
+  const uint64_t part = n_splits > 1 ? fa::split_workspace_bytes(B, Hq, Nq, d, n_splits) : 0;
+  const uint64_t vt_pad = (need + 255) & ~255ull;
+  if (part > (uint64_t)SIZE_MAX - vt_pad) return FA_ERR_SHAPE;
   void* ws = nullptr;
-  if (hipMallocAsync(&ws, (size_t)need, (hipStream_t)stream) != hipSuccess || !ws)
+  if (hipMallocAsync(&ws, (size_t)(vt_pad + part), (hipStream_t)stream) != hipSuccess || !ws)
     return FA_ERR_ALLOC;
   st = fa::launch_vt_pack(v, ws, B, Hkv, Nk, d, cu_seqlens_k, in_dtype, stream);
   if (st == FA_OK) {
     a.vt = ws;
+    if (n_splits > 1) {
+      a.n_splits = n_splits;
+      a.o_part = (float*)((char*)ws + vt_pad);
+      a.lse_part = (float*)((char*)ws + vt_pad + (size_t)n_splits * B * Hq * Nq * d * 4);
+    }
     st = fa::launch_fwd(a, stream);
   }
   if (hipFreeAsync(ws, (hipStream_t)stream) != hipSuccess && st == FA_OK) st = FA_ERR_LAUNCH;

@@ -82,6 +82,11 @@ struct FwdParams {
   float scale_log2;        // scale * log2(e)
   const void* vt;          // packed V^T tiles (16-bit inputs), see fa_vt_pack
   int Hkv, vt_ntiles;      // K/V heads; V^T tiles per (sequence, K/V head)
+  // Split-KV: n_splits > 1 cuts each unit's keys into ranges of split_tiles
+  // 64-key tiles; workgroup (unit, split) writes the normalised partial O
+  // (fp32, [split][B][Hq][N][d]) and partial L ([split][B][Hq][N]).
+  int n_splits, split_tiles, B;
+  float* o_part; float* lse_part;
   long long q_bs, q_hs, q_rs;    // element strides of q (and o): batch, head, row
   long long kv_bs, kv_hs, kv_rs; // element strides of k and v
 };
@@ -271,15 +276,20 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
   // unit's row blocks consecutively: all row blocks of a unit (which share
   // its K/V) stay in one XCD's L2, and every XCD gets an equal share of
   // every sequence, whatever the sequence lengths.
+  int wg = blockIdx.x, split = 0;
+  if (p.n_splits > 1) {                      // consecutive workgroups: splits of one unit
+    split = wg % p.n_splits;
+    wg /= p.n_splits;
+  }
   int unit, rb;
   if (p.xcd_remap) {
-    const int idx = blockIdx.x >> 3;
+    const int idx = wg >> 3;
     const int k = idx / p.n_rblocks;
     rb = idx - k * p.n_rblocks;
-    unit = 8 * k + (blockIdx.x & 7);
+    unit = 8 * k + (wg & 7);
   } else {
-    unit = blockIdx.x / p.n_rblocks;
-    rb = blockIdx.x - unit * p.n_rblocks;
+    unit = wg / p.n_rblocks;
+    rb = wg - unit * p.n_rblocks;
   }
   if (CAUSAL) rb = p.n_rblocks - 1 - rb;     // longest row blocks first
   const int b = unit / p.n_hgroups;
@@ -306,6 +316,14 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
   const bool active = row0 < len;
   const int wave_kv_end = CAUSAL ? max(0, min(min(row0 + WR, len) + off, len_k)) : len_k;
   const int wave_nblk = active ? (wave_kv_end + 31) / 32 : 0;  // blocks this wave needs
+  // This workgroup's key tiles: [t_begin, t_begin + split_tiles) (all of
+  // them without split-KV); blk0 is the first 32-key block.
+  const int t_begin = split * p.split_tiles;
+  const int kv_stop = min(kv_end, (t_begin + p.split_tiles) * BC);
+  const int blk0 = 2 * t_begin;
+  // Blocks this wave softmaxes: its own, and none past the split's range
+  // (their P.V would belong to the next split).
+  const int wave_blk_end = min(wave_nblk, (kv_stop + 31) / 32);
 
   const long long qbase = (VARLEN ? (long long)seq0 * p.q_rs : (long long)b * p.q_bs) +
                           (long long)h * p.q_hs;
@@ -329,7 +347,7 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
     voff[i] = vr * 128 + ((vc ^ vt_swz(vr)) << 4);
   }
   auto gload = [&](int tile, char* dst_base) __attribute__((always_inline)) {
-    const int kb = tile * BC;
+    const int kb = (t_begin + tile) * BC;
     // readfirstlane keeps the clamp (a VALU med3) in a scalar register: the
     // resource of a buffer load must be wave-uniform.
     const int rows = __builtin_amdgcn_readfirstlane(max(0, min(len_k - kb, BC)));
@@ -339,8 +357,9 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
     for (int i = 0; i < LOADS; ++i) lds_load16(r, dst_base + (NT * i + 64 * wave) * 16, koff[i]);
   };
   const char* vtp = (const char*)p.vt + (long long)(b * p.Hkv + kvh) * p.vt_ntiles * TILE_BYTES;
-  auto gload_vt = [&](int tile, char* dst_base) __attribute__((always_inline)) {
+  auto gload_vt = [&](int tile_rel, char* dst_base) __attribute__((always_inline)) {
     // A V^T tile is contiguous; tiles past the sequence end read zeros.
+    const int tile = t_begin + tile_rel;
     const int live_tile = __builtin_amdgcn_readfirstlane(tile * BC < len_k ? 1 : 0);
     const rsrc_t r = make_rsrc(vtp + (long long)min(tile, p.vt_ntiles) * TILE_BYTES,
                                live_tile ? (uint32_t)TILE_BYTES : 0u);
@@ -411,7 +430,7 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
   // a5: masks of block i (keys 32i .. 32i+31), only where it crosses the
   // diagonal or the end of the sequence.
   auto mask = [&](int i, f32x16 (&s)[QB]) __attribute__((always_inline)) {
-    const int kb = i * 32;
+    const int kb = (blk0 + i) * 32;
     if ((CAUSAL && kb + 31 > row0 + off) || (kb + 32 > len_k)) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
@@ -505,7 +524,7 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
                   const uint32_t (&pk_prev)[QB][8], const char* ks_nxt, const char* vs_prev,
                   int hb_prev)
       __attribute__((always_inline)) {
-    const bool live = st < wave_nblk;
+    const bool live = blk0 + st < wave_blk_end;
     mask(st, s_cur);
     float lsum[QB];
     qk(ks_nxt, s_nxt);
@@ -540,7 +559,7 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
     float lsum[QB];
     mask(0, sA);
     qk(k_lds0 + HALF, sB);
-    form_p(sA, pkA, lsum, wave_nblk > 0);
+    form_p(sA, pkA, lsum, blk0 < wave_blk_end);
     settle(sA, pkA, lsum);
   }
   // Barrier B_t follows step 2t: all of K_t and V_{t-1} have been read, so
@@ -555,7 +574,7 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
   // Steps 1 .. nblk (the last one drains P.V), four per iteration so that
   // every buffer is a fixed object: K_t sits in k_lds[t % 2], V_t in
   // v_lds[t % 2]; step s reads K of block s+1 and V of block s-1.
-  const int last_step = (kv_end + 31) / 32;
+  const int last_step = max(0, (kv_stop + 31) / 32 - blk0);
   for (int u = 0; 4 * u + 1 <= last_step; ++u) {
     const int s1 = 4 * u + 1;
     step(s1, sB, sA, pkB, pkA, k_lds1, v_lds0, 0);
@@ -579,6 +598,29 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
   // the epilogue's staging area.
   __syncthreads();
   if (!active) return;
+
+  if (p.n_splits > 1) {
+    // Split-KV partial: this split's normalised O and L (O = 0, L = -inf
+    // where the split holds no visible key); a merge pass combines splits.
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float ell_t = halves_sum(ell[qb]);
+      const float inv = ell_t > 0.0f ? 1.0f / ell_t : 0.0f;
+      const int qrow = row0 + 32 * qb + l32;
+      if (qrow < len) {
+        const long long prow = (((long long)split * p.B + b) * p.Hq + h) * p.N + qrow;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            *(f32x4*)(p.o_part + prow * D + 32 * db + 8 * g4 + 4 * hf) =
+                f32x4{oacc[qb][db][4 * g4] * inv, oacc[qb][db][4 * g4 + 1] * inv,
+                      oacc[qb][db][4 * g4 + 2] * inv, oacc[qb][db][4 * g4 + 3] * inv};
+        if (hf == 0) p.lse_part[prow] = (m_run[qb] + __builtin_amdgcn_logf(ell_t)) * kLn2;
+      }
+    }
+    return;
+  }
 
   // a8: epilogue.  O = acc / ell, L = (m + log2 ell) * ln 2.
   //
@@ -646,6 +688,54 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
       __builtin_amdgcn_s_waitcnt(0xC07F);      // reads done before the slot is rewritten
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Split-KV merge.  Each split s of a row holds O_s (normalised over its keys)
+// and L_s = ln(sum of its exp-scores); the row's result is
+//   L = ln sum_s exp(L_s),   O = sum_s exp(L_s - L) O_s,
+// the same normaliser algebra as the online softmax, applied once.  32
+// lanes per row, D/32 columns each; a row no split saw gives O = 0, L = -inf.
+template <typename OT, int D, bool VARLEN>
+__global__ __launch_bounds__(256) void fa_merge_splits(FwdParams p) {
+  constexpr int PER = D / 32;
+  const int row_id = blockIdx.x * 8 + (threadIdx.x >> 5);     // (b, h, r) flattened
+  const int c0 = (threadIdx.x & 31) * PER;
+  if (row_id >= p.B * p.Hq * p.N) return;
+  const int r = row_id % p.N;
+  const int bh = row_id / p.N;
+  const int h = bh % p.Hq, b = bh / p.Hq;
+  int seq0 = 0, len = p.N;
+  if (VARLEN) {
+    seq0 = p.cu_seqlens[b];
+    len = p.cu_seqlens[b + 1] - seq0;
+  }
+  if (r >= len) return;
+  const long long stride = (long long)p.B * p.Hq * p.N;       // rows per split
+  float lmax = -__builtin_inff();
+  for (int s = 0; s < p.n_splits; ++s) lmax = fmaxf(lmax, p.lse_part[s * stride + row_id]);
+  float acc[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) acc[j] = 0.0f;
+  float wsum = 0.0f;
+  if (lmax != -__builtin_inff()) {
+    for (int s = 0; s < p.n_splits; ++s) {
+      const float w = __expf(p.lse_part[s * stride + row_id] - lmax);
+      wsum += w;
+      const float* src = p.o_part + (s * stride + row_id) * D + c0;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) acc[j] += w * src[j];
+    }
+  }
+  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  const long long orow = (VARLEN ? (long long)(seq0 + r) * p.q_rs : (long long)b * p.q_bs +
+                                                                        (long long)r * p.q_rs) +
+                         (long long)h * p.q_hs;
+  OT* dst = (OT*)p.o + orow + c0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) dst[j] = (OT)(acc[j] * inv);
+  if ((threadIdx.x & 31) == 0)
+    p.lse[((long long)b * p.Hq + h) * p.N + r] = wsum > 0.0f ? lmax + __logf(wsum) : lmax;
 }
 
 // ---------------------------------------------------------------------------
@@ -847,6 +937,31 @@ const PackVariant kPackVariants[] = {
     {FA_F16, 128, 0, fa_vt_pack<_Float16, 128, false>}, {FA_F16, 128, 1, fa_vt_pack<_Float16, 128, true>},
 };
 
+typedef void (*MergeFn)(FwdParams);
+struct MergeVariant {
+  int out_dtype, d, varlen;
+  MergeFn fn;
+};
+const MergeVariant kMergeVariants[] = {
+    {FA_F32, 64, 0, fa_merge_splits<float, 64, false>},
+    {FA_F32, 64, 1, fa_merge_splits<float, 64, true>},
+    {FA_F32, 128, 0, fa_merge_splits<float, 128, false>},
+    {FA_F32, 128, 1, fa_merge_splits<float, 128, true>},
+    {FA_BF16, 64, 0, fa_merge_splits<__bf16, 64, false>},
+    {FA_BF16, 64, 1, fa_merge_splits<__bf16, 64, true>},
+    {FA_BF16, 128, 0, fa_merge_splits<__bf16, 128, false>},
+    {FA_BF16, 128, 1, fa_merge_splits<__bf16, 128, true>},
+    {FA_F16, 64, 0, fa_merge_splits<_Float16, 64, false>},
+    {FA_F16, 64, 1, fa_merge_splits<_Float16, 64, true>},
+    {FA_F16, 128, 0, fa_merge_splits<_Float16, 128, false>},
+    {FA_F16, 128, 1, fa_merge_splits<_Float16, 128, true>},
+};
+MergeFn find_merge(int out_dtype, int d, bool varlen) {
+  for (const MergeVariant& m : kMergeVariants)
+    if (m.out_dtype == out_dtype && m.d == d && m.varlen == (int)varlen) return m.fn;
+  return nullptr;
+}
+
 const char* kernel_name(int in_dtype, int d, int causal, int varlen, int out_dtype) {
   const Variant* v = find_variant(in_dtype, d, causal != 0, varlen != 0, out_dtype);
   return v ? v->name : nullptr;
@@ -867,6 +982,11 @@ int launch_fwd(const LaunchArgs& a, void* stream) {
   p.xcd_remap = (a.in_dtype != FA_F32) && ((uint64_t)a.B * plan.n_hgroups) % 8 == 0;
   p.scale_log2 = a.scale * kLog2e;
   p.vt = a.vt; p.Hkv = a.Hkv; p.vt_ntiles = vt_tiles(a.Nk);
+  const int n_splits = (a.in_dtype != FA_F32 && a.n_splits > 1) ? a.n_splits : 1;
+  p.n_splits = n_splits;
+  p.split_tiles = n_splits > 1 ? (p.vt_ntiles + n_splits - 1) / n_splits : p.vt_ntiles + 1;
+  p.B = a.B; p.o_part = a.o_part; p.lse_part = a.lse_part;
+  if (n_splits > 1) p.xcd_remap = 0;
   const long long d = a.d;
   if (varlen) {
     p.q_bs = 0; p.q_hs = d; p.q_rs = (long long)a.Hq * d;
@@ -876,10 +996,31 @@ int launch_fwd(const LaunchArgs& a, void* stream) {
     p.kv_rs = d; p.kv_hs = (long long)a.Nk * d; p.kv_bs = (long long)a.Hkv * a.Nk * d;
   }
   void* args[] = {&p};
-  const hipError_t e = hipLaunchKernel((const void*)var->fn, dim3((unsigned)plan.total_wg),
+  const hipError_t e = hipLaunchKernel((const void*)var->fn,
+                                       dim3((unsigned)(plan.total_wg * (uint64_t)n_splits)),
                                        dim3(64 * waves_per_wg(a.in_dtype)), args, 0,
                                        (hipStream_t)stream);
-  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  if (e != hipSuccess) return FA_ERR_LAUNCH;
+  if (n_splits == 1) return FA_OK;
+  const MergeFn mf = find_merge(a.out_dtype, a.d, varlen);
+  if (!mf) return FA_ERR_DTYPE;
+  const uint64_t rows = (uint64_t)a.B * a.Hq * a.N;
+  const hipError_t e2 = hipLaunchKernel((const void*)mf, dim3((unsigned)((rows + 7) / 8)),
+                                        dim3(256), args, 0, (hipStream_t)stream);
+  return e2 == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int suggest_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int in_dtype, int cus) {
+  if (in_dtype == FA_F32 || Nq > 64 || cus <= 0) return 1;
+  const Plan plan = make_plan(B, Hq, Hkv, Nq, d, in_dtype);
+  const uint64_t want = 2ull * (uint64_t)cus;          // two waves of workgroups
+  if (plan.total_wg >= want) return 1;
+  const int tiles = vt_tiles(Nk);
+  uint64_t n = (want + plan.total_wg - 1) / plan.total_wg;
+  const uint64_t max_by_len = (uint64_t)tiles / 4;     // at least 4 tiles (256 keys) a split
+  if (n > max_by_len) n = max_by_len;
+  if (n > 64) n = 64;
+  return n < 1 ? 1 : (int)n;
 }
 
 int launch_vt_pack(const void* v, void* vt, int B, int Hkv, int N, int d, const int* cu_seqlens,

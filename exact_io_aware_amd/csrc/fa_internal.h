@@ -75,6 +75,13 @@ int check_packed_args(const void* q, const void* k, const void* vt, uint64_t vt_
 int check_pack_args(const void* v, const void* vt, uint64_t vt_bytes, int B, int Hkv, int N,
                     int d, const int* cu_seqlens, int in_dtype);
 
+// Checks of the split-KV arguments (after check_packed_args): num_splits in
+// [1, 256], the partial buffer (when num_splits > 1) present, 16-byte
+// aligned, large enough and clear of o and lse, and the grid in range.
+int check_split_args(const void* part, uint64_t part_bytes, const void* o, const float* lse,
+                     int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits,
+                     int in_dtype, int out_dtype, bool varlen);
+
 struct LaunchArgs {
   const void* q; const void* k; const void* v; void* o; float* lse;
   const void* vt;      // packed V^T (16-bit inputs; v is then unused)
@@ -83,7 +90,25 @@ struct LaunchArgs {
   int B, Hq, Hkv, N, Nk, d, causal;   // N: max query count, Nk: max key count
   float scale;
   int in_dtype, out_dtype;
+  // Split-KV (16-bit inputs): n_splits > 1 writes partial results to o_part /
+  // lse_part (split_workspace_bytes) and merges them into o / lse.
+  int n_splits;
+  float* o_part;
+  float* lse_part;
 };
+
+// Bytes of the split-KV partials: n_splits x B x Hq x Nq rows of d fp32
+// values plus one fp32 L each.  Saturates at UINT64_MAX.
+inline uint64_t split_workspace_bytes(int B, int Hq, int Nq, int d, int n_splits) {
+  if (B < 1 || Hq < 1 || Nq < 1 || d < 1 || n_splits < 1) return 0;
+  const uint64_t rows = (uint64_t)n_splits * (uint64_t)B * (uint64_t)Hq * (uint64_t)Nq;
+  const uint64_t per = 4ull * ((uint64_t)d + 1);
+  return rows > UINT64_MAX / per ? UINT64_MAX : rows * per;
+}
+
+// A split count that fills the GPU when the grid alone would not: used for
+// decode-like shapes (few query rows per sequence).  1 = no split.
+int suggest_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int in_dtype, int cus);
 
 // Enqueue the kernel for already-checked arguments.  Returns FA_OK or
 // FA_ERR_LAUNCH.  `stream` is a hipStream_t.

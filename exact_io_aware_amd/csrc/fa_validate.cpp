@@ -93,6 +93,29 @@ int check_packed_args(const void* q, const void* k, const void* vt, uint64_t vt_
   return FA_OK;
 }
 
+int check_split_args(const void* part, uint64_t part_bytes, const void* o, const float* lse,
+                     int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits,
+                     int in_dtype, int out_dtype, bool varlen) {
+  (void)Nk;
+  if (num_splits < 1 || num_splits > 256) return FA_ERR_SHAPE;
+  if (num_splits == 1) return FA_OK;
+  if (!part) return FA_ERR_NULL;
+  if (((uintptr_t)part) % 16 != 0) return FA_ERR_ALIGN;
+  const uint64_t need = split_workspace_bytes(B, Hq, Nq, d, num_splits);
+  if (part_bytes < need) return FA_ERR_WORKSPACE;
+  if (grid_size(B, Hq, Hkv, Nq, d, in_dtype) * (uint64_t)num_splits > (uint64_t)INT32_MAX)
+    return FA_ERR_SHAPE;
+  uint64_t rows;
+  if (!mul_ok((uint64_t)B * (uint64_t)Hq, (uint64_t)Nq, &rows)) return FA_ERR_SHAPE;
+  // For the packed layout o's true extent (Tq rows) lives on the device:
+  // only identical start pointers are rejected there.
+  const uint64_t ob = varlen ? 1 : rows * (uint64_t)d * elem_size(out_dtype);
+  if (overlap((uintptr_t)part, need, (uintptr_t)o, ob) ||
+      overlap((uintptr_t)part, need, (uintptr_t)lse, rows * 4))
+    return FA_ERR_ALIAS;
+  return FA_OK;
+}
+
 int check_pack_args(const void* v, const void* vt, uint64_t vt_bytes, int B, int Hkv, int N,
                     int d, const int* cu_seqlens, int in_dtype) {
   if (!v || !vt) return FA_ERR_NULL;

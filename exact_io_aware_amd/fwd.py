@@ -70,7 +70,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor], *, causal: 
         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
         stream: Optional[torch.cuda.Stream] = None, vt: Optional[torch.Tensor] = None,
         library_workspace: bool = False, cu_seqlens_k: Optional[torch.Tensor] = None,
-        max_seqlen_k: Optional[int] = None):
+        max_seqlen_k: Optional[int] = None, num_splits: Optional[int] = None,
+        split_workspace: Optional[torch.Tensor] = None):
     """Exact attention forward on the GPU: returns ``(o, lse)``.
 
     Fixed length: q ``[B, Hq, Nq, d]``, k/v ``[B, Hkv, Nk, d]``.
@@ -92,6 +93,12 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor], *, causal: 
     passes V already packed by ``pack_v`` (``v`` may then be None).
     ``library_workspace`` calls fa_fwd (fa_fwd_kv) instead, which allocates
     its own stream-ordered workspace.
+
+    Split-KV (16-bit, packed path): ``num_splits`` ranges of keys per unit,
+    merged with their logsumexps (fa_fwd_kv_split_packed); default
+    fa_num_splits, which splits only decode-like shapes (at most 64 query
+    rows per sequence) that would not fill the GPU.  ``split_workspace``
+    (uint8, fa_split_workspace_bytes) may be passed to avoid an allocation.
     """
     if v is None and vt is None:
         raise ValueError("v is needed unless a packed vt is given")
@@ -159,8 +166,25 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor], *, causal: 
     if packed and (vt.dtype != torch.uint8 or not vt.is_cuda or not vt.is_contiguous()):
         raise ValueError("vt must be the contiguous uint8 device tensor pack_v returns")
     dt, odt = _DT[q.dtype], _DT[out_dtype]
+    n_splits = 1
+    if packed:
+        with torch.cuda.device(q.device):
+            n_splits = (_lib.num_splits(B, Hq, Hkv, N, Nk, d, dt) if num_splits is None
+                        else int(num_splits))
     with torch.cuda.device(q.device):
-        if packed and same:
+        if packed and n_splits > 1:
+            name = "fa_fwd_kv_split_packed"
+            need = _lib.split_workspace_bytes(B, Hq, N, d, n_splits)
+            if split_workspace is None:
+                split_workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            elif (split_workspace.dtype != torch.uint8 or not split_workspace.is_cuda
+                  or not split_workspace.is_contiguous()):
+                raise ValueError("split_workspace must be a contiguous uint8 device tensor")
+            status = _lib.fwd_kv_split_packed_raw(
+                q.data_ptr(), k.data_ptr(), vt.data_ptr(), vt.numel(), out.data_ptr(),
+                lse.data_ptr(), B, Hq, Hkv, N, Nk, d, causal, float(scale), cu_ptr, cuk_ptr,
+                n_splits, split_workspace.data_ptr(), split_workspace.numel(), st, dt, odt)
+        elif packed and same:
             name = "fa_fwd_packed"
             status = _lib.fwd_packed_raw(q.data_ptr(), k.data_ptr(), vt.data_ptr(), vt.numel(),
                                          out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, N, d,

@@ -164,6 +164,33 @@ int fa_fwd_kv_packed(const void* q, const void* k, const void* vt, size_t vt_byt
                      float scale, const int* cu_seqlens_q, const int* cu_seqlens_k,
                      void* stream, int in_dtype, int out_dtype);
 
+/* Split-KV (decode).  With few query rows per sequence (decode: one new
+ * token per sequence against its KV cache) the grid has too few workgroups
+ * to keep the GPU's memory system busy, so each unit's keys are cut into
+ * num_splits ranges processed by separate workgroups.  Each writes its
+ * range's normalised partial output and logsumexp into `part`; a merge pass
+ * then forms L = ln sum_s exp(L_s) and O = sum_s exp(L_s - L) O_s, the
+ * same normaliser algebra as the online softmax (Kotaemon page, method list)
+ * applied across ranges, so the result is the exact attention of
+ * fa_fwd_kv.
+ *
+ * fa_num_splits: a split count for these sizes on the current device (1 =
+ * no split; only shapes with at most 64 query rows per sequence split).
+ * fa_split_workspace_bytes: bytes of `part` for num_splits (0 if < 2):
+ * num_splits * B * Hq * Nq * (d + 1) * 4.
+ * fa_fwd_kv_split_packed: fa_fwd_kv_packed with num_splits in [1, 256]
+ * (1 = plain fa_fwd_kv_packed; `part` may then be NULL); `part` is device
+ * memory, 16-byte aligned, clear of o and lse; contents on entry do not
+ * matter.  16-bit inputs only.  Allocates nothing.  fa_fwd_kv (and so
+ * fa_fwd) applies fa_num_splits by itself, inside its own workspace. */
+int fa_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int in_dtype);
+size_t fa_split_workspace_bytes(int B, int Hq, int Nq, int d, int num_splits);
+int fa_fwd_kv_split_packed(const void* q, const void* k, const void* vt, size_t vt_bytes,
+                           void* o, float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                           int causal, float scale, const int* cu_seqlens_q,
+                           const int* cu_seqlens_k, int num_splits, void* part,
+                           size_t part_bytes, void* stream, int in_dtype, int out_dtype);
+
 /* The argument checks of fa_fwd alone: returns what fa_fwd would return
  * before touching the device (FA_OK if it would go on to launch).  Makes no
  * HIP call, so it is usable without a GPU. */

@@ -213,3 +213,29 @@ def kv(**kw):
 ])
 def test_fwd_kv_rejects_before_any_device_call(kw, code):
     assert kv(**kw) == S[code]
+
+
+def split(**kw):
+    a = dict(BASE, Nk=64, vt=VT, vt_bytes=WS, n=4, part=0x800000, part_bytes=1 << 24)
+    a.update(kw)
+    return _lib.fwd_kv_split_packed_raw(a["q"], a["k"], a["vt"], a["vt_bytes"], a["o"],
+                                        a["lse"], a["B"], a["Hq"], a["Hkv"], a["N"], a["Nk"],
+                                        a["d"], a["causal"], a["scale"], a["cu_seqlens"],
+                                        a.get("cu_k", a["cu_seqlens"]), a["n"], a["part"],
+                                        a["part_bytes"], None, a["in_dtype"], a["out_dtype"])
+
+
+def test_split_workspace_bytes():
+    assert fa.split_workspace_bytes(2, 8, 64, 128, 4) == 4 * 2 * 8 * 64 * 129 * 4
+    assert fa.split_workspace_bytes(2, 8, 64, 128, 1) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"n": 0}, "FA_ERR_SHAPE"), ({"n": 257}, "FA_ERR_SHAPE"),
+    ({"part": None}, "FA_ERR_NULL"), ({"part": 0x800008}, "FA_ERR_ALIGN"),
+    ({"part_bytes": 4 * 2 * 8 * 64 * 129 * 4 - 1}, "FA_ERR_WORKSPACE"),
+    ({"part": 0x400000 + 4096}, "FA_ERR_ALIAS"),                 # inside o
+    ({"in_dtype": fa.FA_F32}, "FA_ERR_DTYPE"),
+])
+def test_split_rejects_before_any_device_call(kw, code):
+    assert split(**kw) == S[code]

@@ -16,6 +16,8 @@ storage precision with round-to-nearest-even.  The five named workloads are:
                   Hq=32, Hkv=8, d=128, bf16, causal
 * ``prefill_bf16`` chunked prefill: the last 1024 queries of 8192-token
                   sequences, B=4, Hq=32, Hkv=8, d=128, bf16, causal
+* ``decode_bf16`` decode: one new query per sequence against an 8192-token
+                  KV cache, B=32, Hq=32, Hkv=8, d=128, bf16
 
 When a workload has more keys than queries (``Nk``), k and v are drawn with
 the key count and the queries are the last tokens of each sequence.
@@ -73,6 +75,7 @@ WORKLOADS = {
         Workload("varlen_bf16", 16, 32, 8, 8192, 128, "bf16", True, 1005,
                  varlen=True, len_lo=1024, len_hi=8192),
         Workload("prefill_bf16", 4, 32, 8, 1024, 128, "bf16", True, 1006, Nk=8192),
+        Workload("decode_bf16", 32, 32, 8, 1, 128, "bf16", True, 1007, Nk=8192),
     ]
 }
 
