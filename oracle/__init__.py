@@ -16,6 +16,7 @@ from .exact import (  # noqa: F401
     attention_bruteforce,
     attention_tiled_online,
     attention_qk,
+    attention_backward,
     pair_count,
     softmax_rows,
     visible_keys,

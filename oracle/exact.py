@@ -439,6 +439,88 @@ def pair_count(nq: int, nk: int, causal: bool) -> int:
     return sum(max(0, min(r + off + 1, nk)) for r in range(nq))
 
 
+# ---------------------------------------------------------------------------
+# Backward pass: gradients of the forward map.
+
+def _head_backward(q, k, v, do, causal, scale):
+    """Gradients of one head of one sequence, by the chain rule written out.
+
+    With S = scale * q k^T (masked), P = softmax(S) row-wise and O = P v:
+      dV = P^T dO,   dP = dO v^T,
+      dS = P * (dP - D) with D_r = sum_c P_rc dP_rc = sum_j dO_rj O_rj,
+      dQ = scale * dS k,   dK = scale * dS^T q.
+    Rows are taken in chunks (each complete); dK and dV sum over them.
+    """
+    n, d = q.shape
+    dq = np.empty_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    chunk = max(1, _CHUNK_BYTES // (8 * max(n, 1)))
+    cols = np.arange(n)
+    for s in range(0, n, chunk):
+        r = np.arange(s, min(s + chunk, n))
+        S = scores(q[r], k, scale)
+        if causal:
+            S = causal_mask(S, r, cols)
+        P, _, _ = softmax_rows(S)
+        O = combine(P, v)
+        dv += P.T @ do[r]
+        dP = do[r] @ v.T
+        D = np.sum(do[r] * O, axis=1, keepdims=True)
+        dS = P * (dP - D)
+        dq[r] = scale * (dS @ k)
+        dk += scale * (dS.T @ q[r])
+    return dq, dk, dv
+
+
+def _run_unit_bwd(args):
+    return _head_backward(*args)
+
+
+def attention_backward(q, k, v, do, *, causal: bool, scale: float,
+                       cu_seqlens: Optional[np.ndarray] = None, workers: int = 1):
+    """Gradients (dQ, dK, dV) of sum(O * dO) for the attention forward of
+    :func:`attention`, in float64 (same layouts as q, k, v).
+
+    The Kotaemon page describes the method as tiling plus recomputation (the
+    paragraph after the formula): a backward pass recomputes the score
+    blocks from the saved per-row statistics instead of keeping the n x n
+    matrix.  What it must produce is fixed by calculus: the derivative of
+    the forward map.  For grouped-query attention a K/V head's gradient is
+    the sum over the query heads that read it.
+    """
+    units = list(_units(q, k, cu_seqlens))
+    Hq, Hkv = q.shape[1], k.shape[1]
+    jobs = []
+    for b, h in units:
+        qs, ks, vs = _slices(q, k, v, b, h, cu_seqlens)
+        if cu_seqlens is None:
+            dos = do[b, h]
+        else:
+            dos = do[int(cu_seqlens[b]):int(cu_seqlens[b + 1]), h]
+        jobs.append((qs, ks, vs, dos, causal, scale))
+    if workers <= 1:
+        results = [_run_unit_bwd(j) for j in jobs]
+    else:
+        with ProcessPoolExecutor(max_workers=workers, initializer=_one_blas_thread) as ex:
+            results = list(ex.map(_run_unit_bwd, jobs, chunksize=1))
+    dQ = np.empty(q.shape, dtype=np.float64)
+    dK = np.zeros(k.shape, dtype=np.float64)
+    dV = np.zeros(v.shape, dtype=np.float64)
+    for (b, h), (dq, dk, dv) in zip(units, results):
+        g = _group(h, Hq, Hkv)
+        if cu_seqlens is None:
+            dQ[b, h] = dq
+            dK[b, g] += dk
+            dV[b, g] += dv
+        else:
+            s, e = int(cu_seqlens[b]), int(cu_seqlens[b + 1])
+            dQ[s:e, h] = dq
+            dK[s:e, g] += dk
+            dV[s:e, g] += dv
+    return dQ, dK, dV
+
+
 def unit_flops(n: int, d: int, causal: bool) -> float:
     """Algorithmic FLOP of one head of one sequence: the two contractions
     over the visible (query, key) pairs, 2*d each."""
@@ -455,6 +537,7 @@ def default_workers() -> int:
 
 __all__ = [
     "attention", "attention_rows", "attention_bruteforce",
-    "attention_tiled_online", "attention_qk", "pair_count", "softmax_rows",
+    "attention_tiled_online", "attention_qk", "attention_backward", "pair_count",
+    "softmax_rows",
     "visible_keys", "unit_flops", "default_workers",
 ]

@@ -364,3 +364,122 @@ def check_qk_varlen(attn_qk):
 
 QK_CHECKS = [check_qk_chunk_recipe, check_qk_bruteforce, check_qk_library,
              check_qk_no_visible_key, check_qk_varlen]
+
+
+# ---------------------------------------------------------------------------
+# Backward pass.  Each check takes ``attn_bwd(q, k, v, do, *, causal, scale,
+# cu_seqlens=None) -> (dQ, dK, dV)``.
+
+def _rand_bwd(seed, B=2, Hq=4, Hkv=2, N=7, d=5):
+    r = _rng(seed)
+    return (r.standard_normal((B, Hq, N, d)), r.standard_normal((B, Hkv, N, d)),
+            r.standard_normal((B, Hkv, N, d)), r.standard_normal((B, Hq, N, d)))
+
+
+def check_bwd_finite_differences(attn_bwd):
+    """Central differences (Richardson-extrapolated, step 1e-3) of
+    F = sum(O * dO), with O from the pinned forward oracle, against the
+    gradient, on every input element of a tiny case."""
+    from oracle import attention
+    worst = 0.0
+    for causal in (False, True):
+        q, k, v, do = _rand_bwd(71 + causal, B=1, Hq=2, Hkv=1, N=4, d=3)
+        scale = 0.61
+        grads = attn_bwd(q, k, v, do, causal=causal, scale=scale)
+
+        def F(qq, kk, vv):
+            return float(np.sum(attention(qq, kk, vv, causal=causal, scale=scale)[0] * do))
+
+        for which, (x, g) in enumerate(zip((q, k, v), grads)):
+            for idx in np.ndindex(x.shape):
+                def at(hh):
+                    xs = [q.copy(), k.copy(), v.copy()]
+                    xs[which][idx] += hh
+                    return F(*xs)
+
+                def D(hh):
+                    return (at(hh) - at(-hh)) / (2 * hh)
+                fd = (4 * D(5e-4) - D(1e-3)) / 3
+                worst = max(worst, abs(fd - g[idx]))
+    # Richardson error is ~h^4 plus rounding ~1e-13: scale to the common TOL.
+    return worst * (TOL / 1e-8)
+
+
+def check_bwd_library(attn_bwd):
+    """torch autograd through scaled_dot_product_attention (float64, CPU,
+    GQA), the routine the French HolySheep article calls."""
+    import torch
+    import torch.nn.functional as F
+    worst = 0.0
+    for causal in (False, True):
+        q, k, v, do = _rand_bwd(73 + causal, B=2, Hq=6, Hkv=2, N=29, d=16)
+        scale = 0.27
+        dQ, dK, dV = attn_bwd(q, k, v, do, causal=causal, scale=scale)
+        tq, tk, tv = (torch.from_numpy(x).requires_grad_() for x in (q, k, v))
+        o = F.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale,
+                                           enable_gqa=True)
+        (o * torch.from_numpy(do)).sum().backward()
+        worst = max(worst, _err(dQ, tq.grad.numpy()), _err(dK, tk.grad.numpy()),
+                    _err(dV, tv.grad.numpy()))
+    return worst
+
+
+def check_bwd_closed_forms(attn_bwd):
+    """Facts of the softmax derivative: each row of dS sums to zero, so with
+    all keys equal dQ = 0; shifting every key by w leaves O unchanged, so the
+    dK of a K/V head sums to zero over its keys; P's rows sum to one, so
+    dV summed over keys is dO summed over rows and over the group's query
+    heads; causal row 0 sees one key, so its dQ is 0."""
+    worst = 0.0
+    r = _rng(75)
+    for causal in (False, True):
+        q, k, v, do = _rand_bwd(76 + causal)
+        dQ, dK, dV = attn_bwd(q, k, v, do, causal=causal, scale=0.45)
+        worst = max(worst, float(np.abs(dK.sum(axis=2)).max()))
+        G = q.shape[1] // k.shape[1]
+        dos = do.reshape(do.shape[0], k.shape[1], G, *do.shape[2:]).sum(axis=(2, 3))
+        worst = max(worst, _err(dV.sum(axis=2), dos))
+        if causal:
+            worst = max(worst, float(np.abs(dQ[:, :, 0]).max()))
+        keq = np.broadcast_to(r.standard_normal((2, 2, 1, 5)), k.shape).copy()
+        dQ2, _, _ = attn_bwd(q, keq, v, do, causal=causal, scale=0.45)
+        worst = max(worst, float(np.abs(dQ2).max()))
+    return worst
+
+
+def check_bwd_gqa_equals_repeated(attn_bwd):
+    """GQA gradients = MHA gradients with K/V heads repeated per contiguous
+    group, the K/V ones summed back over the group."""
+    q, k, v, do = _rand_bwd(77, Hq=6, Hkv=2)
+    worst = 0.0
+    for causal in (False, True):
+        dQ, dK, dV = attn_bwd(q, k, v, do, causal=causal, scale=0.5)
+        kr, vr = np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1)
+        dQr, dKr, dVr = attn_bwd(q, kr, vr, do, causal=causal, scale=0.5)
+        sh = (dKr.shape[0], 2, 3) + dKr.shape[2:]
+        worst = max(worst, _err(dQ, dQr), _err(dK, dKr.reshape(sh).sum(axis=2)),
+                    _err(dV, dVr.reshape(sh).sum(axis=2)))
+    return worst
+
+
+def check_bwd_varlen_equals_fixed(attn_bwd):
+    """Packed sequences = each sequence alone."""
+    r = _rng(79)
+    lens = [5, 1, 9]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, Hq, Hkv, d = cu[-1], 4, 2, 3
+    q, k, v, do = (r.standard_normal((T, h, d)) for h in (Hq, Hkv, Hkv, Hq))
+    worst = 0.0
+    for causal in (False, True):
+        dQ, dK, dV = attn_bwd(q, k, v, do, causal=causal, scale=0.7, cu_seqlens=cu)
+        for b in range(3):
+            sl = slice(cu[b], cu[b + 1])
+            one = [x[sl].transpose(1, 0, 2)[None] for x in (q, k, v, do)]
+            g = attn_bwd(*one, causal=causal, scale=0.7)
+            for full, part in zip((dQ, dK, dV), g):
+                worst = max(worst, _err(full[sl], part[0].transpose(1, 0, 2)))
+    return worst
+
+
+BWD_CHECKS = [check_bwd_finite_differences, check_bwd_library, check_bwd_closed_forms,
+              check_bwd_gqa_equals_repeated, check_bwd_varlen_equals_fixed]

@@ -184,3 +184,63 @@ def test_pair_count():
         brute = sum(1 for r in range(nq) for c in range(nk) if c <= r + nk - nq)
         assert oracle.pair_count(nq, nk, True) == brute
         assert oracle.pair_count(nq, nk, False) == nq * nk
+
+
+# ---------------------------------------------------------------------------
+# Backward pass.
+
+@pytest.mark.parametrize("check", C.BWD_CHECKS, ids=lambda f: f.__name__)
+def test_oracle_bwd_pin(check):
+    assert check(oracle.attention_backward) <= C.TOL
+
+
+def _bwd_mutant(name):
+    """A copy of the per-head backward with one plausible mistake."""
+    def head(q, k, v, do, causal, scale):
+        n = q.shape[0]
+        S = scale * (q @ k.T)
+        if causal:
+            S = np.where(np.arange(n)[None, :] > np.arange(n)[:, None], -np.inf, S)
+        P = np.exp(S - S.max(1, keepdims=True))
+        P /= P.sum(1, keepdims=True)
+        O = P @ v
+        dv = (P if name == "dv_untransposed" else P.T) @ do
+        dP = do @ v.T
+        D = dP.sum(1, keepdims=True) if name == "delta_without_p" else \
+            np.sum(do * O, 1, keepdims=True)
+        dS = P * dP if name == "no_delta" else P * (dP - D)
+        dq = (1.0 if name == "dq_no_scale" else scale) * (dS @ k)
+        dk = scale * ((dS if name == "dk_untransposed" else dS.T) @ q)
+        return dq, dk, dv
+    return head
+
+
+@pytest.mark.parametrize("name", ["no_delta", "delta_without_p", "dq_no_scale",
+                                  "dk_untransposed", "dv_untransposed", "gqa_first_head_only"])
+def test_bwd_pins_catch_planted_mistake(name, monkeypatch):
+    if name == "gqa_first_head_only":
+        orig = exact.attention_backward
+
+        def attn_bwd(q, k, v, do, *, causal, scale, cu_seqlens=None, workers=1):
+            G = q.shape[1] // k.shape[1]
+            dQ, dK, dV = orig(q, k, v, do, causal=causal, scale=scale, cu_seqlens=cu_seqlens)
+            if G == 1:
+                return dQ, dK, dV
+            keep = np.zeros(q.shape[1], bool)
+            keep[::G] = True
+            do2 = do.copy()
+            do2[:, ~keep] = 0            # head axis is 1 in both layouts
+            _, dK1, dV1 = orig(q, k, v, do2, causal=causal, scale=scale, cu_seqlens=cu_seqlens)
+            return dQ, dK1, dV1
+    else:
+        monkeypatch.setattr(exact, "_head_backward", _bwd_mutant(name))
+        attn_bwd = exact.attention_backward
+    worst = 0.0
+    for check in C.BWD_CHECKS:
+        try:
+            worst = max(worst, check(attn_bwd))
+        except Exception:
+            worst = np.inf
+        if worst > C.TOL:
+            break
+    assert worst > C.TOL, f"no pin caught the planted mistake {name}"
