@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="gqa_bf16")
     ap.add_argument("--out-dtype", choices=["fp32", "in"], default="fp32")
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
+                    help="bwd: time the backward pass (gradients of sum(O * dO)) instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=0,
                     help="query heads (from the first sequences) the oracle is timed on; "
@@ -171,7 +173,30 @@ def main():
     if packed and decode:
         pack()
 
+    bwd_state = None
+    if args.which == "bwd":
+        if not packed or Nk != w["N"] or cuk is not None:
+            raise SystemExit("--pass bwd needs 16-bit inputs with equal query and key counts")
+        # dO: seeded N(0,1) like the inputs, query-shaped
+        g = workloads.make_custom(w["B"], w["Hq"], w["Hq"], w["d"], w["dtype"], seed=w["seed"] + 100,
+                                  **({"N": w["N"]} if cu is None else {"lengths": w["lengths"]}))
+        dout = up(g["q"])
+        o_f, lse_f = fa.fwd(q, k, v, causal=w["causal"], scale=w["scale"], cu_seqlens=cu,
+                            max_seqlen=max_seqlen)
+        ws = torch.empty(fa.bwd_workspace_bytes(w["B"], w["Hq"], w["Hkv"], w["N"], w["d"], dt_code),
+                         dtype=torch.uint8, device=dev)
+        bwd_state = (dout, o_f, lse_f, ws)
+
     def step(mark=None):
+        if bwd_state is not None:
+            dout, o_f, lse_f, ws = bwd_state
+            if mark is not None:
+                mark[0].record(stream)
+            fa.bwd(q, k, v, o_f, lse_f, dout, causal=w["causal"], scale=w["scale"],
+                   cu_seqlens=cu, max_seqlen=max_seqlen, workspace=ws, stream=stream)
+            if mark is not None:
+                mark[1].record(stream)
+            return
         if packed and not decode:
             pack()
         if mark is not None:
@@ -205,12 +230,14 @@ def main():
     per = [a.elapsed_time(b) for a, b in marks]
     total_ms = ev0.elapsed_time(ev1)
     ms_per_step = total_ms / args.steps
+    if args.which == "bwd":
+        flop = 2.5 * flop     # five contractions per visible pair instead of two
     value = flop / (ms_per_step * 1e-3) / 1e12
     avg_launch_ms = sum(per) / len(per)
     achieved = flop / (avg_launch_ms * 1e-3) / 1e12
     # The rest of a step: the V^T packing pass (and the gaps between launches).
     pack_ms = []
-    if packed and not decode:
+    if packed and not decode and args.which == "fwd":
         pack_ms = [marks[i][1].elapsed_time(marks[i + 1][0]) for i in range(args.steps - 1)]
 
     if decode:
@@ -239,7 +266,9 @@ def main():
         "dtype": w["dtype"], "data": "synthetic",
         "config": {"workload": w["name"], "B": w["B"], "Hq": w["Hq"], "Hkv": w["Hkv"],
                    "N": w["N"], "Nk": Nk, "d": w["d"], "causal": w["causal"],
-                   "out_dtype": args.out_dtype, "kernel": kname,
+                   "out_dtype": args.out_dtype, "pass": args.which,
+                   "kernel": kname if args.which == "fwd" else
+                   "fa_bwd (delta, transposes, dkdv, dq)",
                    "algorithmic_flop_per_step": flop},
         "roofline": roofline,
         "timing": {"attn_launch_ms_avg": round(avg_launch_ms, 4),

@@ -7,6 +7,8 @@ is not gfx950, calls raise.
 """
 from ._lib import (  # noqa: F401
     FA_BF16, FA_F16, FA_F32, STATUS, kernel_name, load, status_string,
-    num_splits, split_workspace_bytes, supported, version, workspace_bytes,
+    bwd_workspace_bytes, num_splits, split_workspace_bytes, supported, version,
+    workspace_bytes,
 )
+from .bwd import bwd  # noqa: F401
 from .fwd import fwd, flops, pack_v  # noqa: F401

@@ -50,6 +50,11 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_kv_split_packed.argtypes = [vp, vp, vp, z, vp, vp, i, i, i, i, i, i, i, f, vp,
                                            vp, i, vp, z, vp, i, i]
     lib.fa_fwd_kv_split_packed.restype = i
+    lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.fa_bwd_workspace_bytes.restype = z
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, z,
+                           vp, i, i, i]
+    lib.fa_bwd.restype = i
     lib.fa_fwd_check.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i, i]
     lib.fa_fwd_check.restype = i
     lib.fa_kernel_name.argtypes = [i, i, i, i, i]
@@ -143,3 +148,16 @@ def fwd_kv_split_packed_raw(q, k, vt, vt_bytes, o, lse, B, Hq, Hkv, Nq, Nk, d, c
     return load().fa_fwd_kv_split_packed(q, k, vt, vt_bytes, o, lse, B, Hq, Hkv, Nq, Nk, d,
                                          int(causal), scale, cu_q, cu_k, n_splits, part,
                                          part_bytes, stream, in_dtype, out_dtype)
+
+
+def bwd_workspace_bytes(B, Hq, Hkv, N, d, in_dtype) -> int:
+    """fa_bwd_workspace_bytes."""
+    return load().fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, in_dtype)
+
+
+def bwd_raw(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale, cu_seqlens,
+            workspace, ws_bytes, stream, in_dtype, o_dtype, grad_dtype) -> int:
+    """fa_bwd with raw integer device addresses and a raw hipStream_t."""
+    return load().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, int(causal),
+                         scale, cu_seqlens, workspace, ws_bytes, stream, in_dtype, o_dtype,
+                         grad_dtype)

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa.so")
 
-SOURCES = ["fa_fwd_kernels.hip", "fa_api.cpp", "fa_validate.cpp"]
+SOURCES = ["fa_fwd_kernels.hip", "fa_bwd_kernels.hip", "fa_api.cpp", "fa_validate.cpp"]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in the generated code.
 HIPCC_FLAGS = [

@@ -165,6 +165,27 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                    cu_seqlens, stream, in_dtype, out_dtype);
 }
 
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int in_dtype) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || (d != 64 && d != 128) ||
+      (in_dtype != FA_F16 && in_dtype != FA_BF16))
+    return 0;
+  const uint64_t n = fa::bwd_workspace_bytes(B, Hq, Hkv, N, d);
+  return n > (uint64_t)SIZE_MAX ? SIZE_MAX : (size_t)n;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
+           int causal, float scale, const int* cu_seqlens, void* workspace,
+           size_t workspace_bytes, void* stream, int in_dtype, int o_dtype, int grad_dtype) {
+  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, B, Hq, Hkv, N, d, causal,
+                scale, in_dtype, o_dtype, grad_dtype, workspace};
+  int st = fa::check_bwd_args(a, workspace_bytes);
+  if (st != FA_OK) return st;
+  st = device_status();
+  if (st != FA_OK) return st;
+  return fa::launch_bwd(a, stream);
+}
+
 const char* fa_kernel_name(int in_dtype, int d, int causal, int varlen,
                            int out_dtype) {
   return fa::kernel_name(in_dtype, d, causal, varlen, out_dtype);

@@ -1,0 +1,615 @@
+// Exact attention backward for gfx950 (MI355X): dQ, dK, dV of sum(O * dO).
+//
+// What is computed (the derivative of the forward map, per head; the
+// Kotaemon page "Kotaemon FlashAttention应用：加快注意力计算" describes the
+// method as tiling plus recomputation, paragraph after the formula): with
+// S = scale * Q K^T (masked), P = softmax(S) = exp(S - L) using the forward's
+// per-row logsumexp L, and D_r = sum_j dO_rj O_rj,
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),
+//   dQ = scale * dS K,  dK = scale * dS^T Q.
+// P is recomputed block by block from the saved L, so no N x N matrix is
+// ever stored; grouped-query K/V gradients sum over the group's query heads.
+//
+// gfx950 mapping (our design):
+//  * fa_bwd_delta: D_r, one 32-lane group per row.
+//  * fa_bwd_dkdv: a workgroup of 4 waves owns 128 keys of one K/V head (each
+//    wave 32 keys, its K and V rows in registers as MFMA B operands) and
+//    streams 64-row query tiles of every query head of the group: Q and dO
+//    row-major (A operands of S = Q K^T and dP = dO V^T) and their transposes
+//    Q^T, dO^T (A operands of dK^T += Q^T dS and dV^T += dO^T P).  S's
+//    accumulator puts one key per lane column, which is exactly the
+//    B-operand layout of P and dS for the two products (the query order in
+//    each 16-row chunk permuted as in the packed transposes).  No atomics.
+//  * fa_bwd_dq: the forward kernel's structure: a wave owns 32 query rows
+//    (Q and dO in registers), streams 64-key tiles of K, V (row-major) and
+//    K^T, forms S^T = K Q^T and dP^T = V dO^T with one query per lane
+//    column, and accumulates dQ^T += K^T dS^T.
+//  * The transposes Q^T, dO^T, K^T are written by the V^T packing kernel of
+//    the forward pass (64-row tiles, rows in the P.V fragment order).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <type_traits>
+
+#include "fa.h"
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+struct BwdParams {
+  const void* q; const void* k; const void* v; const void* o; const void* dout;
+  const float* lse;          // [B][Hq][N], natural log
+  float* delta;              // [B][Hq][N], rowsum(dO * O)
+  const void* qt; const void* dot; const void* kt;   // packed transposes
+  void* dq; void* dk; void* dv;
+  const int* cu_seqlens;
+  int B, N, Hq, Hkv, G, ntiles;
+  int hp, rows_per_wg, n_rblocks, n_hgroups;     // dq grid (as the forward)
+  int kv_blocks;                                 // dkdv: 128-key blocks per sequence
+  float scale, scale_log2;
+  long long q_bs, q_hs, q_rs;     // q, o, dO, dQ element strides
+  long long kv_bs, kv_hs, kv_rs;  // k, v, dK, dV element strides
+};
+
+// ---------------------------------------------------------------------------
+// D_r = sum_j dO_rj * O_rj (fp32).  32 lanes per row, D/32 columns each.
+template <typename T, typename OT, int D, bool VARLEN>
+__global__ __launch_bounds__(256) void fa_bwd_delta(BwdParams p) {
+  constexpr int PER = D / 32;
+  const int row_id = blockIdx.x * 8 + (threadIdx.x >> 5);     // (b, h, r)
+  if (row_id >= p.B * p.Hq * p.N) return;
+  const int r = row_id % p.N;
+  const int bh = row_id / p.N;
+  const int h = bh % p.Hq, b = bh / p.Hq;
+  int seq0 = 0, len = p.N;
+  if (VARLEN) {
+    seq0 = p.cu_seqlens[b];
+    len = p.cu_seqlens[b + 1] - seq0;
+  }
+  if (r >= len) return;
+  const long long off = (VARLEN ? (long long)(seq0 + r) * p.q_rs
+                                : (long long)b * p.q_bs + (long long)r * p.q_rs) +
+                        (long long)h * p.q_hs + (threadIdx.x & 31) * PER;
+  const T* dop = (const T*)p.dout + off;
+  const OT* op = (const OT*)p.o + off;
+  float acc = 0.0f;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) acc += (float)dop[j] * (float)op[j];
+#pragma unroll
+  for (int m = 16; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 32);
+  if ((threadIdx.x & 31) == 0) p.delta[((long long)b * p.Hq + h) * p.N + r] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV.  One workgroup: 4 waves x 32 keys of K/V head g of sequence b.
+template <typename T, int D, bool CAUSAL, bool VARLEN, bool OUT_F32>
+__global__ __launch_bounds__(256, 1) void fa_bwd_dkdv(BwdParams p) {
+  using vec8 = typename Ops<T>::vec8;
+  constexpr int NW = 4, NT = 256;
+  constexpr int BR = 64;                     // query rows per tile (two 32-row blocks)
+  constexpr int DB = D / 32, DC = D / 16, CPR = D / 8, RB = D * 2;
+  constexpr int TILE_BYTES = BR * RB;
+  constexpr int HALF = 32 * RB;
+  constexpr int LOADS = BR * CPR / NT;       // 16-byte loads per thread per tile
+
+  // Per buffer: Q, dO (row-major), Q^T, dO^T (packed), L and D of 64 rows.
+  __shared__ __attribute__((aligned(16))) char q_l0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char q_l1[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char do_l0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char do_l1[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char qt_l0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char qt_l1[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char dot_l0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char dot_l1[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) float ld_l0[2 * BR];   // L*log2(e), then D
+  __shared__ __attribute__((aligned(16))) float ld_l1[2 * BR];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hf = lane >> 5;
+
+  // Key-block-major order: every (sequence, K/V head) takes its first key
+  // block before any takes its second, so with the causal mask (early keys
+  // are seen by the most queries) the longest workgroups start first.
+  const int nbg = p.B * p.Hkv;
+  const int kblk = blockIdx.x / nbg;
+  const int bg = blockIdx.x - kblk * nbg;
+  const int g = bg % p.Hkv, b = bg / p.Hkv;
+  int seq0 = 0, len = p.N;
+  if (VARLEN) {
+    seq0 = p.cu_seqlens[b];
+    len = p.cu_seqlens[b + 1] - seq0;
+  }
+  const int kwg = kblk * (NW * 32);
+  if (kwg >= len) return;                    // uniform
+  const int kw0 = kwg + wave * 32;           // this wave's first key
+  const int key = kw0 + l32;                 // the key of this lane's S column
+
+  const long long kvbase = (VARLEN ? (long long)seq0 * p.kv_rs : (long long)b * p.kv_bs) +
+                           (long long)g * p.kv_hs;
+  // Own K and V rows as B operands: lane (l32, hf) holds row key,
+  // columns 16*dc + 8*hf .. +7.
+  vec8 kf[DC], vf[DC];
+  {
+    const int krows = __builtin_amdgcn_readfirstlane(max(0, min(32, len - kw0)));
+    const rsrc_t rk = make_rsrc((const T*)p.k + kvbase + (long long)min(kw0, len) * p.kv_rs,
+                                (uint32_t)krows * (uint32_t)p.kv_rs * 2);
+    const rsrc_t rv = make_rsrc((const T*)p.v + kvbase + (long long)min(kw0, len) * p.kv_rs,
+                                (uint32_t)krows * (uint32_t)p.kv_rs * 2);
+    const uint32_t ko = (uint32_t)(l32 * p.kv_rs + hf * 8) * 2;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      kf[dc] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(rk, ko + dc * 32, 0, 0));
+      vf[dc] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(rv, ko + dc * 32, 0, 0));
+    }
+  }
+
+  // Tile fill offsets (as the forward: row-major swizzled, and packed).
+  uint32_t roff[LOADS], toff[LOADS];
+  const uint32_t q_rs_bytes = (uint32_t)p.q_rs * 2;
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int pch = tid + NT * i;
+    const int r = pch / CPR, pc = pch % CPR;
+    roff[i] = r * q_rs_bytes + ((pc ^ k_swz<D>(r)) << 4);
+    const int tr = pch / 8, tc = pch % 8;
+    toff[i] = tr * 128 + ((tc ^ vt_swz(tr)) << 4);
+  }
+  // Operand read addresses (as the forward's K and V^T reads).
+  int raddr[DC];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc) raddr[dc] = l32 * RB + (((2 * dc + hf) ^ k_swz<D>(l32)) << 4);
+  int taddr[4];
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) taddr[qq] = l32 * 128 + (((2 * qq + hf) ^ vt_swz(l32)) << 4);
+
+  // Iterations: (query head hh of the group, 64-row query tile t).
+  const int t_first = CAUSAL ? kwg / BR : 0;
+  const int nt = (len + BR - 1) / BR - t_first;   // query tiles per head
+  const int n_it = p.G * nt;
+
+  auto tile_load = [&](int it, char* ql, char* dol, char* qtl, char* dotl, float* ldl)
+      __attribute__((always_inline)) {
+    const int hh = it / nt, t = t_first + it % nt;
+    const int h = g * p.G + hh;
+    const int qb = t * BR;
+    const long long qbase = (VARLEN ? (long long)seq0 * p.q_rs : (long long)b * p.q_bs) +
+                            (long long)h * p.q_hs;
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(len - qb, BR)));
+    const uint32_t rbytes = (uint32_t)rows * q_rs_bytes;
+    const rsrc_t rq = make_rsrc((const T*)p.q + qbase + (long long)min(qb, len) * p.q_rs, rbytes);
+    const rsrc_t rdo = make_rsrc((const T*)p.dout + qbase + (long long)min(qb, len) * p.q_rs, rbytes);
+    const long long tix = ((long long)(b * p.Hq + h) * p.ntiles + t) * TILE_BYTES;
+    const rsrc_t rqt = make_rsrc((const char*)p.qt + tix, (uint32_t)TILE_BYTES);
+    const rsrc_t rdot = make_rsrc((const char*)p.dot + tix, (uint32_t)TILE_BYTES);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int o = (NT * i + 64 * wave) * 16;
+      lds_load16(rq, ql + o, roff[i]);
+      lds_load16(rdo, dol + o, roff[i]);
+      lds_load16(rqt, qtl + o, toff[i]);
+      lds_load16(rdot, dotl + o, toff[i]);
+    }
+    // L and D of the 64 rows (128 floats) from wave 0: lanes 0-15 fetch L
+    // into ldl[0, 64), lanes 16-31 D into ldl[64, 128) (the LDS-direct
+    // destination of lane L is base + 16 * L).
+    if (wave == 0) {
+      const long long lrow = ((long long)b * p.Hq + h) * p.N + qb;
+      const int lrows = __builtin_amdgcn_readfirstlane(max(0, min(len - qb, BR)));
+      const rsrc_t rl = make_rsrc(p.lse + lrow, (uint32_t)lrows * 4);
+      const rsrc_t rd = make_rsrc(p.delta + lrow, (uint32_t)lrows * 4);
+      if (lane < 16) lds_load16(rl, (char*)ldl, lane * 16);
+      else if (lane < 32) lds_load16(rd, (char*)ldl, (lane - 16) * 16);
+    }
+  };
+
+  f32x16 dkacc[DB], dvacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dkacc[db] = f32x16{};
+    dvacc[db] = f32x16{};
+  }
+  const float sl2 = p.scale_log2;
+
+  // One 32-row query block (half hb of the tile in the given buffers).
+  auto block = [&](int it, int hb, const char* ql, const char* dol, const char* qtl,
+                   const char* dotl, const float* ldl) __attribute__((always_inline)) {
+    const int t = t_first + it % nt;
+    const int qr0 = t * BR + 32 * hb;          // first query row of the block
+    // S = Q K^T and dP = dO V^T: element e of lane (key, hf) is query row
+    // qr0 + 8*(e/4) + 4*hf + e%4.
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      const vec8 a = *(const vec8*)(ql + hb * HALF + raddr[dc]);
+      s = Ops<T>::mfma(a, kf[dc], s);
+    }
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      const vec8 a = *(const vec8*)(dol + hb * HALF + raddr[dc]);
+      dp = Ops<T>::mfma(a, vf[dc], dp);
+    }
+    uint32_t ppk[8], dpk[8];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int rl = 32 * hb + 8 * g4 + 4 * hf;   // row within the tile
+      const f32x4 L4 = *(const f32x4*)(ldl + rl);
+      const f32x4 D4 = *(const f32x4*)(ldl + BR + rl);
+      float pe[4], de[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = 4 * g4 + j;
+        const int qr = qr0 + 8 * g4 + 4 * hf + j;
+        const bool vis = qr < len && key < len && !(CAUSAL && key > qr);
+        const float pv = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], sl2, -L4[j] * kLog2e))
+                             : 0.0f;
+        pe[j] = pv;
+        de[j] = pv * (dp[e] - D4[j]);
+      }
+      ppk[2 * g4] = Ops<T>::pack(pe[0], pe[1]);
+      ppk[2 * g4 + 1] = Ops<T>::pack(pe[2], pe[3]);
+      dpk[2 * g4] = Ops<T>::pack(de[0], de[1]);
+      dpk[2 * g4 + 1] = Ops<T>::pack(de[2], de[3]);
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS over the block's two 16-row chunks.
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const u32x4 pb = {ppk[4 * kc], ppk[4 * kc + 1], ppk[4 * kc + 2], ppk[4 * kc + 3]};
+      const u32x4 sb = {dpk[4 * kc], dpk[4 * kc + 1], dpk[4 * kc + 2], dpk[4 * kc + 3]};
+      const vec8 pf = __builtin_bit_cast(vec8, pb), sf = __builtin_bit_cast(vec8, sb);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const vec8 ta = *(const vec8*)(dotl + taddr[2 * hb + kc] + db * 32 * 128);
+        dvacc[db] = Ops<T>::mfma(ta, pf, dvacc[db]);
+        const vec8 tq = *(const vec8*)(qtl + taddr[2 * hb + kc] + db * 32 * 128);
+        dkacc[db] = Ops<T>::mfma(tq, sf, dkacc[db]);
+      }
+    }
+  };
+
+  if (n_it > 0) tile_load(0, q_l0, do_l0, qt_l0, dot_l0, ld_l0);
+  for (int it = 0; it < n_it; it += 2) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    if (it + 1 < n_it) tile_load(it + 1, q_l1, do_l1, qt_l1, dot_l1, ld_l1);
+    block(it, 0, q_l0, do_l0, qt_l0, dot_l0, ld_l0);
+    block(it, 1, q_l0, do_l0, qt_l0, dot_l0, ld_l0);
+    if (it + 1 >= n_it) break;
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    if (it + 2 < n_it) tile_load(it + 2, q_l0, do_l0, qt_l0, dot_l0, ld_l0);
+    block(it + 1, 0, q_l1, do_l1, qt_l1, dot_l1, ld_l1);
+    block(it + 1, 1, q_l1, do_l1, qt_l1, dot_l1, ld_l1);
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+
+  // dK = scale * dK^T^T, dV: lane = key, rows 32*db + 8*g4 + 4*hf + 0..3.
+  if (key < len) {
+    const long long row = kvbase + (long long)key * p.kv_rs;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * db + 8 * g4 + 4 * hf;
+        const float k0 = dkacc[db][4 * g4] * p.scale, k1 = dkacc[db][4 * g4 + 1] * p.scale;
+        const float k2 = dkacc[db][4 * g4 + 2] * p.scale, k3 = dkacc[db][4 * g4 + 3] * p.scale;
+        const float v0 = dvacc[db][4 * g4], v1 = dvacc[db][4 * g4 + 1];
+        const float v2 = dvacc[db][4 * g4 + 2], v3 = dvacc[db][4 * g4 + 3];
+        if (OUT_F32) {
+          *(f32x4*)((float*)p.dk + row + d0) = f32x4{k0, k1, k2, k3};
+          *(f32x4*)((float*)p.dv + row + d0) = f32x4{v0, v1, v2, v3};
+        } else {
+          *(u32x2*)((T*)p.dk + row + d0) = u32x2{Ops<T>::pack(k0, k1), Ops<T>::pack(k2, k3)};
+          *(u32x2*)((T*)p.dv + row + d0) = u32x2{Ops<T>::pack(v0, v1), Ops<T>::pack(v2, v3)};
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ.  The forward kernel's layout: 8 waves, each 32 query rows of one head
+// (up to 4 heads of a K/V group per workgroup), 64-key tiles of K, V and
+// K^T double-buffered in LDS.
+template <typename T, int D, bool CAUSAL, bool VARLEN, bool OUT_F32>
+__global__ __launch_bounds__(512, 2) void fa_bwd_dq(BwdParams p) {
+  using vec8 = typename Ops<T>::vec8;
+  constexpr int NT = 512;                    // 8 waves
+  constexpr int BC = 64;
+  constexpr int DB = D / 32, DC = D / 16, CPR = D / 8, RB = D * 2;
+  constexpr int TILE_BYTES = BC * RB;
+  constexpr int HALF = 32 * RB;
+  constexpr int LOADS = BC * CPR / NT;
+
+  __shared__ __attribute__((aligned(16))) char k_l0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char k_l1[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char v_l0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char v_l1[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char kt_l0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char kt_l1[TILE_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hf = lane >> 5;
+
+  const int unit = blockIdx.x / p.n_rblocks;
+  int rb = blockIdx.x - unit * p.n_rblocks;
+  if (CAUSAL) rb = p.n_rblocks - 1 - rb;     // longest row blocks first
+  const int b = unit / p.n_hgroups;
+  const int hgrp = unit - b * p.n_hgroups;
+  const int h = hgrp * p.hp + (wave % p.hp);
+  const int kvh = (hgrp * p.hp) / p.G;
+  int seq0 = 0, len = p.N;
+  if (VARLEN) {
+    seq0 = p.cu_seqlens[b];
+    len = p.cu_seqlens[b + 1] - seq0;
+  }
+  const int wg_row0 = rb * p.rows_per_wg;
+  if (wg_row0 >= len) return;
+  const int row0 = wg_row0 + (wave / p.hp) * 32;
+  const int kv_end = CAUSAL ? min(wg_row0 + p.rows_per_wg, len) : len;
+  const bool active = row0 < len;
+  const int qrow = row0 + l32;
+
+  const long long qbase = (VARLEN ? (long long)seq0 * p.q_rs : (long long)b * p.q_bs) +
+                          (long long)h * p.q_hs;
+  const long long kvbase = (VARLEN ? (long long)seq0 * p.kv_rs : (long long)b * p.kv_bs) +
+                           (long long)kvh * p.kv_hs;
+  const uint32_t kv_rs_bytes = (uint32_t)p.kv_rs * 2;
+
+  // Q and dO rows as B operands; this lane's L (log2 units) and D.
+  vec8 qf[DC], df[DC];
+  float l2 = __builtin_inff(), dl = 0.0f;
+  {
+    const int qrows = __builtin_amdgcn_readfirstlane(active ? min(32, len - row0) : 0);
+    const uint32_t bytes = (uint32_t)qrows * (uint32_t)p.q_rs * 2;
+    const rsrc_t rq = make_rsrc((const T*)p.q + qbase + (long long)(active ? row0 : 0) * p.q_rs, bytes);
+    const rsrc_t rd = make_rsrc((const T*)p.dout + qbase + (long long)(active ? row0 : 0) * p.q_rs,
+                                bytes);
+    const uint32_t qo = (uint32_t)(l32 * p.q_rs + hf * 8) * 2;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      qf[dc] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(rq, qo + dc * 32, 0, 0));
+      df[dc] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(rd, qo + dc * 32, 0, 0));
+    }
+    if (active && qrow < len) {
+      const long long li = ((long long)b * p.Hq + h) * p.N + qrow;
+      l2 = p.lse[li] * kLog2e;
+      dl = p.delta[li];
+    }
+  }
+
+  uint32_t koff[LOADS], toff[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int pch = tid + NT * i;
+    const int r = pch / CPR, pc = pch % CPR;
+    koff[i] = r * kv_rs_bytes + ((pc ^ k_swz<D>(r)) << 4);
+    const int tr = pch / 8, tc = pch % 8;
+    toff[i] = tr * 128 + ((tc ^ vt_swz(tr)) << 4);
+  }
+  const char* ktp = (const char*)p.kt + (long long)(b * p.Hkv + kvh) * p.ntiles * TILE_BYTES;
+  auto tile_load = [&](int t, char* kl, char* vl, char* ktl) __attribute__((always_inline)) {
+    const int kb = t * BC;
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(len - kb, BC)));
+    const long long at = (long long)min(kb, len) * p.kv_rs;
+    const rsrc_t rk = make_rsrc((const T*)p.k + kvbase + at, (uint32_t)rows * kv_rs_bytes);
+    const rsrc_t rv = make_rsrc((const T*)p.v + kvbase + at, (uint32_t)rows * kv_rs_bytes);
+    const int live = __builtin_amdgcn_readfirstlane(kb < len ? 1 : 0);
+    const rsrc_t rt = make_rsrc(ktp + (long long)min(t, p.ntiles) * TILE_BYTES,
+                                live ? (uint32_t)TILE_BYTES : 0u);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int o = (NT * i + 64 * wave) * 16;
+      lds_load16(rk, kl + o, koff[i]);
+      lds_load16(rv, vl + o, koff[i]);
+      lds_load16(rt, ktl + o, toff[i]);
+    }
+  };
+  int kaddr[DC];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc) kaddr[dc] = l32 * RB + (((2 * dc + hf) ^ k_swz<D>(l32)) << 4);
+  int taddr[4];
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) taddr[qq] = l32 * 128 + (((2 * qq + hf) ^ vt_swz(l32)) << 4);
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  const float sl2 = p.scale_log2;
+
+  auto block = [&](int t, int hb, const char* kl, const char* vl, const char* ktl)
+      __attribute__((always_inline)) {
+    const int kb = t * BC + 32 * hb;
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      const vec8 a = *(const vec8*)(kl + hb * HALF + kaddr[dc]);
+      s = Ops<T>::mfma(a, qf[dc], s);
+    }
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      const vec8 a = *(const vec8*)(vl + hb * HALF + kaddr[dc]);
+      dp = Ops<T>::mfma(a, df[dc], dp);
+    }
+    // Element e of lane (query, hf) is key kb + 8*(e/4) + 4*hf + e%4.
+    uint32_t pk[8];
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      float ds[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int kk = kb + 8 * ((e + j) >> 2) + 4 * hf + ((e + j) & 3);
+        const bool vis = kk < len && !(CAUSAL && kk > qrow);
+        const float pv = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[e + j], sl2, -l2)) : 0.0f;
+        ds[j] = pv * (dp[e + j] - dl);
+      }
+      pk[e >> 1] = Ops<T>::pack(ds[0], ds[1]);
+    }
+    // dQ^T += K^T dS^T.
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const u32x4 sb = {pk[4 * kc], pk[4 * kc + 1], pk[4 * kc + 2], pk[4 * kc + 3]};
+      const vec8 sf = __builtin_bit_cast(vec8, sb);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const vec8 a = *(const vec8*)(ktl + taddr[2 * hb + kc] + db * 32 * 128);
+        acc[db] = Ops<T>::mfma(a, sf, acc[db]);
+      }
+    }
+  };
+
+  const int ntl = (kv_end + BC - 1) / BC;
+  tile_load(0, k_l0, v_l0, kt_l0);
+  for (int t = 0; t < ntl; t += 2) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    if (t + 1 < ntl) tile_load(t + 1, k_l1, v_l1, kt_l1);
+    block(t, 0, k_l0, v_l0, kt_l0);
+    block(t, 1, k_l0, v_l0, kt_l0);
+    if (t + 1 >= ntl) break;
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    if (t + 2 < ntl) tile_load(t + 2, k_l0, v_l0, kt_l0);
+    block(t + 1, 0, k_l1, v_l1, kt_l1);
+    block(t + 1, 1, k_l1, v_l1, kt_l1);
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+
+  if (!active || qrow >= len) return;
+  const long long orow = qbase + (long long)qrow * p.q_rs;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d0 = 32 * db + 8 * g4 + 4 * hf;
+      const float a0 = acc[db][4 * g4] * p.scale, a1 = acc[db][4 * g4 + 1] * p.scale;
+      const float a2 = acc[db][4 * g4 + 2] * p.scale, a3 = acc[db][4 * g4 + 3] * p.scale;
+      if (OUT_F32) {
+        *(f32x4*)((float*)p.dq + orow + d0) = f32x4{a0, a1, a2, a3};
+      } else {
+        *(u32x2*)((T*)p.dq + orow + d0) = u32x2{Ops<T>::pack(a0, a1), Ops<T>::pack(a2, a3)};
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch.
+typedef void (*BwdFn)(BwdParams);
+
+struct BwdVariant {
+  int in_dtype, d, causal, varlen, grad_f32;
+  BwdFn dkdv, dq;
+};
+
+#define FA_BV(T, DT, D, C, VL, OF)                                                     \
+  {DT, D, C, VL, OF, fa_bwd_dkdv<T, D, (C != 0), (VL != 0), (OF != 0)>,                  \
+   fa_bwd_dq<T, D, (C != 0), (VL != 0), (OF != 0)>}
+#define FA_BV_ALL(T, DT, D)                                                             \
+  FA_BV(T, DT, D, 0, 0, 0), FA_BV(T, DT, D, 0, 0, 1), FA_BV(T, DT, D, 0, 1, 0),           \
+  FA_BV(T, DT, D, 0, 1, 1), FA_BV(T, DT, D, 1, 0, 0), FA_BV(T, DT, D, 1, 0, 1),           \
+  FA_BV(T, DT, D, 1, 1, 0), FA_BV(T, DT, D, 1, 1, 1)
+
+const BwdVariant kBwdVariants[] = {
+    FA_BV_ALL(__bf16, FA_BF16, 64), FA_BV_ALL(__bf16, FA_BF16, 128),
+    FA_BV_ALL(_Float16, FA_F16, 64), FA_BV_ALL(_Float16, FA_F16, 128),
+};
+
+struct DeltaVariant {
+  int in_dtype, o_f32, d, varlen;
+  BwdFn fn;
+};
+#define FA_DV(T, DT, D)                                                                 \
+  {DT, 0, D, 0, fa_bwd_delta<T, T, D, false>}, {DT, 0, D, 1, fa_bwd_delta<T, T, D, true>}, \
+  {DT, 1, D, 0, fa_bwd_delta<T, float, D, false>},                                       \
+  {DT, 1, D, 1, fa_bwd_delta<T, float, D, true>}
+const DeltaVariant kDeltaVariants[] = {
+    FA_DV(__bf16, FA_BF16, 64), FA_DV(__bf16, FA_BF16, 128),
+    FA_DV(_Float16, FA_F16, 64), FA_DV(_Float16, FA_F16, 128),
+};
+
+}  // namespace
+
+// Workspace layout of the backward pass: D (fp32 rows, padded to 256 B),
+// then the packed Q^T, dO^T (B * Hq * tiles each) and K^T (B * Hkv * tiles).
+struct BwdLayout {
+  uint64_t delta, qt, dot, kt, total;
+};
+static BwdLayout bwd_layout(int B, int Hq, int Hkv, int N, int d) {
+  BwdLayout l;
+  const uint64_t rows = (uint64_t)B * Hq * N;
+  const uint64_t tile = 128ull * d;
+  l.delta = 0;
+  l.qt = (rows * 4 + 255) & ~255ull;
+  l.dot = l.qt + (uint64_t)B * Hq * vt_tiles(N) * tile;
+  l.kt = l.dot + (uint64_t)B * Hq * vt_tiles(N) * tile;
+  l.total = l.kt + (uint64_t)B * Hkv * vt_tiles(N) * tile;
+  return l;
+}
+
+uint64_t bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
+  return bwd_layout(B, Hq, Hkv, N, d).total;
+}
+
+int launch_bwd(const BwdArgs& a, void* stream) {
+  const bool varlen = a.cu_seqlens != nullptr;
+  const BwdVariant* var = nullptr;
+  for (const BwdVariant& v : kBwdVariants)
+    if (v.in_dtype == a.in_dtype && v.d == a.d && v.causal == a.causal &&
+        v.varlen == (int)varlen && v.grad_f32 == (a.grad_dtype == FA_F32))
+      var = &v;
+  const DeltaVariant* dv = nullptr;
+  for (const DeltaVariant& v : kDeltaVariants)
+    if (v.in_dtype == a.in_dtype && v.o_f32 == (a.o_dtype == FA_F32) && v.d == a.d &&
+        v.varlen == (int)varlen)
+      dv = &v;
+  if (!var || !dv) return FA_ERR_DTYPE;
+  const BwdLayout lay = bwd_layout(a.B, a.Hq, a.Hkv, a.N, a.d);
+  char* ws = (char*)a.workspace;
+
+  BwdParams p;
+  p.q = a.q; p.k = a.k; p.v = a.v; p.o = a.o; p.dout = a.dout; p.lse = a.lse;
+  p.delta = (float*)(ws + lay.delta);
+  p.qt = ws + lay.qt; p.dot = ws + lay.dot; p.kt = ws + lay.kt;
+  p.dq = a.dq; p.dk = a.dk; p.dv = a.dv;
+  p.cu_seqlens = a.cu_seqlens;
+  p.B = a.B; p.N = a.N; p.Hq = a.Hq; p.Hkv = a.Hkv; p.G = a.Hq / a.Hkv;
+  p.ntiles = vt_tiles(a.N);
+  const Plan plan = make_plan(a.B, a.Hq, a.Hkv, a.N, a.d, a.in_dtype);
+  p.hp = plan.hp; p.rows_per_wg = plan.rows_per_wg; p.n_rblocks = plan.n_rblocks;
+  p.n_hgroups = plan.n_hgroups;
+  p.kv_blocks = (a.N + 127) / 128;
+  p.scale = a.scale; p.scale_log2 = a.scale * kLog2e;
+  const long long d = a.d;
+  if (varlen) {
+    p.q_bs = 0; p.q_hs = d; p.q_rs = (long long)a.Hq * d;
+    p.kv_bs = 0; p.kv_hs = d; p.kv_rs = (long long)a.Hkv * d;
+  } else {
+    p.q_rs = d; p.q_hs = (long long)a.N * d; p.q_bs = (long long)a.Hq * a.N * d;
+    p.kv_rs = d; p.kv_hs = (long long)a.N * d; p.kv_bs = (long long)a.Hkv * a.N * d;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  void* args[] = {&p};
+  const uint64_t rows = (uint64_t)a.B * a.Hq * a.N;
+  if (hipLaunchKernel((const void*)dv->fn, dim3((unsigned)((rows + 7) / 8)), dim3(256), args, 0,
+                      s) != hipSuccess)
+    return FA_ERR_LAUNCH;
+  int st = launch_vt_pack(a.q, ws + lay.qt, a.B, a.Hq, a.N, a.d, a.cu_seqlens, a.in_dtype, stream);
+  if (st == FA_OK)
+    st = launch_vt_pack(a.dout, ws + lay.dot, a.B, a.Hq, a.N, a.d, a.cu_seqlens, a.in_dtype, stream);
+  if (st == FA_OK)
+    st = launch_vt_pack(a.k, ws + lay.kt, a.B, a.Hkv, a.N, a.d, a.cu_seqlens, a.in_dtype, stream);
+  if (st != FA_OK) return st;
+  const unsigned g1 = (unsigned)((uint64_t)a.B * a.Hkv * p.kv_blocks);
+  if (hipLaunchKernel((const void*)var->dkdv, dim3(g1), dim3(256), args, 0, s) != hipSuccess)
+    return FA_ERR_LAUNCH;
+  if (hipLaunchKernel((const void*)var->dq, dim3((unsigned)plan.total_wg), dim3(512), args, 0,
+                      s) != hipSuccess)
+    return FA_ERR_LAUNCH;
+  return FA_OK;
+}
+
+}  // namespace fa

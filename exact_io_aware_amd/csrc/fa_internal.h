@@ -118,6 +118,21 @@ int launch_fwd(const LaunchArgs& a, void* stream);
 int launch_vt_pack(const void* v, void* vt, int B, int Hkv, int N, int d, const int* cu_seqlens,
                    int in_dtype, void* stream);
 
+// Backward pass (16-bit inputs).
+struct BwdArgs {
+  const void* q; const void* k; const void* v; const void* o; const void* dout;
+  const float* lse;
+  void* dq; void* dk; void* dv;
+  const int* cu_seqlens;
+  int B, Hq, Hkv, N, d, causal;
+  float scale;
+  int in_dtype, o_dtype, grad_dtype;
+  void* workspace;
+};
+uint64_t bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
+int check_bwd_args(const BwdArgs& a, uint64_t ws_bytes);
+int launch_bwd(const BwdArgs& a, void* stream);
+
 // Static name of the kernel instance for these settings, or nullptr.
 const char* kernel_name(int in_dtype, int d, int causal, int varlen, int out_dtype);
 

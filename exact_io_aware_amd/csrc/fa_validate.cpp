@@ -116,6 +116,48 @@ int check_split_args(const void* part, uint64_t part_bytes, const void* o, const
   return FA_OK;
 }
 
+int check_bwd_args(const BwdArgs& a, uint64_t ws_bytes) {
+  if (!a.q || !a.k || !a.v || !a.o || !a.dout || !a.lse || !a.dq || !a.dk || !a.dv ||
+      !a.workspace)
+    return FA_ERR_NULL;
+  // The forward's checks cover shapes, head dim, GQA, scale, alignment of
+  // q, k, v, o and lse, and o against the inputs.
+  const int st = check_args(a.q, a.k, a.v, a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.N, a.d, a.causal,
+                            a.scale, a.cu_seqlens, a.cu_seqlens, a.in_dtype, a.o_dtype);
+  if (st != FA_OK) return st;
+  if (a.in_dtype == FA_F32) return FA_ERR_DTYPE;
+  if (a.grad_dtype != FA_F32 && a.grad_dtype != a.in_dtype) return FA_ERR_DTYPE;
+  auto mis = [](const void* p, uintptr_t al) { return ((uintptr_t)p) % al != 0; };
+  if (mis(a.dout, 16) || mis(a.dq, 16) || mis(a.dk, 16) || mis(a.dv, 16) ||
+      mis(a.workspace, 16))
+    return FA_ERR_ALIGN;
+  if (ws_bytes < bwd_workspace_bytes(a.B, a.Hq, a.Hkv, a.N, a.d)) return FA_ERR_WORKSPACE;
+  if (grid_size(a.B, a.Hq, a.Hkv, a.N, a.d, a.in_dtype) > (uint64_t)INT32_MAX) return FA_ERR_SHAPE;
+  // Outputs must not overlap each other, the inputs or the workspace.  For
+  // the packed layout only identical start pointers are rejected.
+  const uint64_t qn = (uint64_t)a.B * a.N * a.Hq * a.d, kn = (uint64_t)a.B * a.N * a.Hkv * a.d;
+  const uint64_t gs = elem_size(a.grad_dtype), is = elem_size(a.in_dtype);
+  const bool fixed = a.cu_seqlens == nullptr;
+  struct R { const void* p; uint64_t n; };
+  const R outs[3] = {{a.dq, fixed ? qn * gs : 1}, {a.dk, fixed ? kn * gs : 1},
+                     {a.dv, fixed ? kn * gs : 1}};
+  const R ins[7] = {{a.q, fixed ? qn * is : 1}, {a.k, fixed ? kn * is : 1},
+                    {a.v, fixed ? kn * is : 1}, {a.o, fixed ? qn * elem_size(a.o_dtype) : 1},
+                    {a.dout, fixed ? qn * is : 1},
+                    {a.lse, (uint64_t)a.B * a.Hq * a.N * 4}, {a.workspace, ws_bytes}};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 7; ++j)
+      if (outs[i].p == ins[j].p ||
+          overlap((uintptr_t)outs[i].p, outs[i].n, (uintptr_t)ins[j].p, ins[j].n))
+        return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (outs[i].p == outs[j].p ||
+          overlap((uintptr_t)outs[i].p, outs[i].n, (uintptr_t)outs[j].p, outs[j].n))
+        return FA_ERR_ALIAS;
+  }
+  return FA_OK;
+}
+
 int check_pack_args(const void* v, const void* vt, uint64_t vt_bytes, int B, int Hkv, int N,
                     int d, const int* cu_seqlens, int in_dtype) {
   if (!v || !vt) return FA_ERR_NULL;

@@ -191,6 +191,30 @@ int fa_fwd_kv_split_packed(const void* q, const void* k, const void* vt, size_t 
                            const int* cu_seqlens_k, int num_splits, void* part,
                            size_t part_bytes, void* stream, int in_dtype, int out_dtype);
 
+/* Backward pass: the gradients dQ, dK, dV of sum(O * dO) for the forward of
+ * fa_fwd (same B, Hq, Hkv, N, d, causal, scale, cu_seqlens and layouts).
+ * The Kotaemon page calls the method tiling plus recomputation (the
+ * paragraph after the formula): P is recomputed tile by tile from the
+ * forward's lse instead of being stored, so no N x N matrix is kept.
+ * With D_r = sum_j dO_rj O_rj:  dV = P^T dO,  dS = P * (dO V^T - D),
+ * dQ = scale * dS K,  dK = scale * dS^T Q; a K/V head's gradients sum over
+ * the query heads of its group.
+ *
+ * Inputs: q, k, v (in_dtype FA_F16 or FA_BF16), o (the forward's output in
+ * o_dtype, FA_F32 or in_dtype), dout (in_dtype, o's layout), lse (fp32, as
+ * written by the forward).  Outputs dq (q's layout), dk, dv (k's layout)
+ * in grad_dtype (FA_F32 or in_dtype); they must not overlap any input, each
+ * other or the workspace.  workspace: device memory of
+ * fa_bwd_workspace_bytes() bytes, 16-byte aligned (row sums D and packed
+ * transposes of Q, dO and K); contents on entry do not matter.  Allocates
+ * nothing; errors as fa_fwd plus FA_ERR_WORKSPACE, FA_ERR_DTYPE for fp32
+ * inputs. */
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int in_dtype);
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
+           int causal, float scale, const int* cu_seqlens, void* workspace,
+           size_t workspace_bytes, void* stream, int in_dtype, int o_dtype, int grad_dtype);
+
 /* The argument checks of fa_fwd alone: returns what fa_fwd would return
  * before touching the device (FA_OK if it would go on to launch).  Makes no
  * HIP call, so it is usable without a GPU. */

@@ -80,3 +80,16 @@ def o_bar_derived(dtype: str, abs_weighted: np.ndarray):
     u = {"bf16": 2.0 ** -8, "fp16": 2.0 ** -11, "fp32": 0.0}[dtype]
     return np.maximum(O_TOL[dtype], u * abs_weighted + 1e-3)
 
+
+
+def grad_bar(dtype: str) -> float:
+    """Bar on max |error| of a gradient relative to its largest magnitude.
+
+    The backward rounds P and dS to the input precision for the MFMA
+    contractions (unit roundoff u = 2^-8 bf16, 2^-11 fp16) and sums in fp32:
+    each gradient element is a sum of terms each carrying a relative error
+    <= u, so |error| <= u * sum |terms|.  For N(0,1) inputs the sums of
+    absolute terms stay within a few times the largest gradient magnitude;
+    4u of it is the bar.
+    """
+    return 4.0 * {"bf16": 2.0 ** -8, "fp16": 2.0 ** -11}[dtype]

@@ -239,3 +239,40 @@ def test_split_workspace_bytes():
 ])
 def test_split_rejects_before_any_device_call(kw, code):
     assert split(**kw) == S[code]
+
+
+BWD = dict(q=0x100000, k=0x200000, v=0x300000, o=0x400000, do=0x600000, lse=0x500000,
+           dq=0x1000000, dk=0x2000000, dv=0x3000000, ws=0x4000000, ws_bytes=1 << 24,
+           B=2, Hq=8, Hkv=2, N=64, d=128, causal=1, scale=0.125, cu=None,
+           in_dtype=fa.FA_BF16, o_dtype=fa.FA_F32, g_dtype=fa.FA_F32)
+
+
+def bwd(**kw):
+    a = dict(BWD)
+    a.update(kw)
+    return _lib.bwd_raw(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"],
+                        a["dv"], a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["causal"],
+                        a["scale"], a["cu"], a["ws"], a["ws_bytes"], None, a["in_dtype"],
+                        a["o_dtype"], a["g_dtype"])
+
+
+def test_bwd_workspace_bytes():
+    rows = 2 * 8 * 64 * 4
+    pad = (rows + 255) // 256 * 256
+    tile = 128 * 128
+    assert fa.bwd_workspace_bytes(2, 8, 2, 64, 128, fa.FA_BF16) == pad + 2 * 16 * tile + 4 * tile
+    assert fa.bwd_workspace_bytes(2, 8, 2, 64, 128, fa.FA_F32) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"do": None}, "FA_ERR_NULL"), ({"dk": None}, "FA_ERR_NULL"), ({"ws": None}, "FA_ERR_NULL"),
+    ({"in_dtype": fa.FA_F32, "o_dtype": fa.FA_F32}, "FA_ERR_DTYPE"),
+    ({"g_dtype": fa.FA_F16}, "FA_ERR_DTYPE"),
+    ({"ws_bytes": 1000}, "FA_ERR_WORKSPACE"),
+    ({"dq": 0x1000008}, "FA_ERR_ALIGN"), ({"do": 0x600004}, "FA_ERR_ALIGN"),
+    ({"dq": 0x100000}, "FA_ERR_ALIAS"), ({"dk": 0x1000000 + 4096}, "FA_ERR_ALIAS"),
+    ({"dv": 0x4000000 + 64}, "FA_ERR_ALIAS"),
+    ({"d": 96}, "FA_ERR_HEADDIM"), ({"Hq": 6, "Hkv": 4}, "FA_ERR_GQA"),
+])
+def test_bwd_rejects_before_any_device_call(kw, code):
+    assert bwd(**kw) == S[code]

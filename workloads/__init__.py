@@ -194,4 +194,5 @@ def make_inputs(w: Workload | str) -> dict:
     out["causal"] = w.causal
     out["scale"] = w.scale
     out["name"] = w.name
+    out["seed"] = w.seed
     return out
