@@ -217,6 +217,9 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv(BwdParams p) {
   // One 32-row query block (half hb of the tile in the given buffers).
   auto block = [&](int it, int hb, const char* ql, const char* dol, const char* qtl,
                    const char* dotl, const float* ldl) __attribute__((always_inline)) {
+    // Blocks are not interleaved by the scheduler: that would keep two
+    // blocks' operands live at once.
+    __builtin_amdgcn_sched_barrier(0);
     const int t = t_first + it % nt;
     const int qr0 = t * BR + 32 * hb;          // first query row of the block
     // S = Q K^T and dP = dO V^T: element e of lane (key, hf) is query row
@@ -232,6 +235,15 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv(BwdParams p) {
       const vec8 a = *(const vec8*)(dol + hb * HALF + raddr[dc]);
       dp = Ops<T>::mfma(a, vf[dc], dp);
     }
+    // Operand reads two MFMAs ahead of their use, one per MFMA.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * DC - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
     uint32_t ppk[8], dpk[8];
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
@@ -254,6 +266,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv(BwdParams p) {
       dpk[2 * g4] = Ops<T>::pack(de[0], de[1]);
       dpk[2 * g4 + 1] = Ops<T>::pack(de[2], de[3]);
     }
+    __builtin_amdgcn_sched_barrier(0);
     // dV^T += dO^T P and dK^T += Q^T dS over the block's two 16-row chunks.
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
@@ -268,6 +281,14 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv(BwdParams p) {
         dkacc[db] = Ops<T>::mfma(tq, sf, dkacc[db]);
       }
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * DB - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   if (n_it > 0) tile_load(0, q_l0, do_l0, qt_l0, dot_l0, ld_l0);
@@ -423,6 +444,7 @@ __global__ __launch_bounds__(512, 2) void fa_bwd_dq(BwdParams p) {
 
   auto block = [&](int t, int hb, const char* kl, const char* vl, const char* ktl)
       __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
     const int kb = t * BC + 32 * hb;
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -435,6 +457,15 @@ __global__ __launch_bounds__(512, 2) void fa_bwd_dq(BwdParams p) {
       const vec8 a = *(const vec8*)(vl + hb * HALF + kaddr[dc]);
       dp = Ops<T>::mfma(a, df[dc], dp);
     }
+    // Operand reads two MFMAs ahead of their use, one per MFMA.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * DC - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
     // Element e of lane (query, hf) is key kb + 8*(e/4) + 4*hf + e%4.
     uint32_t pk[8];
 #pragma unroll
@@ -449,6 +480,7 @@ __global__ __launch_bounds__(512, 2) void fa_bwd_dq(BwdParams p) {
       }
       pk[e >> 1] = Ops<T>::pack(ds[0], ds[1]);
     }
+    __builtin_amdgcn_sched_barrier(0);
     // dQ^T += K^T dS^T.
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
@@ -460,6 +492,14 @@ __global__ __launch_bounds__(512, 2) void fa_bwd_dq(BwdParams p) {
         acc[db] = Ops<T>::mfma(a, sf, acc[db]);
       }
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * DB - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   const int ntl = (kv_end + BC - 1) / BC;
