@@ -12,14 +12,17 @@
 //
 // gfx950 mapping (our design):
 //  * fa_bwd_delta: D_r, one 32-lane group per row.
-//  * fa_bwd_dkdv: a workgroup of 4 waves owns 128 keys of one K/V head (each
-//    wave 32 keys, its K and V rows in registers as MFMA B operands) and
-//    streams 64-row query tiles of every query head of the group: Q and dO
-//    row-major (A operands of S = Q K^T and dP = dO V^T) and their transposes
-//    Q^T, dO^T (A operands of dK^T += Q^T dS and dV^T += dO^T P).  S's
+//  * fa_bwd_dkdv<MODE>: a workgroup of 8 waves owns 256 keys of one K/V head
+//    (each wave 32 keys, its K (and V) rows in registers as MFMA B operands)
+//    and streams 64-row query tiles of every query head of the group.  The
+//    dV kernel (MODE 0) reads Q row-major (A operand of S = Q K^T) and dO^T
+//    (A operand of dV^T += dO^T P); the dK kernel (MODE 1) reads Q and dO
+//    row-major (S and dP = dO V^T) and Q^T (dK^T += Q^T dS).  S's
 //    accumulator puts one key per lane column, which is exactly the
-//    B-operand layout of P and dS for the two products (the query order in
-//    each 16-row chunk permuted as in the packed transposes).  No atomics.
+//    B-operand layout of P and dS for the gradient products (the query order
+//    in each 16-row chunk permuted as in the packed transposes).  Split in
+//    two, S is formed twice but neither kernel runs out of registers (fused,
+//    K, V, two score blocks and two accumulators do).  No atomics.
 //  * fa_bwd_dq: the forward kernel's structure: a wave owns 32 query rows
 //    (Q and dO in registers), streams 64-key tiles of K, V (row-major) and
 //    K^T, forms S^T = K Q^T and dP^T = V dO^T with one query per lane
@@ -47,7 +50,7 @@ struct BwdParams {
   const int* cu_seqlens;
   int B, N, Hq, Hkv, G, ntiles;
   int hp, rows_per_wg, n_rblocks, n_hgroups;     // dq grid (as the forward)
-  int kv_blocks;                                 // dkdv: 128-key blocks per sequence
+  int kv_blocks;                                 // dV, dK: 256-key blocks per sequence
   float scale, scale_log2;
   long long q_bs, q_hs, q_rs;     // q, o, dO, dQ element strides
   long long kv_bs, kv_hs, kv_rs;  // k, v, dK, dV element strides
@@ -83,26 +86,31 @@ __global__ __launch_bounds__(256) void fa_bwd_delta(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV.  One workgroup: 4 waves x 32 keys of K/V head g of sequence b.
-template <typename T, int D, bool CAUSAL, bool VARLEN, bool OUT_F32>
-__global__ __launch_bounds__(256, 1) void fa_bwd_dkdv(BwdParams p) {
+// dV (MODE 0) or dK (MODE 1).  One workgroup: 8 waves x 32 keys of K/V head g
+// of sequence b.  The two gradients run as two kernels: fused, the four
+// products' operands and two accumulators exceed one wave's registers.
+//   MODE 0: S = Q K^T, P, dV^T += dO^T P          (tiles Q, dO^T; L)
+//   MODE 1: S, dP = dO V^T, dS, dK^T += Q^T dS    (tiles Q, dO, Q^T; L, D)
+template <typename T, int D, bool CAUSAL, bool VARLEN, bool OUT_F32, int MODE>
+__global__ __launch_bounds__(512, 1) void fa_bwd_dkdv(BwdParams p) {
   using vec8 = typename Ops<T>::vec8;
-  constexpr int NW = 4, NT = 256;
+  constexpr int NW = 8, NT = 512;
   constexpr int BR = 64;                     // query rows per tile (two 32-row blocks)
   constexpr int DB = D / 32, DC = D / 16, CPR = D / 8, RB = D * 2;
   constexpr int TILE_BYTES = BR * RB;
   constexpr int HALF = 32 * RB;
   constexpr int LOADS = BR * CPR / NT;       // 16-byte loads per thread per tile
+  constexpr int DO_BYTES = MODE == 1 ? TILE_BYTES : 16;
+  static_assert(LOADS >= 1 && BR * CPR == LOADS * NT, "tile fill");
 
-  // Per buffer: Q, dO (row-major), Q^T, dO^T (packed), L and D of 64 rows.
+  // Per buffer: Q (row-major), dO (row-major, dK only), the transposed
+  // operand of the gradient product (dO^T for dV, Q^T for dK), L and D.
   __shared__ __attribute__((aligned(16))) char q_l0[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char q_l1[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char do_l0[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char do_l1[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char qt_l0[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char qt_l1[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char dot_l0[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char dot_l1[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char do_l0[DO_BYTES];
+  __shared__ __attribute__((aligned(16))) char do_l1[DO_BYTES];
+  __shared__ __attribute__((aligned(16))) char t_l0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char t_l1[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) float ld_l0[2 * BR];   // L*log2(e), then D
   __shared__ __attribute__((aligned(16))) float ld_l1[2 * BR];
 
@@ -126,24 +134,28 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv(BwdParams p) {
   const int kwg = kblk * (NW * 32);
   if (kwg >= len) return;                    // uniform
   const int kw0 = kwg + wave * 32;           // this wave's first key
+  const bool wave_live = kw0 < len;          // wave-uniform
   const int key = kw0 + l32;                 // the key of this lane's S column
 
   const long long kvbase = (VARLEN ? (long long)seq0 * p.kv_rs : (long long)b * p.kv_bs) +
                            (long long)g * p.kv_hs;
-  // Own K and V rows as B operands: lane (l32, hf) holds row key,
+  // Own K (and V) rows as B operands: lane (l32, hf) holds row key,
   // columns 16*dc + 8*hf .. +7.
-  vec8 kf[DC], vf[DC];
+  vec8 kf[DC], vf[MODE == 1 ? DC : 1];
   {
     const int krows = __builtin_amdgcn_readfirstlane(max(0, min(32, len - kw0)));
-    const rsrc_t rk = make_rsrc((const T*)p.k + kvbase + (long long)min(kw0, len) * p.kv_rs,
-                                (uint32_t)krows * (uint32_t)p.kv_rs * 2);
-    const rsrc_t rv = make_rsrc((const T*)p.v + kvbase + (long long)min(kw0, len) * p.kv_rs,
-                                (uint32_t)krows * (uint32_t)p.kv_rs * 2);
+    const long long at = kvbase + (long long)min(kw0, len) * p.kv_rs;
+    const uint32_t bytes = (uint32_t)krows * (uint32_t)p.kv_rs * 2;
+    const rsrc_t rk = make_rsrc((const T*)p.k + at, bytes);
     const uint32_t ko = (uint32_t)(l32 * p.kv_rs + hf * 8) * 2;
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
+    for (int dc = 0; dc < DC; ++dc)
       kf[dc] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(rk, ko + dc * 32, 0, 0));
-      vf[dc] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(rv, ko + dc * 32, 0, 0));
+    if (MODE == 1) {
+      const rsrc_t rv = make_rsrc((const T*)p.v + at, bytes);
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+        vf[dc] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(rv, ko + dc * 32, 0, 0));
     }
   }
 
@@ -171,7 +183,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv(BwdParams p) {
   const int nt = (len + BR - 1) / BR - t_first;   // query tiles per head
   const int n_it = p.G * nt;
 
-  auto tile_load = [&](int it, char* ql, char* dol, char* qtl, char* dotl, float* ldl)
+  auto tile_load = [&](int it, char* ql, char* dol, char* tl, float* ldl)
       __attribute__((always_inline)) {
     const int hh = it / nt, t = t_first + it % nt;
     const int h = g * p.G + hh;
@@ -180,49 +192,51 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv(BwdParams p) {
                             (long long)h * p.q_hs;
     const int rows = __builtin_amdgcn_readfirstlane(max(0, min(len - qb, BR)));
     const uint32_t rbytes = (uint32_t)rows * q_rs_bytes;
-    const rsrc_t rq = make_rsrc((const T*)p.q + qbase + (long long)min(qb, len) * p.q_rs, rbytes);
-    const rsrc_t rdo = make_rsrc((const T*)p.dout + qbase + (long long)min(qb, len) * p.q_rs, rbytes);
+    const long long at = qbase + (long long)min(qb, len) * p.q_rs;
+    const rsrc_t rq = make_rsrc((const T*)p.q + at, rbytes);
     const long long tix = ((long long)(b * p.Hq + h) * p.ntiles + t) * TILE_BYTES;
-    const rsrc_t rqt = make_rsrc((const char*)p.qt + tix, (uint32_t)TILE_BYTES);
-    const rsrc_t rdot = make_rsrc((const char*)p.dot + tix, (uint32_t)TILE_BYTES);
+    const rsrc_t rt = make_rsrc((const char*)(MODE == 1 ? p.qt : p.dot) + tix, (uint32_t)TILE_BYTES);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int o = (NT * i + 64 * wave) * 16;
       lds_load16(rq, ql + o, roff[i]);
-      lds_load16(rdo, dol + o, roff[i]);
-      lds_load16(rqt, qtl + o, toff[i]);
-      lds_load16(rdot, dotl + o, toff[i]);
+      lds_load16(rt, tl + o, toff[i]);
+    }
+    if (MODE == 1) {
+      const rsrc_t rdo = make_rsrc((const T*)p.dout + at, rbytes);
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) lds_load16(rdo, dol + (NT * i + 64 * wave) * 16, roff[i]);
     }
     // L and D of the 64 rows (128 floats) from wave 0: lanes 0-15 fetch L
     // into ldl[0, 64), lanes 16-31 D into ldl[64, 128) (the LDS-direct
     // destination of lane L is base + 16 * L).
     if (wave == 0) {
       const long long lrow = ((long long)b * p.Hq + h) * p.N + qb;
-      const int lrows = __builtin_amdgcn_readfirstlane(max(0, min(len - qb, BR)));
-      const rsrc_t rl = make_rsrc(p.lse + lrow, (uint32_t)lrows * 4);
-      const rsrc_t rd = make_rsrc(p.delta + lrow, (uint32_t)lrows * 4);
-      if (lane < 16) lds_load16(rl, (char*)ldl, lane * 16);
-      else if (lane < 32) lds_load16(rd, (char*)ldl, (lane - 16) * 16);
+      const rsrc_t rl = make_rsrc(p.lse + lrow, (uint32_t)rows * 4);
+      if (lane < 16) {
+        lds_load16(rl, (char*)ldl, lane * 16);
+      } else if (MODE == 1 && lane < 32) {
+        const rsrc_t rd = make_rsrc(p.delta + lrow, (uint32_t)rows * 4);
+        lds_load16(rd, (char*)ldl, (lane - 16) * 16);
+      }
     }
   };
 
-  f32x16 dkacc[DB], dvacc[DB];
+  f32x16 acc[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    dkacc[db] = f32x16{};
-    dvacc[db] = f32x16{};
-  }
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
   const float sl2 = p.scale_log2;
 
   // One 32-row query block (half hb of the tile in the given buffers).
-  auto block = [&](int it, int hb, const char* ql, const char* dol, const char* qtl,
-                   const char* dotl, const float* ldl) __attribute__((always_inline)) {
-    // Blocks are not interleaved by the scheduler: that would keep two
-    // blocks' operands live at once.
-    __builtin_amdgcn_sched_barrier(0);
+  auto block = [&](int it, int hb, const char* ql, const char* dol, const char* tl,
+                   const float* ldl) __attribute__((always_inline)) {
     const int t = t_first + it % nt;
     const int qr0 = t * BR + 32 * hb;          // first query row of the block
-    // S = Q K^T and dP = dO V^T: element e of lane (key, hf) is query row
+    // A block whose rows all precede this wave's keys (causal), or a wave
+    // with no keys, adds nothing.
+    if (!wave_live || (CAUSAL && qr0 + 31 < kw0)) return;
+    __builtin_amdgcn_sched_barrier(0);
+    // S = Q K^T (and dP = dO V^T): element e of lane (key, hf) is query row
     // qr0 + 8*(e/4) + 4*hf + e%4.
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -230,27 +244,31 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv(BwdParams p) {
       const vec8 a = *(const vec8*)(ql + hb * HALF + raddr[dc]);
       s = Ops<T>::mfma(a, kf[dc], s);
     }
+    if (MODE == 1) {
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
-      const vec8 a = *(const vec8*)(dol + hb * HALF + raddr[dc]);
-      dp = Ops<T>::mfma(a, vf[dc], dp);
+      for (int dc = 0; dc < DC; ++dc) {
+        const vec8 a = *(const vec8*)(dol + hb * HALF + raddr[dc]);
+        dp = Ops<T>::mfma(a, vf[dc], dp);
+      }
     }
     // Operand reads two MFMAs ahead of their use, one per MFMA.
+    constexpr int NM = MODE == 1 ? 2 * DC : DC;
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-    for (int i = 0; i < 2 * DC - 2; ++i) {
+    for (int i = 0; i < NM - 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_sched_barrier(0);
-    uint32_t ppk[8], dpk[8];
+    uint32_t pk[8];
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int rl = 32 * hb + 8 * g4 + 4 * hf;   // row within the tile
       const f32x4 L4 = *(const f32x4*)(ldl + rl);
-      const f32x4 D4 = *(const f32x4*)(ldl + BR + rl);
-      float pe[4], de[4];
+      f32x4 D4 = f32x4{};
+      if (MODE == 1) D4 = *(const f32x4*)(ldl + BR + rl);
+      float pe[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int e = 4 * g4 + j;
@@ -258,32 +276,26 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv(BwdParams p) {
         const bool vis = qr < len && key < len && !(CAUSAL && key > qr);
         const float pv = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], sl2, -L4[j] * kLog2e))
                              : 0.0f;
-        pe[j] = pv;
-        de[j] = pv * (dp[e] - D4[j]);
+        pe[j] = MODE == 1 ? pv * (dp[e] - D4[j]) : pv;
       }
-      ppk[2 * g4] = Ops<T>::pack(pe[0], pe[1]);
-      ppk[2 * g4 + 1] = Ops<T>::pack(pe[2], pe[3]);
-      dpk[2 * g4] = Ops<T>::pack(de[0], de[1]);
-      dpk[2 * g4 + 1] = Ops<T>::pack(de[2], de[3]);
+      pk[2 * g4] = Ops<T>::pack(pe[0], pe[1]);
+      pk[2 * g4 + 1] = Ops<T>::pack(pe[2], pe[3]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // dV^T += dO^T P and dK^T += Q^T dS over the block's two 16-row chunks.
+    // dV^T += dO^T P, or dK^T += Q^T dS, over the block's two 16-row chunks.
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
-      const u32x4 pb = {ppk[4 * kc], ppk[4 * kc + 1], ppk[4 * kc + 2], ppk[4 * kc + 3]};
-      const u32x4 sb = {dpk[4 * kc], dpk[4 * kc + 1], dpk[4 * kc + 2], dpk[4 * kc + 3]};
-      const vec8 pf = __builtin_bit_cast(vec8, pb), sf = __builtin_bit_cast(vec8, sb);
+      const u32x4 pb = {pk[4 * kc], pk[4 * kc + 1], pk[4 * kc + 2], pk[4 * kc + 3]};
+      const vec8 pf = __builtin_bit_cast(vec8, pb);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const vec8 ta = *(const vec8*)(dotl + taddr[2 * hb + kc] + db * 32 * 128);
-        dvacc[db] = Ops<T>::mfma(ta, pf, dvacc[db]);
-        const vec8 tq = *(const vec8*)(qtl + taddr[2 * hb + kc] + db * 32 * 128);
-        dkacc[db] = Ops<T>::mfma(tq, sf, dkacc[db]);
+        const vec8 ta = *(const vec8*)(tl + taddr[2 * hb + kc] + db * 32 * 128);
+        acc[db] = Ops<T>::mfma(ta, pf, acc[db]);
       }
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-    for (int i = 0; i < 4 * DB - 2; ++i) {
+    for (int i = 0; i < 2 * DB - 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
@@ -291,41 +303,38 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv(BwdParams p) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  if (n_it > 0) tile_load(0, q_l0, do_l0, qt_l0, dot_l0, ld_l0);
+  if (n_it > 0) tile_load(0, q_l0, do_l0, t_l0, ld_l0);
   for (int it = 0; it < n_it; it += 2) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
-    if (it + 1 < n_it) tile_load(it + 1, q_l1, do_l1, qt_l1, dot_l1, ld_l1);
-    block(it, 0, q_l0, do_l0, qt_l0, dot_l0, ld_l0);
-    block(it, 1, q_l0, do_l0, qt_l0, dot_l0, ld_l0);
+    if (it + 1 < n_it) tile_load(it + 1, q_l1, do_l1, t_l1, ld_l1);
+    block(it, 0, q_l0, do_l0, t_l0, ld_l0);
+    block(it, 1, q_l0, do_l0, t_l0, ld_l0);
     if (it + 1 >= n_it) break;
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
-    if (it + 2 < n_it) tile_load(it + 2, q_l0, do_l0, qt_l0, dot_l0, ld_l0);
-    block(it + 1, 0, q_l1, do_l1, qt_l1, dot_l1, ld_l1);
-    block(it + 1, 1, q_l1, do_l1, qt_l1, dot_l1, ld_l1);
+    if (it + 2 < n_it) tile_load(it + 2, q_l0, do_l0, t_l0, ld_l0);
+    block(it + 1, 0, q_l1, do_l1, t_l1, ld_l1);
+    block(it + 1, 1, q_l1, do_l1, t_l1, ld_l1);
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
-  // dK = scale * dK^T^T, dV: lane = key, rows 32*db + 8*g4 + 4*hf + 0..3.
+  // dK = scale * (dK^T)^T, or dV: lane = key, rows 32*db + 8*g4 + 4*hf + 0..3.
   if (key < len) {
     const long long row = kvbase + (long long)key * p.kv_rs;
+    void* out = MODE == 1 ? p.dk : p.dv;
+    const float f = MODE == 1 ? p.scale : 1.0f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = 32 * db + 8 * g4 + 4 * hf;
-        const float k0 = dkacc[db][4 * g4] * p.scale, k1 = dkacc[db][4 * g4 + 1] * p.scale;
-        const float k2 = dkacc[db][4 * g4 + 2] * p.scale, k3 = dkacc[db][4 * g4 + 3] * p.scale;
-        const float v0 = dvacc[db][4 * g4], v1 = dvacc[db][4 * g4 + 1];
-        const float v2 = dvacc[db][4 * g4 + 2], v3 = dvacc[db][4 * g4 + 3];
-        if (OUT_F32) {
-          *(f32x4*)((float*)p.dk + row + d0) = f32x4{k0, k1, k2, k3};
-          *(f32x4*)((float*)p.dv + row + d0) = f32x4{v0, v1, v2, v3};
-        } else {
-          *(u32x2*)((T*)p.dk + row + d0) = u32x2{Ops<T>::pack(k0, k1), Ops<T>::pack(k2, k3)};
-          *(u32x2*)((T*)p.dv + row + d0) = u32x2{Ops<T>::pack(v0, v1), Ops<T>::pack(v2, v3)};
-        }
+        const float a0 = acc[db][4 * g4] * f, a1 = acc[db][4 * g4 + 1] * f;
+        const float a2 = acc[db][4 * g4 + 2] * f, a3 = acc[db][4 * g4 + 3] * f;
+        if (OUT_F32)
+          *(f32x4*)((float*)out + row + d0) = f32x4{a0, a1, a2, a3};
+        else
+          *(u32x2*)((T*)out + row + d0) = u32x2{Ops<T>::pack(a0, a1), Ops<T>::pack(a2, a3)};
       }
   }
 }
@@ -542,11 +551,12 @@ typedef void (*BwdFn)(BwdParams);
 
 struct BwdVariant {
   int in_dtype, d, causal, varlen, grad_f32;
-  BwdFn dkdv, dq;
+  BwdFn dv, dk, dq;
 };
 
 #define FA_BV(T, DT, D, C, VL, OF)                                                     \
-  {DT, D, C, VL, OF, fa_bwd_dkdv<T, D, (C != 0), (VL != 0), (OF != 0)>,                  \
+  {DT, D, C, VL, OF, fa_bwd_dkdv<T, D, (C != 0), (VL != 0), (OF != 0), 0>,               \
+   fa_bwd_dkdv<T, D, (C != 0), (VL != 0), (OF != 0), 1>,                                 \
    fa_bwd_dq<T, D, (C != 0), (VL != 0), (OF != 0)>}
 #define FA_BV_ALL(T, DT, D)                                                             \
   FA_BV(T, DT, D, 0, 0, 0), FA_BV(T, DT, D, 0, 0, 1), FA_BV(T, DT, D, 0, 1, 0),           \
@@ -621,7 +631,7 @@ int launch_bwd(const BwdArgs& a, void* stream) {
   const Plan plan = make_plan(a.B, a.Hq, a.Hkv, a.N, a.d, a.in_dtype);
   p.hp = plan.hp; p.rows_per_wg = plan.rows_per_wg; p.n_rblocks = plan.n_rblocks;
   p.n_hgroups = plan.n_hgroups;
-  p.kv_blocks = (a.N + 127) / 128;
+  p.kv_blocks = (a.N + 255) / 256;
   p.scale = a.scale; p.scale_log2 = a.scale * kLog2e;
   const long long d = a.d;
   if (varlen) {
@@ -644,7 +654,8 @@ int launch_bwd(const BwdArgs& a, void* stream) {
     st = launch_vt_pack(a.k, ws + lay.kt, a.B, a.Hkv, a.N, a.d, a.cu_seqlens, a.in_dtype, stream);
   if (st != FA_OK) return st;
   const unsigned g1 = (unsigned)((uint64_t)a.B * a.Hkv * p.kv_blocks);
-  if (hipLaunchKernel((const void*)var->dkdv, dim3(g1), dim3(256), args, 0, s) != hipSuccess)
+  if (hipLaunchKernel((const void*)var->dv, dim3(g1), dim3(512), args, 0, s) != hipSuccess ||
+      hipLaunchKernel((const void*)var->dk, dim3(g1), dim3(512), args, 0, s) != hipSuccess)
     return FA_ERR_LAUNCH;
   if (hipLaunchKernel((const void*)var->dq, dim3((unsigned)plan.total_wg), dim3(512), args, 0,
                       s) != hipSuccess)
