@@ -258,7 +258,7 @@ def main():
         roofline = {"bound": "mfma", "achieved": round(achieved, 2),
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                    "traffic": traffic_for(kname, w["name"])}
+                    "traffic": traffic_for(kname, w["name"]) if args.which == "fwd" else None}
     rec = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
