@@ -17,6 +17,8 @@ from .exact import (  # noqa: F401
     attention_tiled_online,
     attention_qk,
     attention_backward,
+    attention_block_sparse,
+    sparse_pair_count,
     pair_count,
     softmax_rows,
     visible_keys,

@@ -440,6 +440,126 @@ def pair_count(nq: int, nk: int, causal: bool) -> int:
 
 
 # ---------------------------------------------------------------------------
+# Block-sparse attention.
+#
+# The Kotaemon page names block-sparse attention only as a direction of the
+# method, with no layout.  Reading taken here: a 0/1 mask over blocks of
+# ``block`` query rows x ``block`` keys of the (query row, key) grid of each
+# sequence and head admits or removes whole blocks of scores; removed scores
+# are -inf, exactly as the causal mask removes single scores.  Everything
+# else is the definition above.
+
+def sparse_allowed(bm: np.ndarray, rows: np.ndarray, nk: int, block: int, causal: bool,
+                   offset: int) -> np.ndarray:
+    """Visibility of keys 0..nk-1 for the given query rows: the block of
+    (row, key) is admitted by ``bm`` [row blocks, key blocks], and with
+    ``causal`` the key is at most the row's position ``row + offset``."""
+    cols = np.arange(nk)
+    allowed = bm[rows // block][:, cols // block] != 0
+    if causal:
+        allowed &= cols[None, :] <= rows[:, None] + offset
+    return allowed
+
+
+def _head_rows_sparse(q: np.ndarray, k: np.ndarray, v: np.ndarray, bm: np.ndarray,
+                      causal: bool, scale: float, block: int):
+    """One head of one sequence under the block mask ``bm``, by the
+    definition.  Rows that see no key get O = 0 and L = -inf."""
+    nq, nk = q.shape[0], k.shape[0]
+    O = np.zeros((nq, v.shape[1]), dtype=np.float64)
+    L = np.full(nq, -np.inf, dtype=np.float64)
+    chunk = max(1, _CHUNK_BYTES // (8 * max(nk, 1)))
+    for s in range(0, nq, chunk):
+        r = np.arange(s, min(nq, s + chunk))
+        allowed = sparse_allowed(bm, r, nk, block, causal, nk - nq)
+        seen = allowed.any(axis=1)
+        if not seen.any():
+            continue
+        rs = r[seen]
+        S = np.where(allowed[seen], scores(q[rs], k, scale), -np.inf)
+        P, m, ell = softmax_rows(S)
+        O[rs] = combine(P, v)
+        L[rs] = logsumexp_of(m, ell)
+    return O, L
+
+
+def _run_unit_sparse(args):
+    return _head_rows_sparse(*args)
+
+
+def attention_block_sparse(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                           block_mask: np.ndarray, *, causal: bool, scale: float,
+                           block: int = 64, cu_seqlens_q: Optional[np.ndarray] = None,
+                           cu_seqlens_k: Optional[np.ndarray] = None, workers: int = 1):
+    """Block-sparse attention: returns ``(O, L)`` in float64.
+
+    ``block_mask`` has shape ``[Bm, Hm, ceil(Nq/block), ceil(Nk/block)]``
+    with Bm in {1, B} and Hm in {1, Hq} (1 = the same mask for every
+    sequence / query head); entry [b, h, i, j] != 0 admits the scores of
+    query rows [i*block, (i+1)*block) against keys [j*block, (j+1)*block)
+    of sequence b, head h (row and key indices within the sequence; the
+    queries are the last nq tokens, as in :func:`attention_qk`).  With
+    ``causal`` the causal mask applies as well.  Rows that see no key get
+    O = 0 and L = -inf.  Layouts as :func:`attention_qk`.
+    """
+    if (cu_seqlens_q is None) != (cu_seqlens_k is None):
+        raise ValueError("give both cu_seqlens_q and cu_seqlens_k, or neither")
+    Hq, Hkv = q.shape[1], k.shape[1]
+    B = q.shape[0] if cu_seqlens_q is None else len(cu_seqlens_q) - 1
+    bm_all = np.asarray(block_mask)
+    if bm_all.ndim != 4 or bm_all.shape[0] not in (1, B) or bm_all.shape[1] not in (1, Hq):
+        raise ValueError("block_mask must be [1 or B, 1 or Hq, row blocks, key blocks]")
+
+    def mask_of(b, h, nq, nk):
+        m = bm_all[b if bm_all.shape[0] > 1 else 0, h if bm_all.shape[1] > 1 else 0]
+        need = (-(-nq // block), -(-nk // block))
+        if m.shape[0] < need[0] or m.shape[1] < need[1]:
+            raise ValueError("block_mask too small for the sequence")
+        return m[:need[0], :need[1]]
+
+    units = [(b, h) for b in range(B) for h in range(Hq)]
+    jobs = []
+    for b, h in units:
+        g = _group(h, Hq, Hkv)
+        if cu_seqlens_q is None:
+            qs, ks, vs = q[b, h], k[b, g], v[b, g]
+        else:
+            sq, eq = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])
+            sk, ek = int(cu_seqlens_k[b]), int(cu_seqlens_k[b + 1])
+            qs, ks, vs = q[sq:eq, h], k[sk:ek, g], v[sk:ek, g]
+        jobs.append((qs, ks, vs, mask_of(b, h, qs.shape[0], ks.shape[0]), causal, scale, block))
+    if workers <= 1:
+        results = [_run_unit_sparse(j) for j in jobs]
+    else:
+        with ProcessPoolExecutor(max_workers=workers, initializer=_one_blas_thread) as ex:
+            results = list(ex.map(_run_unit_sparse, jobs, chunksize=1))
+    O = np.empty(q.shape, dtype=np.float64)
+    if cu_seqlens_q is None:
+        L = np.empty(q.shape[:3], dtype=np.float64)
+        for (b, h), (o, l) in zip(units, results):
+            O[b, h] = o
+            L[b, h] = l
+        return O, L
+    lens = np.diff(np.asarray(cu_seqlens_q, dtype=np.int64))
+    L = np.full((B, Hq, int(lens.max()) if B else 0), np.nan)
+    for (b, h), (o, l) in zip(units, results):
+        s = int(cu_seqlens_q[b])
+        O[s:s + o.shape[0], h] = o
+        L[b, h, :o.shape[0]] = l
+    return O, L
+
+
+def sparse_pair_count(bm: np.ndarray, nq: int, nk: int, causal: bool, block: int = 64) -> int:
+    """Visible (query, key) pairs of one head of one sequence under the
+    block mask ``bm`` [ceil(nq/block), ceil(nk/block)]."""
+    total = 0
+    for s in range(0, nq, block):
+        r = np.arange(s, min(nq, s + block))
+        total += int(sparse_allowed(bm, r, nk, block, causal, nk - nq).sum())
+    return total
+
+
+# ---------------------------------------------------------------------------
 # Backward pass: gradients of the forward map.
 
 def _head_backward(q, k, v, do, causal, scale):

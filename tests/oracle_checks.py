@@ -367,6 +367,181 @@ QK_CHECKS = [check_qk_chunk_recipe, check_qk_bruteforce, check_qk_library,
 
 
 # ---------------------------------------------------------------------------
+# Block-sparse attention.  Each check takes ``attn_sp(q, k, v, block_mask, *,
+# causal, scale, block=64, cu_seqlens_q=None, cu_seqlens_k=None) -> (O, L)``.
+
+def _elementwise(bm2, nq, nk, block):
+    """The element mask of a block mask, by repeating every entry into a
+    block x block square (numpy kron) and cutting to nq x nk."""
+    return np.kron(bm2 != 0, np.ones((block, block), dtype=bool))[:nq, :nk]
+
+
+def _same_inf(a, b):
+    """-inf in the same places of two L arrays; 0 or inf as an error."""
+    return 0.0 if np.array_equal(np.isneginf(a), np.isneginf(b)) else math.inf
+
+
+def _finite_err(a, b):
+    fa, fb = np.where(np.isneginf(a), 0.0, a), np.where(np.isneginf(b), 0.0, b)
+    return max(_same_inf(a, b), _err(fa, fb))
+
+
+def check_sparse_all_ones(attn_sp):
+    """A mask that admits every block is plain attention (the pinned
+    query/key oracle), fixed and packed, with and without causal, with
+    more keys than queries, at block sizes 4 and 64."""
+    from oracle import attention_qk
+    worst = 0.0
+    for causal in (False, True):
+        for (nq, nk, blk) in ((13, 13, 4), (5, 11, 4), (70, 70, 64), (33, 90, 64)):
+            q, k, v = _rand_qk(81 + nq, B=2, Hq=4, Hkv=2, Nq=nq, Nk=nk, d=5)
+            bm = np.ones((1, 1, -(-nq // blk), -(-nk // blk)), np.uint8)
+            O, L = attn_sp(q, k, v, bm, causal=causal, scale=0.41, block=blk)
+            Oq, Lq = attention_qk(q, k, v, causal=causal, scale=0.41)
+            worst = max(worst, _err(O, Oq), _err(L, Lq))
+    r = _rng(82)
+    nq, nk = [3, 1, 6], [7, 1, 6]
+    cq = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    ck = np.concatenate([[0], np.cumsum(nk)]).astype(np.int32)
+    q = r.standard_normal((cq[-1], 4, 5))
+    k, v = r.standard_normal((ck[-1], 2, 5)), r.standard_normal((ck[-1], 2, 5))
+    for causal in (False, True):
+        O, L = attn_sp(q, k, v, np.ones((3, 4, 2, 2), np.uint8), causal=causal, scale=0.6,
+                       block=4, cu_seqlens_q=cq, cu_seqlens_k=ck)
+        Oq, Lq = attention_qk(q, k, v, causal=causal, scale=0.6, cu_seqlens_q=cq,
+                              cu_seqlens_k=ck)
+        worst = max(worst, _err(O, Oq), _err(np.nan_to_num(L, nan=7.0),
+                                              np.nan_to_num(Lq, nan=7.0)))
+    return worst
+
+
+def check_sparse_library(attn_sp):
+    """torch's scaled_dot_product_attention, float64 on the CPU, with the
+    block mask expanded to an explicit boolean mask (numpy kron) and
+    combined with the bottom-right causal mask; a different random mask per
+    sequence and query head; every row keeps key block 0 so that no row is
+    empty (the library returns NaN there)."""
+    import torch
+    import torch.nn.functional as F
+    worst = 0.0
+    r = _rng(83)
+    B, Hq, Hkv, Nq, Nk, d, blk = 2, 6, 3, 11, 17, 16, 3
+    for causal in (False, True):
+        q, k, v = _rand_qk(84 + causal, B=B, Hq=Hq, Hkv=Hkv, Nq=Nq, Nk=Nk, d=d)
+        bm = (r.random((B, Hq, -(-Nq // blk), -(-Nk // blk))) < 0.5).astype(np.uint8)
+        bm[..., 0] = 1
+        O, L = attn_sp(q, k, v, bm, causal=causal, scale=0.23, block=blk)
+        vis = np.stack([np.stack([_elementwise(bm[b, h], Nq, Nk, blk) for h in range(Hq)])
+                        for b in range(B)])
+        if causal:
+            vis &= np.arange(Nk)[None, :] <= np.arange(Nq)[:, None] + (Nk - Nq)
+        tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+        kr = tk.repeat_interleave(Hq // Hkv, dim=1)
+        vr = tv.repeat_interleave(Hq // Hkv, dim=1)
+        tm = torch.from_numpy(vis)
+        To = F.scaled_dot_product_attention(tq, kr, vr, attn_mask=tm, scale=0.23)
+        S = (0.23 * torch.matmul(tq, kr.transpose(-1, -2))).masked_fill(~tm, -math.inf)
+        worst = max(worst, _err(O, To.numpy()), _err(L, torch.logsumexp(S, -1).numpy()))
+    return worst
+
+
+def check_sparse_bruteforce(attn_sp):
+    """Pure-Python sums over the admitted (row, key) pairs, no maximum
+    subtracted, on tiny inputs whose masks leave some rows with no key
+    (O = 0, L = -inf there)."""
+    r = _rng(85)
+    B, Hq, Hkv, Nq, Nk, d, blk = 1, 2, 1, 5, 7, 3, 2
+    worst = 0.0
+    for causal in (False, True):
+        q, k, v = _rand_qk(86 + causal, B=B, Hq=Hq, Hkv=Hkv, Nq=Nq, Nk=Nk, d=d)
+        bm = (r.random((B, Hq, 3, 4)) < 0.5).astype(np.uint8)
+        bm[0, 0, 1, :] = 0                       # rows 2, 3 of head 0 see nothing
+        bm[0, 1, 0, :] = 1
+        O, L = attn_sp(q, k, v, bm, causal=causal, scale=0.7, block=blk)
+        for h in range(Hq):
+            for i in range(Nq):
+                keys = [c for c in range(Nk) if bm[0, h, i // blk, c // blk]
+                        and (not causal or c <= i + Nk - Nq)]
+                if not keys:
+                    if not (L[0, h, i] == -math.inf and not np.any(O[0, h, i])):
+                        return math.inf
+                    continue
+                w = [math.exp(0.7 * sum(q[0, h, i, t] * k[0, 0, c, t] for t in range(d)))
+                     for c in keys]
+                tot = math.fsum(w)
+                for t in range(d):
+                    o = math.fsum(wc * v[0, 0, c, t] for wc, c in zip(w, keys)) / tot
+                    worst = max(worst, abs(O[0, h, i, t] - o))
+                worst = max(worst, abs(L[0, h, i] - math.log(tot)))
+    return worst
+
+
+def check_sparse_removed_key_blocks(attn_sp):
+    """Without causal, a mask that admits the same key blocks for every row
+    block is attention over those keys alone (the pinned query/key oracle
+    on the gathered K and V)."""
+    from oracle import attention_qk
+    q, k, v = _rand_qk(87, B=2, Hq=4, Hkv=2, Nq=9, Nk=22, d=4)
+    keep_blocks = np.array([1, 0, 1, 1, 0, 1], np.uint8)      # blocks of 4 keys
+    bm = np.broadcast_to(keep_blocks, (1, 1, 3, 6)).copy()
+    O, L = attn_sp(q, k, v, bm, causal=False, scale=0.5, block=4)
+    keep = np.repeat(keep_blocks != 0, 4)[:22]
+    Oq, Lq = attention_qk(q, k[:, :, keep], v[:, :, keep], causal=False, scale=0.5)
+    return max(_err(O, Oq), _err(L, Lq))
+
+
+def check_sparse_block_diagonal(attn_sp):
+    """A block-diagonal mask makes every block of rows its own sequence:
+    equal to the pinned packed-sequence oracle with one sequence per block
+    (causal and not)."""
+    from oracle import attention
+    r = _rng(88)
+    N, blk = 10, 4
+    q, k, v = (r.standard_normal((1, h, N, 3)) for h in (4, 2, 2))
+    bm = np.eye(3, dtype=np.uint8)[None, None]
+    cu = np.array([0, 4, 8, 10], np.int32)
+    worst = 0.0
+    for causal in (False, True):
+        O, L = attn_sp(q, k, v, bm, causal=causal, scale=0.9, block=blk)
+        Op, Lp = attention(*(x[0].transpose(1, 0, 2) for x in (q, k, v)), causal=causal,
+                           scale=0.9, cu_seqlens=cu)
+        worst = max(worst, _err(O[0], Op.transpose(1, 0, 2)))
+        for b in range(3):
+            worst = max(worst, _err(L[0, :, cu[b]:cu[b + 1]], Lp[b, :, :cu[b + 1] - cu[b]]))
+    return worst
+
+
+def check_sparse_broadcast(attn_sp):
+    """A mask given once (1 x 1) equals the same mask repeated for every
+    sequence and head; a per-head mask gives each head its own pattern
+    (head h alone, run as a one-head problem, matches)."""
+    r = _rng(89)
+    q, k, v = _rand_qk(90, B=2, Hq=4, Hkv=2, Nq=8, Nk=8, d=3)
+    one = (r.random((1, 1, 4, 4)) < 0.6).astype(np.uint8)
+    one[..., 0] = 1
+    worst = 0.0
+    for causal in (False, True):
+        O1, L1 = attn_sp(q, k, v, one, causal=causal, scale=0.5, block=2)
+        Or, Lr = attn_sp(q, k, v, np.broadcast_to(one, (2, 4, 4, 4)).copy(), causal=causal,
+                         scale=0.5, block=2)
+        worst = max(worst, _finite_err(L1, Lr), _err(O1, Or))
+        per = (r.random((2, 4, 4, 4)) < 0.6).astype(np.uint8)
+        Oh, Lh = attn_sp(q, k, v, per, causal=causal, scale=0.5, block=2)
+        for b in range(2):
+            for h in range(4):
+                g = h // 2
+                Os, Ls = attn_sp(q[b:b + 1, h:h + 1], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1],
+                                 per[b:b + 1, h:h + 1], causal=causal, scale=0.5, block=2)
+                worst = max(worst, _err(Oh[b, h], Os[0, 0]), _finite_err(Lh[b, h], Ls[0, 0]))
+    return worst
+
+
+SPARSE_CHECKS = [check_sparse_all_ones, check_sparse_library, check_sparse_bruteforce,
+                 check_sparse_removed_key_blocks, check_sparse_block_diagonal,
+                 check_sparse_broadcast]
+
+
+# ---------------------------------------------------------------------------
 # Backward pass.  Each check takes ``attn_bwd(q, k, v, do, *, causal, scale,
 # cu_seqlens=None) -> (dQ, dK, dV)``.
 

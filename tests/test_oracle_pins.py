@@ -187,6 +187,74 @@ def test_pair_count():
 
 
 # ---------------------------------------------------------------------------
+# Block-sparse attention.
+
+@pytest.mark.parametrize("check", C.SPARSE_CHECKS, ids=lambda f: f.__name__)
+def test_oracle_sparse_pin(check):
+    assert check(oracle.attention_block_sparse) <= C.TOL
+
+
+def _sparse_allowed_mutant(name):
+    def allowed(bm, rows, nk, block, causal, offset):
+        cols = np.arange(nk)
+        rb = (rows + 1) // block if name == "row_block_off_by_one" else rows // block
+        cb = (cols + 1) // block if name == "key_block_off_by_one" else cols // block
+        rb = np.minimum(rb, bm.shape[0] - 1)
+        cb = np.minimum(cb, bm.shape[1] - 1)
+        if name == "block_transposed":        # key block used as the row-block index
+            a = bm[np.minimum(cb, bm.shape[0] - 1)][:, np.minimum(rb, bm.shape[1] - 1)].T != 0
+        elif name == "mask_ignored":
+            a = np.ones((rows.size, nk), bool)
+        else:
+            a = bm[rb][:, cb] != 0
+        if causal and name != "causal_dropped":
+            a &= cols[None, :] <= rows[:, None] + (0 if name == "causal_top_left" else offset)
+        return a
+    return allowed
+
+
+@pytest.mark.parametrize("name", ["row_block_off_by_one", "key_block_off_by_one",
+                                  "block_transposed", "mask_ignored", "causal_dropped",
+                                  "causal_top_left", "mask_of_kv_head", "empty_rows_zero"])
+def test_sparse_pins_catch_planted_mistake(name, monkeypatch):
+    orig = exact.attention_block_sparse
+    if name == "mask_of_kv_head":
+        def attn_sp(q, k, v, bm, *, causal, scale, block=64, cu_seqlens_q=None,
+                    cu_seqlens_k=None):
+            G = q.shape[1] // k.shape[1]
+            if bm.shape[1] > 1:             # head h reads the mask of head h // G
+                bm = bm[:, np.arange(bm.shape[1]) // G]
+            return orig(q, k, v, bm, causal=causal, scale=scale, block=block,
+                        cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k)
+    elif name == "empty_rows_zero":
+        def attn_sp(*a, **kw):
+            O, L = orig(*a, **kw)
+            return O, np.where(np.isneginf(L), 0.0, L)
+    else:
+        monkeypatch.setattr(exact, "sparse_allowed", _sparse_allowed_mutant(name))
+        attn_sp = orig
+    worst = 0.0
+    for check in C.SPARSE_CHECKS:
+        try:
+            worst = max(worst, check(attn_sp))
+        except Exception:
+            worst = np.inf
+        if worst > C.TOL:
+            break
+    assert worst > C.TOL, f"no pin caught the planted mistake {name}"
+
+
+def test_sparse_pair_count():
+    r = np.random.default_rng(91)
+    for nq, nk, blk in ((9, 9, 2), (5, 13, 4), (13, 5, 3)):
+        bm = (r.random((-(-nq // blk), -(-nk // blk))) < 0.5).astype(np.uint8)
+        for causal in (False, True):
+            brute = sum(1 for i in range(nq) for c in range(nk)
+                        if bm[i // blk, c // blk] and (not causal or c <= i + nk - nq))
+            assert oracle.sparse_pair_count(bm, nq, nk, causal, blk) == brute
+
+
+# ---------------------------------------------------------------------------
 # Backward pass.
 
 @pytest.mark.parametrize("check", C.BWD_CHECKS, ids=lambda f: f.__name__)

@@ -18,6 +18,10 @@ storage precision with round-to-nearest-even.  The five named workloads are:
                   sequences, B=4, Hq=32, Hkv=8, d=128, bf16, causal
 * ``decode_bf16`` decode: one new query per sequence against an 8192-token
                   KV cache, B=32, Hq=32, Hkv=8, d=128, bf16
+* ``streaming_bf16`` block-sparse: the gqa_bf16 shape (seed 1008) under a
+                  streaming block mask of 64 x 64 blocks: every query block
+                  sees key block 0 (the "sink") and the 16 key blocks ending
+                  at its own (a 1024-key window), causal
 
 When a workload has more keys than queries (``Nk``), k and v are drawn with
 the key count and the queries are the last tokens of each sequence.
@@ -42,7 +46,10 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "HEADLINE", "make_inputs", "make_custom", "make_custom_qk",
     "round_to_bf16_bits", "bf16_bits_to_f32", "to_f64", "varlen_lengths",
+    "streaming_block_mask", "random_block_mask", "SPARSE_BLOCK",
 ]
+
+SPARSE_BLOCK = 64        # query rows and keys per block of a block mask
 
 
 @dataclasses.dataclass(frozen=True)
@@ -60,6 +67,8 @@ class Workload:
     len_lo: int = 0      # varlen: inclusive range of the uniform lengths
     len_hi: int = 0
     Nk: int = 0          # keys per sequence when more than the queries (0: = N)
+    sink_blocks: int = 0     # block-sparse streaming mask (0 window: dense)
+    window_blocks: int = 0
 
     @property
     def scale(self) -> float:
@@ -76,6 +85,8 @@ WORKLOADS = {
                  varlen=True, len_lo=1024, len_hi=8192),
         Workload("prefill_bf16", 4, 32, 8, 1024, 128, "bf16", True, 1006, Nk=8192),
         Workload("decode_bf16", 32, 32, 8, 1, 128, "bf16", True, 1007, Nk=8192),
+        Workload("streaming_bf16", 4, 32, 8, 4096, 128, "bf16", True, 1008,
+                 sink_blocks=1, window_blocks=16),
     ]
 }
 
@@ -181,6 +192,26 @@ def make_custom_qk(B: int, Hq: int, Hkv: int, d: int, dtype: str, seed: int,
     return _draw(rng, B, Hq, Hkv, d, dtype, Nq, lengths_q, Nk, lengths_k)
 
 
+def streaming_block_mask(n: int, sink_blocks: int, window_blocks: int,
+                         block: int = SPARSE_BLOCK) -> np.ndarray:
+    """Streaming pattern over an n x n (query, key) grid, as a uint8 block
+    mask [1, 1, nb, nb]: query block i admits key blocks j < sink_blocks and
+    i - window_blocks < j <= i."""
+    nb = -(-n // block)
+    i = np.arange(nb)[:, None]
+    j = np.arange(nb)[None, :]
+    m = (j < sink_blocks) | ((j <= i) & (j > i - window_blocks))
+    return m.astype(np.uint8)[None, None]
+
+
+def random_block_mask(rng: np.random.Generator, Bm: int, Hm: int, nq: int, nk: int,
+                      density: float, block: int = SPARSE_BLOCK) -> np.ndarray:
+    """A uint8 block mask [Bm, Hm, ceil(nq/block), ceil(nk/block)] whose
+    entries are 1 with probability ``density``."""
+    shape = (Bm, Hm, -(-nq // block), -(-nk // block))
+    return (rng.random(shape) < density).astype(np.uint8)
+
+
 def make_inputs(w: Workload | str) -> dict:
     """Seeded inputs of a named workload (see the module docstring)."""
     if isinstance(w, str):
@@ -195,4 +226,6 @@ def make_inputs(w: Workload | str) -> dict:
     out["scale"] = w.scale
     out["name"] = w.name
     out["seed"] = w.seed
+    if w.window_blocks:
+        out["block_mask"] = streaming_block_mask(w.N, w.sink_blocks, w.window_blocks)
     return out
