@@ -99,7 +99,12 @@ def cpu_baseline(w, heads: int):
         ks = np.ascontiguousarray(k[:nb, :hq // G])
         vs = np.ascontiguousarray(v[:nb, :hq // G])
         t0 = time.perf_counter()
-        if w["Nk"] != w["N"]:
+        if w.get("block_mask") is not None:
+            oracle.attention_block_sparse(qs, ks, vs, w["block_mask"], causal=w["causal"],
+                                          scale=w["scale"], workers=workers)
+            fl = nb * hq * 4.0 * w["d"] * oracle.sparse_pair_count(
+                w["block_mask"][0, 0], w["N"], w["Nk"], w["causal"])
+        elif w["Nk"] != w["N"]:
             oracle.attention_qk(qs, ks, vs, causal=w["causal"], scale=w["scale"],
                                 workers=workers)
             fl = nb * hq * 4.0 * w["d"] * oracle.pair_count(w["N"], w["Nk"], w["causal"])
@@ -144,7 +149,8 @@ def main():
     lengths_k = None
     if Nk != w["N"] or cuk is not None:
         lengths_k = [Nk] * w["B"] if cuk is None else list(np.diff(w["cu_seqlens_k"]))
-    flop = fa.flops(w["Hq"], w["d"], lengths, w["causal"], lengths_k)
+    bm_np = w.get("block_mask")
+    flop = fa.flops(w["Hq"], w["d"], lengths, w["causal"], lengths_k, block_mask=bm_np)
     dt_code = {"fp32": fa.FA_F32, "fp16": fa.FA_F16, "bf16": fa.FA_BF16}[w["dtype"]]
     kname = fa.kernel_name(dt_code, w["d"], w["causal"], cu is not None,
                            fa.FA_F32 if args.out_dtype == "fp32" else dt_code)
@@ -161,6 +167,11 @@ def main():
                          dtype=torch.uint8, device=dev)
     n_splits = fa.num_splits(w["B"], w["Hq"], w["Hkv"], w["N"], Nk, w["d"], dt_code) \
         if packed else 1
+    bm = None
+    if bm_np is not None:          # block-sparse: never split over keys
+        bm = torch.from_numpy(np.ascontiguousarray(bm_np)).to(dev)
+        n_splits = 1
+        kname += "_sparse"
     split_ws = None
     if n_splits > 1:
         split_ws = torch.empty(fa.split_workspace_bytes(w["B"], w["Hq"], w["N"], w["d"],
@@ -204,8 +215,9 @@ def main():
         fa.fwd(q, k, None if packed else v, causal=w["causal"], scale=w["scale"],
                cu_seqlens=cu, max_seqlen=max_seqlen, out_dtype=out_dtype, out=o, lse=lse,
                stream=stream, vt=vt, cu_seqlens_k=cuk,
-               max_seqlen_k=Nk if cu is not None else None, num_splits=n_splits,
-               split_workspace=split_ws)
+               max_seqlen_k=Nk if cu is not None else None,
+               num_splits=n_splits if bm is None else None, split_workspace=split_ws,
+               block_mask=bm)
         if mark is not None:
             mark[1].record(stream)
 

@@ -50,6 +50,12 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_kv_split_packed.argtypes = [vp, vp, vp, z, vp, vp, i, i, i, i, i, i, i, f, vp,
                                            vp, i, vp, z, vp, i, i]
     lib.fa_fwd_kv_split_packed.restype = i
+    lib.fa_fwd_sparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, vp, i, i,
+                                  vp, i, i]
+    lib.fa_fwd_sparse.restype = i
+    lib.fa_fwd_sparse_packed.argtypes = [vp, vp, vp, z, vp, vp, i, i, i, i, i, i, i, f, vp, vp,
+                                         vp, i, i, vp, i, i]
+    lib.fa_fwd_sparse_packed.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = z
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, z,
@@ -161,3 +167,20 @@ def bwd_raw(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale, 
     return load().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, int(causal),
                          scale, cu_seqlens, workspace, ws_bytes, stream, in_dtype, o_dtype,
                          grad_dtype)
+
+
+def fwd_sparse_raw(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, cu_q, cu_k,
+                   mask, mask_batches, mask_heads, stream, in_dtype, out_dtype) -> int:
+    """fa_fwd_sparse with raw integer device addresses and a raw hipStream_t."""
+    return load().fa_fwd_sparse(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, int(causal), scale,
+                                cu_q, cu_k, mask, mask_batches, mask_heads, stream, in_dtype,
+                                out_dtype)
+
+
+def fwd_sparse_packed_raw(q, k, vt, vt_bytes, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale,
+                          cu_q, cu_k, mask, mask_batches, mask_heads, stream, in_dtype,
+                          out_dtype) -> int:
+    """fa_fwd_sparse_packed with raw integer device addresses."""
+    return load().fa_fwd_sparse_packed(q, k, vt, vt_bytes, o, lse, B, Hq, Hkv, Nq, Nk, d,
+                                       int(causal), scale, cu_q, cu_k, mask, mask_batches,
+                                       mask_heads, stream, in_dtype, out_dtype)

@@ -165,6 +165,60 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                    cu_seqlens, stream, in_dtype, out_dtype);
 }
 
+int fa_fwd_sparse_packed(const void* q, const void* k, const void* vt, size_t vt_bytes,
+                         void* o, float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                         int causal, float scale, const int* cu_seqlens_q,
+                         const int* cu_seqlens_k, const unsigned char* block_mask,
+                         int mask_batches, int mask_heads, void* stream, int in_dtype,
+                         int out_dtype) {
+  int st = fa::check_packed_args(q, k, vt, vt_bytes, o, lse, B, Hq, Hkv, Nq, Nk, d, causal,
+                                 scale, cu_seqlens_q, cu_seqlens_k, in_dtype, out_dtype);
+  if (st != FA_OK) return st;
+  st = fa::check_sparse_args(block_mask, mask_batches, mask_heads, o, lse, B, Hq, Nq, Nk, d,
+                             in_dtype, out_dtype, cu_seqlens_q != nullptr);
+  if (st != FA_OK) return st;
+  st = device_status();
+  if (st != FA_OK) return st;
+  fa::LaunchArgs a{q, k, nullptr, o, lse, vt, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, Nq, Nk,
+                   d, causal, scale, in_dtype, out_dtype};
+  a.block_mask = block_mask;
+  a.mask_batches = mask_batches;
+  a.mask_heads = mask_heads;
+  return fa::launch_fwd(a, stream);
+}
+
+int fa_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k,
+                  const unsigned char* block_mask, int mask_batches, int mask_heads,
+                  void* stream, int in_dtype, int out_dtype) {
+  int st = fa::check_args(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale,
+                          cu_seqlens_q, cu_seqlens_k, in_dtype, out_dtype);
+  if (st != FA_OK) return st;
+  st = fa::check_sparse_args(block_mask, mask_batches, mask_heads, o, lse, B, Hq, Nq, Nk, d,
+                             in_dtype, out_dtype, cu_seqlens_q != nullptr);
+  if (st != FA_OK) return st;
+  st = device_status();
+  if (st != FA_OK) return st;
+  const uint64_t need = fa::workspace_bytes(B, Hkv, Nk, d, in_dtype);
+  if (need / (128ull * (uint64_t)d) > (uint64_t)INT32_MAX || need > (uint64_t)SIZE_MAX)
+    return FA_ERR_SHAPE;
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, (size_t)need, (hipStream_t)stream) != hipSuccess || !ws)
+    return FA_ERR_ALLOC;
+  st = fa::launch_vt_pack(v, ws, B, Hkv, Nk, d, cu_seqlens_k, in_dtype, stream);
+  if (st == FA_OK) {
+    fa::LaunchArgs a{q, k, v, o, lse, ws, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, Nq, Nk,
+                     d, causal, scale, in_dtype, out_dtype};
+    a.block_mask = block_mask;
+    a.mask_batches = mask_batches;
+    a.mask_heads = mask_heads;
+    st = fa::launch_fwd(a, stream);
+  }
+  if (hipFreeAsync(ws, (hipStream_t)stream) != hipSuccess && st == FA_OK) st = FA_ERR_LAUNCH;
+  return st;
+}
+
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int in_dtype) {
   if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || (d != 64 && d != 128) ||
       (in_dtype != FA_F16 && in_dtype != FA_BF16))

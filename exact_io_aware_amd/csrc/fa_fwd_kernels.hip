@@ -66,7 +66,20 @@ struct FwdParams {
   float* o_part; float* lse_part;
   long long q_bs, q_hs, q_rs;    // element strides of q (and o): batch, head, row
   long long kv_bs, kv_hs, kv_rs; // element strides of k and v
+  // Block-sparse: uint8 mask over 64 x 64 (query row, key) blocks; entry
+  // (b, h, i, j) at mask_bs * b + mask_hs * h + mask_nkb * i + j (a stride
+  // is 0 where one mask serves every sequence or head).
+  const uint8_t* block_mask;
+  long long mask_bs, mask_hs;
+  int mask_nkb;
 };
+
+// LDS list of a block-sparse workgroup's key tiles (entry: tile index in
+// the low 16 bits, one bit per wave that needs the tile above them) and
+// per-wave counts for building it; a placeholder in the dense kernels.
+template <bool SPARSE> struct SparseTiles { int e[kMaxSparseTiles]; int cnt[8]; };
+template <> struct SparseTiles<false> { int e[1]; int cnt[1]; };
+static_assert(kMaxSparseTiles <= 0xffff, "tile index in 16 bits");
 
 // ---------------------------------------------------------------------------
 // V^T packing: for every (sequence, K/V head, 64-key tile), write the tile
@@ -132,7 +145,11 @@ __global__ __launch_bounds__(256) void fa_vt_pack(VtParams p) {
 // Step i of a wave masks block i if needed, issues the MFMAs of block i+1's
 // scores, forms block i's probabilities (independent work, so the matrix
 // cores and the vector ALUs overlap), then accumulates P.V of block i.
-template <typename T, int D, bool CAUSAL, bool VARLEN, bool OUT_F32>
+//
+// SPARSE: a block mask removes whole 64 x 64 blocks of scores.  The
+// workgroup streams only the key tiles that some wave's mask row admits, in
+// key order; a wave whose own row does not admit a tile forms P = 0 for it.
+template <typename T, int D, bool CAUSAL, bool VARLEN, bool OUT_F32, bool SPARSE>
 __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(FwdParams p) {
   using vec8 = typename Ops<T>::vec8;
   constexpr int NW = waves_per_wg(FA_BF16);        // waves per workgroup
@@ -154,6 +171,8 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
   __shared__ __attribute__((aligned(16))) char k_lds1[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char v_lds0[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char v_lds1[TILE_BYTES];
+  __shared__ SparseTiles<SPARSE> sp;
+  static_assert(!SPARSE || NW <= 8, "one list bit per wave");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -222,6 +241,74 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
   const char* kp = (const char*)((const T*)p.k + kvbase);
   const uint32_t kv_rs_bytes = (uint32_t)p.kv_rs * 2;
 
+  // Block-sparse: list the key tiles some wave needs, in key order.  Wave w
+  // (head hgrp*hp + w%hp, rows from r0) needs tile j if the mask row of its
+  // 64-row query block admits j and, with the causal mask, the tile starts
+  // before the wave's last visible key.  Each thread tests one tile; a
+  // ballot and the per-wave counts place the admitted tiles.
+  int n_list = 0;
+  if constexpr (SPARSE) {
+    const int ntk = (kv_end + BC - 1) / BC;
+    const uint8_t* mb = p.block_mask + p.mask_bs * b;
+    for (int base = 0; base < ntk; base += NT) {
+      const int j = base + tid;
+      uint32_t bits = 0;
+      if (j < ntk) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const int r0 = wg_row0 + (w / p.hp) * WR;
+          const int hw = hgrp * p.hp + (w % p.hp);
+          const int kend = CAUSAL ? min(min(r0 + WR, len) + off, len_k) : len_k;
+          if (r0 < len && j * BC < kend &&
+              mb[p.mask_hs * hw + (long long)(r0 / kSparseBlock) * p.mask_nkb + j] != 0)
+            bits |= 1u << w;
+        }
+      }
+      const uint64_t bal = __ballot(bits != 0);
+      if (lane == 0) sp.cnt[wave] = (int)__popcll(bal);
+      __syncthreads();
+      int before = 0, total = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int c = sp.cnt[w];
+        before += w < wave ? c : 0;
+        total += c;
+      }
+      if (bits != 0)
+        sp.e[n_list + before + (int)__popcll(bal & ((1ull << lane) - 1ull))] =
+            j | (int)(bits << 16);
+      n_list += total;
+      __syncthreads();
+    }
+    n_list = __builtin_amdgcn_readfirstlane(n_list);
+  }
+  // Key tile streamed at position rel (sparse: past the list, a tile past
+  // every sequence end, which reads zeros).
+  auto tile_at = [&](int rel) __attribute__((always_inline)) -> int {
+    if constexpr (SPARSE)
+      return rel < n_list ? (__builtin_amdgcn_readfirstlane(sp.e[rel]) & 0xffff) : p.vt_ntiles;
+    else
+      return t_begin + rel;
+  };
+  // Key block i of the streamed sequence: its first key, and whether this
+  // wave softmaxes it (a block past the wave's keys or, sparse, outside its
+  // mask row gets P = 0).
+  auto blk = [&](int i, int& kb, bool& live) __attribute__((always_inline)) {
+    if constexpr (SPARSE) {
+      if (i < 2 * n_list) {
+        const int e = __builtin_amdgcn_readfirstlane(sp.e[i >> 1]);
+        kb = (e & 0xffff) * BC + 32 * (i & 1);
+        live = ((e >> (16 + wave)) & 1) != 0 && kb < wave_kv_end;
+      } else {
+        kb = len_k;
+        live = false;
+      }
+    } else {
+      kb = (blk0 + i) * 32;
+      live = blk0 + i < wave_blk_end;
+    }
+  };
+
   // a3: tile loads go straight from memory into LDS (buffer_load ... lds):
   // lane L of wave w in load i fills 16-byte LDS chunk position
   // q = NT*i + 64*w + L of the tile, i.e. row q / CPR, position q % CPR,
@@ -237,7 +324,7 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
     voff[i] = vr * 128 + ((vc ^ vt_swz(vr)) << 4);
   }
   auto gload = [&](int tile, char* dst_base) __attribute__((always_inline)) {
-    const int kb = (t_begin + tile) * BC;
+    const int kb = tile_at(tile) * BC;
     // readfirstlane keeps the clamp (a VALU med3) in a scalar register: the
     // resource of a buffer load must be wave-uniform.
     const int rows = __builtin_amdgcn_readfirstlane(max(0, min(len_k - kb, BC)));
@@ -249,7 +336,7 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
   const char* vtp = (const char*)p.vt + (long long)(b * p.Hkv + kvh) * p.vt_ntiles * TILE_BYTES;
   auto gload_vt = [&](int tile_rel, char* dst_base) __attribute__((always_inline)) {
     // A V^T tile is contiguous; tiles past the sequence end read zeros.
-    const int tile = t_begin + tile_rel;
+    const int tile = tile_at(tile_rel);
     const int live_tile = __builtin_amdgcn_readfirstlane(tile * BC < len_k ? 1 : 0);
     const rsrc_t r = make_rsrc(vtp + (long long)min(tile, p.vt_ntiles) * TILE_BYTES,
                                live_tile ? (uint32_t)TILE_BYTES : 0u);
@@ -317,10 +404,9 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
       for (int qb = 0; qb < QB; ++qb) s[qb] = Ops<T>::mfma(kf[dc], qf[qb][dc], s[qb]);
   };
 
-  // a5: masks of block i (keys 32i .. 32i+31), only where it crosses the
+  // a5: masks of the 32-key block from key kb, only where it crosses the
   // diagonal or the end of the sequence.
-  auto mask = [&](int i, f32x16 (&s)[QB]) __attribute__((always_inline)) {
-    const int kb = (blk0 + i) * 32;
+  auto mask = [&](int kb, f32x16 (&s)[QB]) __attribute__((always_inline)) {
     if ((CAUSAL && kb + 31 > row0 + off) || (kb + 32 > len_k)) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
@@ -414,8 +500,10 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
                   const uint32_t (&pk_prev)[QB][8], const char* ks_nxt, const char* vs_prev,
                   int hb_prev)
       __attribute__((always_inline)) {
-    const bool live = blk0 + st < wave_blk_end;
-    mask(st, s_cur);
+    int kb;
+    bool live;
+    blk(st, kb, live);
+    mask(kb, s_cur);
     float lsum[QB];
     qk(ks_nxt, s_nxt);
     form_p(s_cur, pk_cur, lsum, live);
@@ -447,9 +535,12 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
   qk(k_lds0, sA);
   {                                  // step 0: no P.V yet
     float lsum[QB];
-    mask(0, sA);
+    int kb0;
+    bool live0;
+    blk(0, kb0, live0);
+    mask(kb0, sA);
     qk(k_lds0 + HALF, sB);
-    form_p(sA, pkA, lsum, blk0 < wave_blk_end);
+    form_p(sA, pkA, lsum, live0);
     settle(sA, pkA, lsum);
   }
   // Barrier B_t follows step 2t: all of K_t and V_{t-1} have been read, so
@@ -464,7 +555,7 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
   // Steps 1 .. nblk (the last one drains P.V), four per iteration so that
   // every buffer is a fixed object: K_t sits in k_lds[t % 2], V_t in
   // v_lds[t % 2]; step s reads K of block s+1 and V of block s-1.
-  const int last_step = max(0, (kv_stop + 31) / 32 - blk0);
+  const int last_step = SPARSE ? 2 * n_list : max(0, (kv_stop + 31) / 32 - blk0);
   for (int u = 0; 4 * u + 1 <= last_step; ++u) {
     const int s1 = 4 * u + 1;
     step(s1, sB, sA, pkB, pkA, k_lds1, v_lds0, 0);
@@ -773,7 +864,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_f32(FwdParams p) {
 typedef void (*KernelFn)(FwdParams);
 
 struct Variant {
-  int in_dtype, d, causal, varlen, out_dtype;
+  int in_dtype, d, causal, varlen, out_dtype, sparse;
   KernelFn fn;
   const char* name;
 };
@@ -785,30 +876,36 @@ struct Variant {
 #define FA_SFX_O_0 ""
 #define FA_SFX_O_1 "_of32"
 #define FA_CAT(a, b) a##b
-#define FA_V16(T, TN, DT, D, C, VL, OF)                                          \
-  {DT, D, C, VL, (OF) ? FA_F32 : DT, fa_fwd_mfma<T, D, (C != 0), (VL != 0), (OF != 0)>, \
+#define FA_SFX_S_0 ""
+#define FA_SFX_S_1 "_sparse"
+#define FA_V16(T, TN, DT, D, C, VL, OF, SP)                                        \
+  {DT, D, C, VL, (OF) ? FA_F32 : DT, SP,                                           \
+   fa_fwd_mfma<T, D, (C != 0), (VL != 0), (OF != 0), (SP != 0)>,                   \
    "fa_fwd_mfma_" TN "_d" #D FA_CAT(FA_SFX_C_, C) FA_CAT(FA_SFX_V_, VL)           \
-       FA_CAT(FA_SFX_O_, OF)}
-#define FA_V16_ALL(T, TN, DT, D)                                                  \
-  FA_V16(T, TN, DT, D, 0, 0, 0), FA_V16(T, TN, DT, D, 0, 0, 1),                    \
-  FA_V16(T, TN, DT, D, 0, 1, 0), FA_V16(T, TN, DT, D, 0, 1, 1),                    \
-  FA_V16(T, TN, DT, D, 1, 0, 0), FA_V16(T, TN, DT, D, 1, 0, 1),                    \
-  FA_V16(T, TN, DT, D, 1, 1, 0), FA_V16(T, TN, DT, D, 1, 1, 1)
+       FA_CAT(FA_SFX_O_, OF) FA_CAT(FA_SFX_S_, SP)}
+#define FA_V16_ALL(T, TN, DT, D, SP)                                              \
+  FA_V16(T, TN, DT, D, 0, 0, 0, SP), FA_V16(T, TN, DT, D, 0, 0, 1, SP),            \
+  FA_V16(T, TN, DT, D, 0, 1, 0, SP), FA_V16(T, TN, DT, D, 0, 1, 1, SP),            \
+  FA_V16(T, TN, DT, D, 1, 0, 0, SP), FA_V16(T, TN, DT, D, 1, 0, 1, SP),            \
+  FA_V16(T, TN, DT, D, 1, 1, 0, SP), FA_V16(T, TN, DT, D, 1, 1, 1, SP)
 #define FA_V32(D, C, VL)                                                           \
-  {FA_F32, D, C, VL, FA_F32, fa_fwd_f32<D, (C != 0), (VL != 0)>,                   \
+  {FA_F32, D, C, VL, FA_F32, 0, fa_fwd_f32<D, (C != 0), (VL != 0)>,                \
    "fa_fwd_f32_d" #D FA_CAT(FA_SFX_C_, C) FA_CAT(FA_SFX_V_, VL)}
 
 const Variant kVariants[] = {
-    FA_V16_ALL(__bf16, "bf16", FA_BF16, 64), FA_V16_ALL(__bf16, "bf16", FA_BF16, 128),
-    FA_V16_ALL(_Float16, "f16", FA_F16, 64), FA_V16_ALL(_Float16, "f16", FA_F16, 128),
+    FA_V16_ALL(__bf16, "bf16", FA_BF16, 64, 0), FA_V16_ALL(__bf16, "bf16", FA_BF16, 128, 0),
+    FA_V16_ALL(_Float16, "f16", FA_F16, 64, 0), FA_V16_ALL(_Float16, "f16", FA_F16, 128, 0),
+    FA_V16_ALL(__bf16, "bf16", FA_BF16, 64, 1), FA_V16_ALL(__bf16, "bf16", FA_BF16, 128, 1),
+    FA_V16_ALL(_Float16, "f16", FA_F16, 64, 1), FA_V16_ALL(_Float16, "f16", FA_F16, 128, 1),
     FA_V32(64, 0, 0), FA_V32(64, 0, 1), FA_V32(64, 1, 0), FA_V32(64, 1, 1),
     FA_V32(128, 0, 0), FA_V32(128, 0, 1), FA_V32(128, 1, 0), FA_V32(128, 1, 1),
 };
 
-const Variant* find_variant(int in_dtype, int d, int causal, int varlen, int out_dtype) {
+const Variant* find_variant(int in_dtype, int d, int causal, int varlen, int out_dtype,
+                            int sparse = 0) {
   for (const Variant& v : kVariants)
     if (v.in_dtype == in_dtype && v.d == d && v.causal == causal && v.varlen == varlen &&
-        v.out_dtype == out_dtype)
+        v.out_dtype == out_dtype && v.sparse == sparse)
       return &v;
   return nullptr;
 }
@@ -859,7 +956,9 @@ const char* kernel_name(int in_dtype, int d, int causal, int varlen, int out_dty
 
 int launch_fwd(const LaunchArgs& a, void* stream) {
   const bool varlen = a.cu_seqlens != nullptr;
-  const Variant* var = find_variant(a.in_dtype, a.d, a.causal, varlen, a.out_dtype);
+  const bool sparse = a.block_mask != nullptr;
+  if (sparse && a.in_dtype == FA_F32) return FA_ERR_DTYPE;
+  const Variant* var = find_variant(a.in_dtype, a.d, a.causal, varlen, a.out_dtype, sparse);
   if (!var) return FA_ERR_DTYPE;
   const Plan plan = make_plan(a.B, a.Hq, a.Hkv, a.N, a.d, a.in_dtype);
 
@@ -872,10 +971,17 @@ int launch_fwd(const LaunchArgs& a, void* stream) {
   p.xcd_remap = (a.in_dtype != FA_F32) && ((uint64_t)a.B * plan.n_hgroups) % 8 == 0;
   p.scale_log2 = a.scale * kLog2e;
   p.vt = a.vt; p.Hkv = a.Hkv; p.vt_ntiles = vt_tiles(a.Nk);
-  const int n_splits = (a.in_dtype != FA_F32 && a.n_splits > 1) ? a.n_splits : 1;
+  const int n_splits = (a.in_dtype != FA_F32 && !sparse && a.n_splits > 1) ? a.n_splits : 1;
   p.n_splits = n_splits;
   p.split_tiles = n_splits > 1 ? (p.vt_ntiles + n_splits - 1) / n_splits : p.vt_ntiles + 1;
   p.B = a.B; p.o_part = a.o_part; p.lse_part = a.lse_part;
+  p.block_mask = a.block_mask;
+  p.mask_nkb = (a.Nk + kSparseBlock - 1) / kSparseBlock;
+  {
+    const long long slab = (long long)((a.N + kSparseBlock - 1) / kSparseBlock) * p.mask_nkb;
+    p.mask_hs = a.mask_heads > 1 ? slab : 0;
+    p.mask_bs = a.mask_batches > 1 ? slab * a.mask_heads : 0;
+  }
   if (n_splits > 1) p.xcd_remap = 0;
   const long long d = a.d;
   if (varlen) {

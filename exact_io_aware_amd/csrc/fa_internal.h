@@ -17,6 +17,12 @@ constexpr int rows_per_wave(int in_dtype) { return in_dtype == FA_F32 ? 32 : 32;
 // each K/V tile in LDS), 4 for fp32 inputs.
 constexpr int waves_per_wg(int in_dtype) { return in_dtype == FA_F32 ? 4 : 8; }
 
+// Block-sparse attention: query rows and keys per block of a block mask,
+// and the most 64-key tiles one sequence may have (the attention kernel
+// keeps a list of them in LDS).
+constexpr int kSparseBlock = 64;
+constexpr int kMaxSparseTiles = 4096;
+
 // How the launch covers the work.  A workgroup is waves_per_wg() waves; each
 // wave owns rows_per_wave() query rows of one query head.  `hp` query heads that share
 // one K/V head are packed into a workgroup (GQA), so one K/V tile in LDS
@@ -78,6 +84,13 @@ int check_pack_args(const void* v, const void* vt, uint64_t vt_bytes, int B, int
 // Checks of the split-KV arguments (after check_packed_args): num_splits in
 // [1, 256], the partial buffer (when num_splits > 1) present, 16-byte
 // aligned, large enough and clear of o and lse, and the grid in range.
+// Block mask arguments of fa_fwd_sparse*: pointer, broadcast counts, the
+// key-tile limit, 16-bit inputs, and no overlap with o or lse.
+int check_sparse_args(const void* block_mask, int mask_batches, int mask_heads, const void* o,
+                      const float* lse, int B, int Hq, int Nq, int Nk, int d, int in_dtype,
+                      int out_dtype, bool varlen);
+uint64_t sparse_mask_bytes(int mask_batches, int mask_heads, int Nq, int Nk);
+
 int check_split_args(const void* part, uint64_t part_bytes, const void* o, const float* lse,
                      int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits,
                      int in_dtype, int out_dtype, bool varlen);
@@ -95,6 +108,10 @@ struct LaunchArgs {
   int n_splits;
   float* o_part;
   float* lse_part;
+  // Block-sparse (16-bit inputs): uint8 mask [mask_batches][mask_heads]
+  // [ceil(N/64)][ceil(Nk/64)], or nullptr.
+  const uint8_t* block_mask;
+  int mask_batches, mask_heads;
 };
 
 // Bytes of the split-KV partials: n_splits x B x Hq x Nq rows of d fp32

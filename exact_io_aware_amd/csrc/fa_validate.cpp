@@ -116,6 +116,35 @@ int check_split_args(const void* part, uint64_t part_bytes, const void* o, const
   return FA_OK;
 }
 
+uint64_t sparse_mask_bytes(int mask_batches, int mask_heads, int Nq, int Nk) {
+  const uint64_t nqb = ((uint64_t)Nq + kSparseBlock - 1) / kSparseBlock;
+  const uint64_t nkb = ((uint64_t)Nk + kSparseBlock - 1) / kSparseBlock;
+  uint64_t n;
+  if (!mul_ok((uint64_t)mask_batches * (uint64_t)mask_heads, nqb * nkb, &n)) return UINT64_MAX;
+  return n;
+}
+
+int check_sparse_args(const void* block_mask, int mask_batches, int mask_heads, const void* o,
+                      const float* lse, int B, int Hq, int Nq, int Nk, int d, int in_dtype,
+                      int out_dtype, bool varlen) {
+  if (!block_mask) return FA_ERR_NULL;
+  if (in_dtype == FA_F32) return FA_ERR_DTYPE;
+  if ((mask_batches != 1 && mask_batches != B) || (mask_heads != 1 && mask_heads != Hq))
+    return FA_ERR_SHAPE;
+  if (((uint64_t)Nk + kSparseBlock - 1) / kSparseBlock > (uint64_t)kMaxSparseTiles)
+    return FA_ERR_SHAPE;
+  const uint64_t mb = sparse_mask_bytes(mask_batches, mask_heads, Nq, Nk);
+  if (mb > (uint64_t)INT64_MAX / 2) return FA_ERR_SHAPE;
+  // The mask is an input: it must not overlap the outputs.  For the packed
+  // layout o's true extent lives on the device (only the start is checked).
+  uint64_t rows = (uint64_t)B * (uint64_t)Hq * (uint64_t)Nq;
+  const uint64_t ob = varlen ? 1 : rows * (uint64_t)d * elem_size(out_dtype);
+  if (block_mask == o || overlap((uintptr_t)block_mask, mb, (uintptr_t)o, ob) ||
+      overlap((uintptr_t)block_mask, mb, (uintptr_t)lse, rows * 4))
+    return FA_ERR_ALIAS;
+  return FA_OK;
+}
+
 int check_bwd_args(const BwdArgs& a, uint64_t ws_bytes) {
   if (!a.q || !a.k || !a.v || !a.o || !a.dout || !a.lse || !a.dq || !a.dk || !a.dv ||
       !a.workspace)

@@ -71,7 +71,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor], *, causal: 
         stream: Optional[torch.cuda.Stream] = None, vt: Optional[torch.Tensor] = None,
         library_workspace: bool = False, cu_seqlens_k: Optional[torch.Tensor] = None,
         max_seqlen_k: Optional[int] = None, num_splits: Optional[int] = None,
-        split_workspace: Optional[torch.Tensor] = None):
+        split_workspace: Optional[torch.Tensor] = None,
+        block_mask: Optional[torch.Tensor] = None):
     """Exact attention forward on the GPU: returns ``(o, lse)``.
 
     Fixed length: q ``[B, Hq, Nq, d]``, k/v ``[B, Hkv, Nk, d]``.
@@ -99,6 +100,12 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor], *, causal: 
     fa_num_splits, which splits only decode-like shapes (at most 64 query
     rows per sequence) that would not fill the GPU.  ``split_workspace``
     (uint8, fa_split_workspace_bytes) may be passed to avoid an allocation.
+
+    Block-sparse (16-bit): ``block_mask`` is a contiguous uint8 device
+    tensor ``[1 or B, 1 or Hq, ceil(Nq/64), ceil(Nk/64)]``; a nonzero entry
+    (b, h, i, j) admits query rows [64i, 64i+64) of sequence b, head h
+    against keys [64j, 64j+64) (fa_fwd_sparse_packed, or fa_fwd_sparse with
+    ``library_workspace``).  Rows that see no key get O = 0, L = -inf.
     """
     if v is None and vt is None:
         raise ValueError("v is needed unless a packed vt is given")
@@ -166,6 +173,35 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor], *, causal: 
     if packed and (vt.dtype != torch.uint8 or not vt.is_cuda or not vt.is_contiguous()):
         raise ValueError("vt must be the contiguous uint8 device tensor pack_v returns")
     dt, odt = _DT[q.dtype], _DT[out_dtype]
+    if block_mask is not None:
+        if q.dtype == torch.float32:
+            raise ValueError("block_mask needs float16 or bfloat16 inputs")
+        nqb, nkb = -(-N // 64), -(-Nk // 64)
+        if (block_mask.dtype != torch.uint8 or not block_mask.is_cuda
+                or not block_mask.is_contiguous() or block_mask.dim() != 4
+                or block_mask.shape[0] not in (1, B) or block_mask.shape[1] not in (1, Hq)
+                or tuple(block_mask.shape[2:]) != (nqb, nkb)):
+            raise ValueError(f"block_mask must be a contiguous uint8 device tensor "
+                             f"[1 or {B}, 1 or {Hq}, {nqb}, {nkb}]")
+        if num_splits not in (None, 1):
+            raise ValueError("block-sparse attention does not split over keys")
+        mb, mh = int(block_mask.shape[0]), int(block_mask.shape[1])
+        with torch.cuda.device(q.device):
+            if packed:
+                name = "fa_fwd_sparse_packed"
+                status = _lib.fwd_sparse_packed_raw(
+                    q.data_ptr(), k.data_ptr(), vt.data_ptr(), vt.numel(), out.data_ptr(),
+                    lse.data_ptr(), B, Hq, Hkv, N, Nk, d, causal, float(scale), cu_ptr, cuk_ptr,
+                    block_mask.data_ptr(), mb, mh, st, dt, odt)
+            else:
+                name = "fa_fwd_sparse"
+                status = _lib.fwd_sparse_raw(
+                    q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B,
+                    Hq, Hkv, N, Nk, d, causal, float(scale), cu_ptr, cuk_ptr,
+                    block_mask.data_ptr(), mb, mh, st, dt, odt)
+        if status != _lib.FA_OK:
+            raise RuntimeError(f"{name} failed ({status}): {_lib.status_string(status)}")
+        return out, lse
     n_splits = 1
     if packed:
         with torch.cuda.device(q.device):
@@ -210,11 +246,39 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor], *, causal: 
     return out, lse
 
 
+def _block_pairs(bm, nq: int, nk: int, causal: bool) -> int:
+    """Visible (query, key) pairs of one head of one sequence under the
+    block mask ``bm`` [row blocks, key blocks] of 64 x 64 blocks."""
+    import numpy as np
+    nqb, nkb = -(-nq // 64), -(-nk // 64)
+    m = (np.asarray(bm)[:nqb, :nkb] != 0).astype(np.int64)
+    r = np.arange(nq)
+    span = np.minimum(nk, np.maximum(0, r + (nk - nq) + 1)) if causal else np.full(nq, nk)
+    # keys of block j visible to row r: clip(span_r - 64 j, 0, min(64, nk - 64 j))
+    j0 = 64 * np.arange(nkb)
+    width = np.minimum(64, nk - j0)
+    per = np.clip(span[:, None] - j0[None, :], 0, width[None, :])      # [nq, nkb]
+    return int((per * m[r // 64]).sum())
+
+
 def flops(Hq: int, d: int, lengths: Sequence[int], causal: bool,
-          lengths_k: Optional[Sequence[int]] = None) -> float:
+          lengths_k: Optional[Sequence[int]] = None, block_mask=None) -> float:
     """Algorithmic FLOP of one forward: 4*d*Hq per visible (query, key) pair.
     ``lengths_k`` gives per-sequence key counts when they differ from the
-    query counts (the queries are then the last tokens of each sequence)."""
+    query counts (the queries are then the last tokens of each sequence).
+    ``block_mask`` (numpy, [1 or B, 1 or Hq, row blocks, key blocks]) counts
+    only the pairs its admitted 64 x 64 blocks hold."""
+    if block_mask is not None:
+        bm = block_mask
+        ks = lengths if lengths_k is None else lengths_k
+        pairs = 0
+        for b, (nq, nk) in enumerate(zip(lengths, ks)):
+            mb = bm[b if bm.shape[0] > 1 else 0]
+            if mb.shape[0] == 1:
+                pairs += Hq * _block_pairs(mb[0], int(nq), int(nk), causal)
+            else:
+                pairs += sum(_block_pairs(mb[h], int(nq), int(nk), causal) for h in range(Hq))
+        return 4.0 * d * pairs
     if lengths_k is None:
         pairs = sum(n * (n + 1) // 2 if causal else n * n for n in lengths)
     else:

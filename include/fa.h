@@ -215,6 +215,41 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            int causal, float scale, const int* cu_seqlens, void* workspace,
            size_t workspace_bytes, void* stream, int in_dtype, int o_dtype, int grad_dtype);
 
+/* Block-sparse attention.  The Kotaemon page names block-sparse attention
+ * only as a direction of the method (its closing outlook), with no layout;
+ * the reading here: a 0/1 mask over blocks of 64 query rows x 64 keys
+ * removes whole blocks of scores (set to -inf, as the causal mask removes
+ * single scores); everything else is fa_fwd_kv.
+ *
+ * block_mask: DEVICE uint8 array [mask_batches][mask_heads][ceil(Nq/64)]
+ * [ceil(Nk/64)], C order.  Entry (b, h, i, j) != 0 admits query rows
+ * [64i, 64i+64) of sequence b, query head h against its keys [64j, 64j+64)
+ * (row and key indices within the sequence, so for the packed layout each
+ * sequence uses the top-left corner of its slab).  mask_batches is 1 (one
+ * mask for every sequence) or B; mask_heads is 1 or Hq.  With causal = 1
+ * the causal mask (bottom-right, as fa_fwd_kv) applies as well.  Rows that
+ * see no key get O = 0 and L = -inf.  The mask must not overlap o or lse;
+ * its size is not checked (the caller allocates mask_batches * mask_heads *
+ * ceil(Nq/64) * ceil(Nk/64) bytes).
+ *
+ * 16-bit inputs only (FA_ERR_DTYPE for fp32); ceil(Nk/64) <= 4096 (keys per
+ * sequence <= 262144, else FA_ERR_SHAPE); never split over keys.
+ * fa_fwd_sparse allocates its V^T workspace as fa_fwd does;
+ * fa_fwd_sparse_packed reads V packed by fa_pack_v (called with N = Nk and
+ * cu_seqlens = cu_seqlens_k) and allocates nothing.  Other arguments and
+ * errors as fa_fwd_kv. */
+int fa_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k,
+                  const unsigned char* block_mask, int mask_batches, int mask_heads,
+                  void* stream, int in_dtype, int out_dtype);
+int fa_fwd_sparse_packed(const void* q, const void* k, const void* vt, size_t vt_bytes,
+                         void* o, float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                         int causal, float scale, const int* cu_seqlens_q,
+                         const int* cu_seqlens_k, const unsigned char* block_mask,
+                         int mask_batches, int mask_heads, void* stream, int in_dtype,
+                         int out_dtype);
+
 /* The argument checks of fa_fwd alone: returns what fa_fwd would return
  * before touching the device (FA_OK if it would go on to launch).  Makes no
  * HIP call, so it is usable without a GPU. */

@@ -93,3 +93,23 @@ def grad_bar(dtype: str) -> float:
     4u of it is the bar.
     """
     return 4.0 * {"bf16": 2.0 ** -8, "fp16": 2.0 ** -11}[dtype]
+
+
+def compare_qk(w, O, L, Oref, Lref, out_dtype="fp32"):
+    """Element-wise bars; rows that see no key must give O = 0, L = -inf;
+    L rows past a packed sequence's query count stay untouched (NaN)."""
+    if w["cu_seqlens"] is not None:
+        for b, n in enumerate(np.diff(w["cu_seqlens"])):
+            assert np.isnan(L[b, :, n:]).all(), "padded lse rows must stay untouched"
+            L[b, :, n:] = Lref[b, :, n:] = 0.0
+    none = np.isneginf(Lref)
+    assert np.array_equal(np.isneginf(L), none), "rows without keys"
+    assert np.isfinite(O).all()
+    eo = np.abs(O - Oref)
+    bar = o_bar(w["dtype"], out_dtype, Oref)
+    assert (eo <= bar).all(), f"O error {eo.max():.3e}"
+    el = np.abs(np.where(none, 0.0, L - Lref))
+    assert el.max() <= L_TOL, f"L error {el.max():.3e}"
+    if w["dtype"] == "fp32":
+        assert eo.max() <= FP32_STRICT and el.max() <= FP32_STRICT
+    return float(eo.max()), float(el.max())

@@ -276,3 +276,62 @@ def test_bwd_workspace_bytes():
 ])
 def test_bwd_rejects_before_any_device_call(kw, code):
     assert bwd(**kw) == S[code]
+
+
+def sparse(packed_vt=True, **kw):
+    a = dict(BASE, Nk=64, vt=VT, vt_bytes=WS, mask=0x900000, mb=1, mh=1)
+    a.update(kw)
+    if packed_vt:
+        return _lib.fwd_sparse_packed_raw(a["q"], a["k"], a["vt"], a["vt_bytes"], a["o"],
+                                          a["lse"], a["B"], a["Hq"], a["Hkv"], a["N"], a["Nk"],
+                                          a["d"], a["causal"], a["scale"], a["cu_seqlens"],
+                                          a.get("cu_k", a["cu_seqlens"]), a["mask"], a["mb"],
+                                          a["mh"], None, a["in_dtype"], a["out_dtype"])
+    return _lib.fwd_sparse_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"],
+                               a["Hkv"], a["N"], a["Nk"], a["d"], a["causal"], a["scale"],
+                               a["cu_seqlens"], a.get("cu_k", a["cu_seqlens"]), a["mask"],
+                               a["mb"], a["mh"], None, a["in_dtype"], a["out_dtype"])
+
+
+@pytest.mark.parametrize("packed_vt", [True, False])
+@pytest.mark.parametrize("kw,code", [
+    ({"mask": None}, "FA_ERR_NULL"),
+    ({"in_dtype": fa.FA_F32}, "FA_ERR_DTYPE"),
+    ({"mb": 3}, "FA_ERR_SHAPE"), ({"mh": 2}, "FA_ERR_SHAPE"), ({"mh": 0}, "FA_ERR_SHAPE"),
+    ({"Nk": 64 * 4096 + 1, "vt_bytes": 1 << 40, "k": 1 << 40, "v": 2 << 40, "vt": 3 << 40},
+     "FA_ERR_SHAPE"),                                                 # more than 4096 key tiles
+    ({"mask": 0x400000}, "FA_ERR_ALIAS"),                             # the mask is o
+    ({"mask": 0x500000 + 64}, "FA_ERR_ALIAS"),                        # inside lse
+    ({"d": 96}, "FA_ERR_HEADDIM"),
+])
+def test_sparse_rejects_before_any_device_call(packed_vt, kw, code):
+    if kw.get("in_dtype") == fa.FA_F32 and packed_vt:
+        code = "FA_ERR_DTYPE"            # the packed path rejects fp32 first
+    assert sparse(packed_vt, **kw) == S[code]
+
+
+def test_sparse_valid_arguments_reach_the_device_check():
+    # Valid arguments pass every check; without a gfx950 device the entry
+    # point stops at the device query.
+    for packed_vt in (True, False):
+        for mb, mh in ((1, 1), (2, 8), (1, 8), (2, 1)):
+            st = sparse(packed_vt, mb=mb, mh=mh)
+            assert st in (S["FA_ERR_DEVICE"], S["FA_OK"]) or st == S["FA_ERR_ALLOC"], st
+
+
+def test_sparse_flops_count_admitted_pairs():
+    """The bench's FLOP count under a block mask equals the oracle's pair
+    count (brute force over the admitted blocks)."""
+    import numpy as np
+
+    import oracle
+    r = np.random.default_rng(5)
+    for nq, nk in ((300, 300), (100, 333), (130, 64)):
+        for causal in (False, True):
+            bm = (r.random((2, 3, -(-nq // 64), -(-nk // 64))) < 0.5).astype(np.uint8)
+            want = sum(oracle.sparse_pair_count(bm[b, h], nq, nk, causal)
+                       for b in range(2) for h in range(3))
+            assert fa.flops(3, 16, [nq, nq], causal, [nk, nk], block_mask=bm) == 4.0 * 16 * want
+            one = bm[:1, :1]
+            want1 = 6 * oracle.sparse_pair_count(one[0, 0], nq, nk, causal)
+            assert fa.flops(3, 16, [nq, nq], causal, [nk, nk], block_mask=one) == 4.0 * 16 * want1

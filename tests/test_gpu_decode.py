@@ -9,7 +9,7 @@ import pytest
 import oracle
 import workloads
 from tests import gpu_util as G
-from tests.test_gpu_prefill import _compare, _make, _oracle
+from tests.test_gpu_prefill import _make, _oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -51,7 +51,7 @@ def test_decode_parity_auto_splits(i):
     for od in ("fp32", w["dtype"]):
         G.say(f"decode case {case} out={od}")
         O, L = _run(w, out_dtype=G.torch_dtype(od))
-        G.say(f"  errors {_compare(w, O, L, Oref, Lref, od)}")
+        G.say(f"  errors {G.compare_qk(w, O, L, Oref, Lref, od)}")
 
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 16, 40])
@@ -62,7 +62,7 @@ def test_decode_explicit_splits(splits):
     Oref, Lref = _oracle(w)
     G.say(f"decode with {splits} splits")
     O, L = _run(w, num_splits=splits)
-    G.say(f"  errors {_compare(w, O, L, Oref, Lref)}")
+    G.say(f"  errors {G.compare_qk(w, O, L, Oref, Lref)}")
 
 
 def test_splits_on_prefill_shape():
@@ -72,7 +72,7 @@ def test_splits_on_prefill_shape():
     for splits in (1, 4):
         G.say(f"prefill shape with {splits} splits")
         O, L = _run(w, num_splits=splits)
-        G.say(f"  errors {_compare(w, O, L, Oref, Lref)}")
+        G.say(f"  errors {G.compare_qk(w, O, L, Oref, Lref)}")
 
 
 def test_num_splits_heuristic():
@@ -93,4 +93,4 @@ def test_decode_workload_sampled():
     Oref, Lref = oracle.attention_qk(q[sel], k[sel], v[sel], causal=True, scale=w["scale"],
                                      workers=min(16, oracle.default_workers()))
     w1 = dict(w, cu_seqlens=None)
-    G.say(f"  errors {_compare(w1, O[sel], L[sel], Oref, Lref)}")
+    G.say(f"  errors {G.compare_qk(w1, O[sel], L[sel], Oref, Lref)}")

@@ -64,26 +64,6 @@ def _oracle(w):
                                cu_seqlens_q=w["cu_seqlens"], cu_seqlens_k=w["cu_seqlens_k"])
 
 
-def _compare(w, O, L, Oref, Lref, out_dtype="fp32"):
-    """Element-wise bars; rows that see no key must give O = 0, L = -inf;
-    L rows past a packed sequence's query count stay untouched (NaN)."""
-    if w["cu_seqlens"] is not None:
-        for b, n in enumerate(np.diff(w["cu_seqlens"])):
-            assert np.isnan(L[b, :, n:]).all(), "padded lse rows must stay untouched"
-            L[b, :, n:] = Lref[b, :, n:] = 0.0
-    none = np.isneginf(Lref)
-    assert np.array_equal(np.isneginf(L), none), "rows without keys"
-    assert np.isfinite(O).all()
-    eo = np.abs(O - Oref)
-    bar = G.o_bar(w["dtype"], out_dtype, Oref)
-    assert (eo <= bar).all(), f"O error {eo.max():.3e}"
-    el = np.abs(np.where(none, 0.0, L - Lref))
-    assert el.max() <= G.L_TOL, f"L error {el.max():.3e}"
-    if w["dtype"] == "fp32":
-        assert eo.max() <= G.FP32_STRICT and el.max() <= G.FP32_STRICT
-    return float(eo.max()), float(el.max())
-
-
 @pytest.mark.parametrize("i", range(len(CASES)),
                          ids=lambda i: "-".join(map(str, CASES[i][:7])).replace(" ", ""))
 def test_prefill_parity(i):
@@ -94,7 +74,7 @@ def test_prefill_parity(i):
     for od in outs:
         G.say(f"prefill case {case} out={od}")
         O, L = _run(w, out_dtype=G.torch_dtype(od))
-        G.say(f"  errors {_compare(w, O, L, Oref, Lref, od)}")
+        G.say(f"  errors {G.compare_qk(w, O, L, Oref, Lref, od)}")
 
 
 def test_prefill_library_workspace_matches_packed():
@@ -138,4 +118,4 @@ def test_prefill_workload_first_sequence():
     Oref, Lref = oracle.attention_qk(q[:1], k[:1], v[:1], causal=True, scale=w["scale"],
                                      workers=min(16, oracle.default_workers()))
     w1 = dict(w, cu_seqlens=None)
-    G.say(f"  errors {_compare(w1, O[:1], L[:1], Oref, Lref)}")
+    G.say(f"  errors {G.compare_qk(w1, O[:1], L[:1], Oref, Lref)}")
