@@ -282,27 +282,29 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
     }
     n_list = __builtin_amdgcn_readfirstlane(n_list);
   }
-  // Key tile streamed at position rel (sparse: past the list, a tile past
-  // every sequence end, which reads zeros).
-  auto tile_at = [&](int rel) __attribute__((always_inline)) -> int {
-    if constexpr (SPARSE)
-      return rel < n_list ? (__builtin_amdgcn_readfirstlane(sp.e[rel]) & 0xffff) : p.vt_ntiles;
-    else
-      return t_begin + rel;
-  };
-  // Key block i of the streamed sequence: its first key, and whether this
-  // wave softmaxes it (a block past the wave's keys or, sparse, outside its
-  // mask row gets P = 0).
-  auto blk = [&](int i, int& kb, bool& live) __attribute__((always_inline)) {
+  // The tile streamed at position pos, as a list entry: dense, the tile
+  // index; sparse, the list entry (past the list, a tile past every
+  // sequence end with no wave bits: it reads zeros and is never softmaxed).
+  // The sparse loop reads the entries it needs once per iteration, right
+  // after a barrier, when no other LDS read is waiting.
+  auto entry = [&](int pos) __attribute__((always_inline)) -> int {
     if constexpr (SPARSE) {
-      if (i < 2 * n_list) {
-        const int e = __builtin_amdgcn_readfirstlane(sp.e[i >> 1]);
-        kb = (e & 0xffff) * BC + 32 * (i & 1);
-        live = ((e >> (16 + wave)) & 1) != 0 && kb < wave_kv_end;
-      } else {
-        kb = len_k;
-        live = false;
-      }
+      const int e = __builtin_amdgcn_readfirstlane(sp.e[min(pos, kMaxSparseTiles - 1)]);
+      return pos < n_list ? e : p.vt_ntiles;
+    } else {
+      return t_begin + pos;
+    }
+  };
+  auto tile_of = [&](int e) __attribute__((always_inline)) -> int {
+    return SPARSE ? (e & 0xffff) : e;
+  };
+  // Key block i of the streamed sequence (half i % 2 of the tile whose entry
+  // is e): its first key, and whether this wave softmaxes it (a block past
+  // the wave's keys or, sparse, outside its mask row gets P = 0).
+  auto blk = [&](int i, int e, int& kb, bool& live) __attribute__((always_inline)) {
+    if constexpr (SPARSE) {
+      kb = (e & 0xffff) * BC + 32 * (i & 1);
+      live = ((e >> (16 + wave)) & 1) != 0 && kb < wave_kv_end;
     } else {
       kb = (blk0 + i) * 32;
       live = blk0 + i < wave_blk_end;
@@ -323,8 +325,8 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
     const int vr = pch / 8, vc = pch % 8;       // V^T tile: 8 chunks per row
     voff[i] = vr * 128 + ((vc ^ vt_swz(vr)) << 4);
   }
-  auto gload = [&](int tile, char* dst_base) __attribute__((always_inline)) {
-    const int kb = tile_at(tile) * BC;
+  auto gload = [&](int e, char* dst_base) __attribute__((always_inline)) {
+    const int kb = tile_of(e) * BC;
     // readfirstlane keeps the clamp (a VALU med3) in a scalar register: the
     // resource of a buffer load must be wave-uniform.
     const int rows = __builtin_amdgcn_readfirstlane(max(0, min(len_k - kb, BC)));
@@ -334,9 +336,9 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
     for (int i = 0; i < LOADS; ++i) lds_load16(r, dst_base + (NT * i + 64 * wave) * 16, koff[i]);
   };
   const char* vtp = (const char*)p.vt + (long long)(b * p.Hkv + kvh) * p.vt_ntiles * TILE_BYTES;
-  auto gload_vt = [&](int tile_rel, char* dst_base) __attribute__((always_inline)) {
+  auto gload_vt = [&](int e, char* dst_base) __attribute__((always_inline)) {
     // A V^T tile is contiguous; tiles past the sequence end read zeros.
-    const int tile = tile_at(tile_rel);
+    const int tile = tile_of(e);
     const int live_tile = __builtin_amdgcn_readfirstlane(tile * BC < len_k ? 1 : 0);
     const rsrc_t r = make_rsrc(vtp + (long long)min(tile, p.vt_ntiles) * TILE_BYTES,
                                live_tile ? (uint32_t)TILE_BYTES : 0u);
@@ -345,9 +347,9 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
   };
 
   // Prologue loads: K_0, K_1 and V_0 (K runs ahead of V).
-  gload(0, k_lds0);
-  gload_vt(0, v_lds0);
-  gload(1, k_lds1);
+  gload(entry(0), k_lds0);
+  gload_vt(entry(0), v_lds0);
+  gload(entry(1), k_lds1);
 
   // a2: this wave's Q rows as MFMA B operands (query block qb, d-chunk dc,
   // 8 values per lane: Q[row0 + 32*qb + l32][16*dc + 8*hf .. +7]).  Rows past
@@ -496,13 +498,13 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
   // same straight-line code serves every step: past a wave's last block its
   // P is zero (and its scores, reads of loaded or zero-filled LDS, unused),
   // so the step after the last one just drains P.V.
-  auto step = [&](int st, f32x16 (&s_cur)[QB], f32x16 (&s_nxt)[QB], uint32_t (&pk_cur)[QB][8],
-                  const uint32_t (&pk_prev)[QB][8], const char* ks_nxt, const char* vs_prev,
-                  int hb_prev)
+  auto step = [&](int st, int e_st, f32x16 (&s_cur)[QB], f32x16 (&s_nxt)[QB],
+                  uint32_t (&pk_cur)[QB][8], const uint32_t (&pk_prev)[QB][8],
+                  const char* ks_nxt, const char* vs_prev, int hb_prev)
       __attribute__((always_inline)) {
     int kb;
     bool live;
-    blk(st, kb, live);
+    blk(st, e_st, kb, live);
     mask(kb, s_cur);
     float lsum[QB];
     qk(ks_nxt, s_nxt);
@@ -537,7 +539,7 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
     float lsum[QB];
     int kb0;
     bool live0;
-    blk(0, kb0, live0);
+    blk(0, entry(0), kb0, live0);
     mask(kb0, sA);
     qk(k_lds0 + HALF, sB);
     form_p(sA, pkA, lsum, live0);
@@ -549,8 +551,8 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
   // fetch nothing and write zeros.
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
-  gload(2, k_lds0);
-  gload_vt(1, v_lds1);
+  gload(entry(2), k_lds0);
+  gload_vt(entry(1), v_lds1);
 
   // Steps 1 .. nblk (the last one drains P.V), four per iteration so that
   // every buffer is a fixed object: K_t sits in k_lds[t % 2], V_t in
@@ -558,21 +560,26 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
   const int last_step = SPARSE ? 2 * n_list : max(0, (kv_stop + 31) / 32 - blk0);
   for (int u = 0; 4 * u + 1 <= last_step; ++u) {
     const int s1 = 4 * u + 1;
-    step(s1, sB, sA, pkB, pkA, k_lds1, v_lds0, 0);
+    // Steps s1 .. s1+3 softmax blocks of tiles 2u (second half), 2u+1 and
+    // 2u+2 (first half); this iteration loads K of tiles 2u+3, 2u+4 and V
+    // of tiles 2u+2, 2u+3.
+    const int e0 = entry(2 * u), e1 = entry(2 * u + 1), e2 = entry(2 * u + 2);
+    const int e3 = entry(2 * u + 3), e4 = entry(2 * u + 4);
+    step(s1, e0, sB, sA, pkB, pkA, k_lds1, v_lds0, 0);
     if (s1 + 1 > last_step) break;
-    step(s1 + 1, sA, sB, pkA, pkB, k_lds1 + HALF, v_lds0, 1);
+    step(s1 + 1, e1, sA, sB, pkA, pkB, k_lds1 + HALF, v_lds0, 1);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
-    gload(2 * u + 3, k_lds1);
-    gload_vt(2 * u + 2, v_lds0);
+    gload(e3, k_lds1);
+    gload_vt(e2, v_lds0);
     if (s1 + 2 > last_step) break;
-    step(s1 + 2, sB, sA, pkB, pkA, k_lds0, v_lds1, 0);
+    step(s1 + 2, e1, sB, sA, pkB, pkA, k_lds0, v_lds1, 0);
     if (s1 + 3 > last_step) break;
-    step(s1 + 3, sA, sB, pkA, pkB, k_lds0 + HALF, v_lds1, 1);
+    step(s1 + 3, e2, sA, sB, pkA, pkB, k_lds0 + HALF, v_lds1, 1);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
-    gload(2 * u + 4, k_lds0);
-    gload_vt(2 * u + 3, v_lds1);
+    gload(e4, k_lds0);
+    gload_vt(e3, v_lds1);
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // no load left in flight
   // Every wave has finished reading K/V from LDS: the tile buffers become
