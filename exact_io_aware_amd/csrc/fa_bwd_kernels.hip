@@ -45,6 +45,7 @@ struct BwdParams {
   const void* q; const void* k; const void* v; const void* o; const void* dout;
   const float* lse;          // [B][Hq][N], natural log
   float* delta;              // [B][Hq][N], rowsum(dO * O)
+  float* lse2;               // [B][Hq][N], lse * log2(e)
   const void* qt; const void* dot; const void* kt;   // packed transposes
   void* dq; void* dk; void* dv;
   const int* cu_seqlens;
@@ -57,7 +58,8 @@ struct BwdParams {
 };
 
 // ---------------------------------------------------------------------------
-// D_r = sum_j dO_rj * O_rj (fp32).  32 lanes per row, D/32 columns each.
+// D_r = sum_j dO_rj * O_rj (fp32), and L_r * log2(e) (the exponent offset
+// of the base-2 exponentials).  32 lanes per row, D/32 columns each.
 template <typename T, typename OT, int D, bool VARLEN>
 __global__ __launch_bounds__(256) void fa_bwd_delta(BwdParams p) {
   constexpr int PER = D / 32;
@@ -82,7 +84,11 @@ __global__ __launch_bounds__(256) void fa_bwd_delta(BwdParams p) {
   for (int j = 0; j < PER; ++j) acc += (float)dop[j] * (float)op[j];
 #pragma unroll
   for (int m = 16; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 32);
-  if ((threadIdx.x & 31) == 0) p.delta[((long long)b * p.Hq + h) * p.N + r] = acc;
+  if ((threadIdx.x & 31) == 0) {
+    const long long li = ((long long)b * p.Hq + h) * p.N + r;
+    p.delta[li] = acc;
+    p.lse2[li] = p.lse[li] * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -111,7 +117,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv(BwdParams p) {
   __shared__ __attribute__((aligned(16))) char do_l1[DO_BYTES];
   __shared__ __attribute__((aligned(16))) char t_l0[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char t_l1[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) float ld_l0[2 * BR];   // L*log2(e), then D
+  __shared__ __attribute__((aligned(16))) float ld_l0[2 * BR];   // L * log2(e), then D
   __shared__ __attribute__((aligned(16))) float ld_l1[2 * BR];
 
   const int tid = threadIdx.x;
@@ -183,9 +189,8 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv(BwdParams p) {
   const int nt = (len + BR - 1) / BR - t_first;   // query tiles per head
   const int n_it = p.G * nt;
 
-  auto tile_load = [&](int it, char* ql, char* dol, char* tl, float* ldl)
+  auto tile_load = [&](int hh, int t, char* ql, char* dol, char* tl, float* ldl)
       __attribute__((always_inline)) {
-    const int hh = it / nt, t = t_first + it % nt;
     const int h = g * p.G + hh;
     const int qb = t * BR;
     const long long qbase = (VARLEN ? (long long)seq0 * p.q_rs : (long long)b * p.q_bs) +
@@ -212,7 +217,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv(BwdParams p) {
     // destination of lane L is base + 16 * L).
     if (wave == 0) {
       const long long lrow = ((long long)b * p.Hq + h) * p.N + qb;
-      const rsrc_t rl = make_rsrc(p.lse + lrow, (uint32_t)rows * 4);
+      const rsrc_t rl = make_rsrc(p.lse2 + lrow, (uint32_t)rows * 4);
       if (lane < 16) {
         lds_load16(rl, (char*)ldl, lane * 16);
       } else if (MODE == 1 && lane < 32) {
@@ -228,9 +233,8 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv(BwdParams p) {
   const float sl2 = p.scale_log2;
 
   // One 32-row query block (half hb of the tile in the given buffers).
-  auto block = [&](int it, int hb, const char* ql, const char* dol, const char* tl,
+  auto block = [&](int t, int hb, const char* ql, const char* dol, const char* tl,
                    const float* ldl) __attribute__((always_inline)) {
-    const int t = t_first + it % nt;
     const int qr0 = t * BR + 32 * hb;          // first query row of the block
     // A block whose rows all precede this wave's keys (causal), or a wave
     // with no keys, adds nothing.
@@ -261,26 +265,35 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv(BwdParams p) {
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_sched_barrier(0);
+    // P (and dS); the masks are tested only in blocks that cross the
+    // diagonal or an end of the sequence.
     uint32_t pk[8];
+    auto form = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int rl = 32 * hb + 8 * g4 + 4 * hf;   // row within the tile
-      const f32x4 L4 = *(const f32x4*)(ldl + rl);
-      f32x4 D4 = f32x4{};
-      if (MODE == 1) D4 = *(const f32x4*)(ldl + BR + rl);
-      float pe[4];
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int rl = 32 * hb + 8 * g4 + 4 * hf;   // row within the tile
+        const f32x4 L4 = *(const f32x4*)(ldl + rl);
+        f32x4 D4 = f32x4{};
+        if (MODE == 1) D4 = *(const f32x4*)(ldl + BR + rl);
+        float pe[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = 4 * g4 + j;
-        const int qr = qr0 + 8 * g4 + 4 * hf + j;
-        const bool vis = qr < len && key < len && !(CAUSAL && key > qr);
-        const float pv = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], sl2, -L4[j] * kLog2e))
-                             : 0.0f;
-        pe[j] = MODE == 1 ? pv * (dp[e] - D4[j]) : pv;
+        for (int j = 0; j < 4; ++j) {
+          const int e = 4 * g4 + j;
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], sl2, -L4[j]));
+          if (decltype(masked)::value) {
+            const int qr = qr0 + 8 * g4 + 4 * hf + j;
+            if (qr >= len || key >= len || (CAUSAL && key > qr)) pv = 0.0f;
+          }
+          pe[j] = MODE == 1 ? pv * (dp[e] - D4[j]) : pv;
+        }
+        pk[2 * g4] = Ops<T>::pack(pe[0], pe[1]);
+        pk[2 * g4 + 1] = Ops<T>::pack(pe[2], pe[3]);
       }
-      pk[2 * g4] = Ops<T>::pack(pe[0], pe[1]);
-      pk[2 * g4 + 1] = Ops<T>::pack(pe[2], pe[3]);
-    }
+    };
+    if (qr0 + 31 >= len || kw0 + 31 >= len || (CAUSAL && kw0 + 31 > qr0))
+      form(BoolTag<true>{});
+    else
+      form(BoolTag<false>{});
     __builtin_amdgcn_sched_barrier(0);
     // dV^T += dO^T P, or dK^T += Q^T dS, over the block's two 16-row chunks.
 #pragma unroll
@@ -303,19 +316,35 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv(BwdParams p) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  if (n_it > 0) tile_load(0, q_l0, do_l0, t_l0, ld_l0);
+  // Iteration it is (query head hh, tile t); the pair advances without a
+  // division.
+  auto next = [&](int& hh, int& t) __attribute__((always_inline)) {
+    if (++t == t_first + nt) {
+      t = t_first;
+      ++hh;
+    }
+  };
+  int h0 = 0, t0 = t_first, h1 = 0, t1 = t_first;
+  next(h1, t1);
+  if (n_it > 0) tile_load(h0, t0, q_l0, do_l0, t_l0, ld_l0);
   for (int it = 0; it < n_it; it += 2) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
-    if (it + 1 < n_it) tile_load(it + 1, q_l1, do_l1, t_l1, ld_l1);
-    block(it, 0, q_l0, do_l0, t_l0, ld_l0);
-    block(it, 1, q_l0, do_l0, t_l0, ld_l0);
+    if (it + 1 < n_it) tile_load(h1, t1, q_l1, do_l1, t_l1, ld_l1);
+    block(t0, 0, q_l0, do_l0, t_l0, ld_l0);
+    block(t0, 1, q_l0, do_l0, t_l0, ld_l0);
     if (it + 1 >= n_it) break;
+    h0 = h1;
+    t0 = t1;
+    next(h0, t0);                              // iteration it + 2
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
-    if (it + 2 < n_it) tile_load(it + 2, q_l0, do_l0, t_l0, ld_l0);
-    block(it + 1, 0, q_l1, do_l1, t_l1, ld_l1);
-    block(it + 1, 1, q_l1, do_l1, t_l1, ld_l1);
+    if (it + 2 < n_it) tile_load(h0, t0, q_l0, do_l0, t_l0, ld_l0);
+    block(t1, 0, q_l1, do_l1, t_l1, ld_l1);
+    block(t1, 1, q_l1, do_l1, t_l1, ld_l1);
+    h1 = h0;
+    t1 = t0;
+    next(h1, t1);                              // iteration it + 3
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
@@ -475,16 +504,22 @@ __global__ __launch_bounds__(512, 2) void fa_bwd_dq(BwdParams p) {
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_sched_barrier(0);
-    // Element e of lane (query, hf) is key kb + 8*(e/4) + 4*hf + e%4.
+    // Element e of lane (query, hf) is key kb + 8*(e/4) + 4*hf + e%4.  Only
+    // a block that crosses the diagonal or the end of the sequence is masked
+    // (scores set to -inf, so P = 0); rows past the end have l2 = +inf.
+    if ((CAUSAL && kb + 31 > row0) || kb + 32 > len) {
+      const int lim = (CAUSAL ? min(len, qrow + 1) : len) - kb - 4 * hf;
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (8 * (e >> 2) + (e & 3) >= lim) s[e] = -__builtin_inff();
+    }
     uint32_t pk[8];
 #pragma unroll
     for (int e = 0; e < 16; e += 2) {
       float ds[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int kk = kb + 8 * ((e + j) >> 2) + 4 * hf + ((e + j) & 3);
-        const bool vis = kk < len && !(CAUSAL && kk > qrow);
-        const float pv = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[e + j], sl2, -l2)) : 0.0f;
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e + j], sl2, -l2));
         ds[j] = pv * (dp[e + j] - dl);
       }
       pk[e >> 1] = Ops<T>::pack(ds[0], ds[1]);
@@ -583,17 +618,19 @@ const DeltaVariant kDeltaVariants[] = {
 
 }  // namespace
 
-// Workspace layout of the backward pass: D (fp32 rows, padded to 256 B),
-// then the packed Q^T, dO^T (B * Hq * tiles each) and K^T (B * Hkv * tiles).
+// Workspace layout of the backward pass: D and L * log2(e) (fp32 rows, each
+// padded to 256 B), then the packed Q^T, dO^T (B * Hq * tiles each) and K^T
+// (B * Hkv * tiles).
 struct BwdLayout {
-  uint64_t delta, qt, dot, kt, total;
+  uint64_t delta, lse2, qt, dot, kt, total;
 };
 static BwdLayout bwd_layout(int B, int Hq, int Hkv, int N, int d) {
   BwdLayout l;
   const uint64_t rows = (uint64_t)B * Hq * N;
   const uint64_t tile = 128ull * d;
   l.delta = 0;
-  l.qt = (rows * 4 + 255) & ~255ull;
+  l.lse2 = (rows * 4 + 255) & ~255ull;
+  l.qt = 2 * l.lse2;
   l.dot = l.qt + (uint64_t)B * Hq * vt_tiles(N) * tile;
   l.kt = l.dot + (uint64_t)B * Hq * vt_tiles(N) * tile;
   l.total = l.kt + (uint64_t)B * Hkv * vt_tiles(N) * tile;
@@ -623,6 +660,7 @@ int launch_bwd(const BwdArgs& a, void* stream) {
   BwdParams p;
   p.q = a.q; p.k = a.k; p.v = a.v; p.o = a.o; p.dout = a.dout; p.lse = a.lse;
   p.delta = (float*)(ws + lay.delta);
+  p.lse2 = (float*)(ws + lay.lse2);
   p.qt = ws + lay.qt; p.dot = ws + lay.dot; p.kt = ws + lay.kt;
   p.dq = a.dq; p.dk = a.dk; p.dv = a.dv;
   p.cu_seqlens = a.cu_seqlens;
