@@ -502,6 +502,10 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
                   uint32_t (&pk_cur)[QB][8], const uint32_t (&pk_prev)[QB][8],
                   const char* ks_nxt, const char* vs_prev, int hb_prev)
       __attribute__((always_inline)) {
+    // A wave with no rows (past the sequence end: a partial last row block,
+    // or the empty row groups of a decode step) only takes part in the
+    // loads and barriers.
+    if (!active) return;
     int kb;
     bool live;
     blk(st, e_st, kb, live);
