@@ -1020,7 +1020,9 @@ int launch_fwd(const LaunchArgs& a, void* stream) {
 int suggest_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int in_dtype, int cus) {
   if (in_dtype == FA_F32 || Nq > 64 || cus <= 0) return 1;
   const Plan plan = make_plan(B, Hq, Hkv, Nq, d, in_dtype);
-  const uint64_t want = 2ull * (uint64_t)cus;          // two waves of workgroups
+  // One workgroup fills a compute unit (its eight waves take the VGPRs of
+  // two per SIMD); split only grids smaller than one per compute unit.
+  const uint64_t want = (uint64_t)cus;
   if (plan.total_wg >= want) return 1;
   const int tiles = vt_tiles(Nk);
   uint64_t n = (want + plan.total_wg - 1) / plan.total_wg;

@@ -77,7 +77,8 @@ def test_splits_on_prefill_shape():
 
 def test_num_splits_heuristic():
     import exact_io_aware_amd as fa
-    assert fa.num_splits(32, 32, 8, 1, 8192, 128, fa.FA_BF16) > 1      # decode: split
+    assert fa.num_splits(4, 32, 8, 1, 8192, 128, fa.FA_BF16) > 1       # small decode: split
+    assert fa.num_splits(32, 32, 8, 1, 8192, 128, fa.FA_BF16) == 1     # one workgroup per CU
     assert fa.num_splits(4, 32, 8, 4096, 4096, 128, fa.FA_BF16) == 1   # prefill: no split
     assert fa.num_splits(4, 32, 8, 1, 8192, 128, fa.FA_F32) == 1        # fp32: never
 
