@@ -149,3 +149,36 @@ def test_streaming_workload_sampled_heads():
         el = np.abs(L[b, h] - Lref[0, 0]).max()
         G.say(f"  unit ({b},{h}) errors O {eo:.3e} L {el:.3e}")
         assert eo <= G.O_TOL["bf16"] and el <= G.L_TOL
+
+
+def test_sparse_longest_tile_list():
+    """The longest tile list a workgroup can hold (4096 key tiles: 262144
+    keys per sequence).  The last 64-row query block admits every key block;
+    every other query block only its own.  Its rows are plain attention over
+    all keys (the oracle on those 64 rows); a few diagonal blocks are plain
+    attention over their own 64 keys."""
+    import torch
+
+    import exact_io_aware_amd as fa
+    N, nb = 64 * 4096, 4096
+    w = workloads.make_custom(1, 2, 1, 128, "bf16", seed=970, N=N)
+    bm = np.eye(nb, dtype=np.uint8)[None, None]
+    bm[0, 0, nb - 1, :] = 1
+    G.say("sparse: 4096-tile list, N = 262144")
+    q, k, v = (G.to_device(w[x], "bf16", "cuda:0") for x in "qkv")
+    o, lse = fa.fwd(q, k, v, causal=False, block_mask=torch.from_numpy(bm).to("cuda:0"))
+    torch.cuda.synchronize()
+    O, L = o.double().cpu().numpy(), lse.double().cpu().numpy()
+    qf, kf, vf = G.f64_inputs(w)
+    scale = 128 ** -0.5
+    Oref, Lref = oracle.attention_qk(qf[:, :, N - 64:], kf, vf, causal=False, scale=scale)
+    eo = np.abs(O[:, :, N - 64:] - Oref).max()
+    el = np.abs(L[:, :, N - 64:] - Lref).max()
+    G.say(f"  last block errors O {eo:.3e} L {el:.3e}")
+    assert eo <= G.O_TOL["bf16"] and el <= G.L_TOL
+    for i in (0, 1, 2047, 4094):
+        sl = slice(64 * i, 64 * i + 64)
+        Ob, Lb = oracle.attention(qf[:, :, sl], kf[:, :, sl], vf[:, :, sl], causal=False,
+                                  scale=scale)
+        assert np.abs(O[:, :, sl] - Ob).max() <= G.O_TOL["bf16"], i
+        assert np.abs(L[:, :, sl] - Lb).max() <= G.L_TOL, i
