@@ -441,17 +441,22 @@ __global__ __launch_bounds__(512, 2) void fa_bwd_dq(BwdParams p) {
     }
   }
 
-  uint32_t koff[LOADS], toff[LOADS];
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int pch = tid + NT * i;
-    const int r = pch / CPR, pc = pch % CPR;
-    koff[i] = r * kv_rs_bytes + ((pc ^ k_swz<D>(r)) << 4);
-    const int tr = pch / 8, tc = pch % 8;
-    toff[i] = tr * 128 + ((tc ^ vt_swz(tr)) << 4);
-  }
   const char* ktp = (const char*)p.kt + (long long)(b * p.Hkv + kvh) * p.ntiles * TILE_BYTES;
   auto tile_load = [&](int t, char* kl, char* vl, char* ktl) __attribute__((always_inline)) {
+    // The per-lane fill offsets are recomputed at each tile (a few integer
+    // instructions) rather than kept in registers across the loop, where
+    // they would be spilled.
+    int tid_t = tid;
+    asm volatile("" : "+v"(tid_t));
+    uint32_t koff[LOADS], toff[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int pch = tid_t + NT * i;
+      const int r = pch / CPR, pc = pch % CPR;
+      koff[i] = r * kv_rs_bytes + ((pc ^ k_swz<D>(r)) << 4);
+      const int tr = pch / 8, tc = pch % 8;
+      toff[i] = tr * 128 + ((tc ^ vt_swz(tr)) << 4);
+    }
     const int kb = t * BC;
     const int rows = __builtin_amdgcn_readfirstlane(max(0, min(len - kb, BC)));
     const long long at = (long long)min(kb, len) * p.kv_rs;

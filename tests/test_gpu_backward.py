@@ -19,6 +19,7 @@ CASES = [
     ("fp16", 64, 2, 6, 3, 97, False),
     ("bf16", 128, 3, 8, 2, [70, 1, 190], True),
     ("fp16", 64, 2, 4, 2, [129, 64], False),
+    ("bf16", 128, 3, 8, 2, [70, 0, 33], True),        # an empty sequence
 ]
 
 

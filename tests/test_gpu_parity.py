@@ -59,6 +59,8 @@ MEDIUM = [
     ("bf16", 64, 3, 4, 2, [200, 7, 128], False),
     ("fp16", 128, 3, 4, 4, [65, 1, 190], True),
     ("fp32", 64, 2, 2, 1, [31, 90], True),
+    ("bf16", 128, 3, 8, 2, [100, 0, 64], True),      # an empty sequence
+    ("fp32", 64, 3, 2, 1, [0, 40, 0], False),
 ]
 
 

@@ -25,6 +25,7 @@ CASES = [
     ("bf16", 128, 4, 8, 2, [70, 1, 190, 130], [70, 1, 190, 130], True, "both", 0.5),
     ("fp16", 64, 3, 4, 2, [10, 64, 100], [40, 64, 300], True, "head", 0.6),
     ("bf16", 128, 1, 32, 8, 600, 600, True, "head", 0.15),     # many empty rows
+    ("bf16", 128, 3, 8, 2, [50, 0, 80], [50, 0, 80], True, "both", 0.5),  # an empty sequence
 ]
 
 
