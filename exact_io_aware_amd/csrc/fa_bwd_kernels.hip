@@ -14,21 +14,23 @@
 //  * fa_bwd_delta: D_r, one 32-lane group per row.
 //  * fa_bwd_dkdv<MODE>: a workgroup of 8 waves owns 256 keys of one K/V head
 //    (each wave 32 keys, its K (and V) rows in registers as MFMA B operands)
-//    and streams 64-row query tiles of every query head of the group.  The
-//    dV kernel (MODE 0) reads Q row-major (A operand of S = Q K^T) and dO^T
-//    (A operand of dV^T += dO^T P); the dK kernel (MODE 1) reads Q and dO
-//    row-major (S and dP = dO V^T) and Q^T (dK^T += Q^T dS).  S's
-//    accumulator puts one key per lane column, which is exactly the
-//    B-operand layout of P and dS for the gradient products (the query order
-//    in each 16-row chunk permuted as in the packed transposes).  Split in
-//    two, S is formed twice but neither kernel runs out of registers (fused,
-//    K, V, two score blocks and two accumulators do).  No atomics.
+//    and streams 64-row query tiles (Q and dO, row-major) of every query
+//    head of the group.  The dV kernel (MODE 0) reads Q by rows (A operand
+//    of S = Q K^T) and dO transposed (A operand of dV^T += dO^T P); the dK
+//    kernel (MODE 1) reads Q and dO by rows (S and dP = dO V^T) and Q
+//    transposed (dK^T += Q^T dS).  S's accumulator puts one key per lane
+//    column, which is exactly the B-operand layout of P and dS for the
+//    gradient products, and the transposing LDS reads deliver the query
+//    rows in that accumulator's order.  Split in two, S is formed twice but
+//    neither kernel runs out of registers (fused, K, V, two score blocks and
+//    two accumulators do).  No atomics.
 //  * fa_bwd_dq: the forward kernel's structure: a wave owns 32 query rows
-//    (Q and dO in registers), streams 64-key tiles of K, V (row-major) and
-//    K^T, forms S^T = K Q^T and dP^T = V dO^T with one query per lane
-//    column, and accumulates dQ^T += K^T dS^T.
-//  * The transposes Q^T, dO^T, K^T are written by the V^T packing kernel of
-//    the forward pass (64-row tiles, rows in the P.V fragment order).
+//    (Q and dO in registers), streams 64-key tiles of K and V (row-major),
+//    forms S^T = K Q^T and dP^T = V dO^T with one query per lane column, and
+//    accumulates dQ^T += K^T dS^T, K^T read from the same K tile.
+//  * Every tile is row-major in LDS with the rm_swz layout, read by rows or
+//    transposed (gfx950's ds_read_b64_tr_b16), so no transposed copy of any
+//    tensor is made.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -46,10 +48,9 @@ struct BwdParams {
   const float* lse;          // [B][Hq][N], natural log
   float* delta;              // [B][Hq][N], rowsum(dO * O)
   float* lse2;               // [B][Hq][N], lse * log2(e)
-  const void* qt; const void* dot; const void* kt;   // packed transposes
   void* dq; void* dk; void* dv;
   const int* cu_seqlens;
-  int B, N, Hq, Hkv, G, ntiles;
+  int B, N, Hq, Hkv, G;
   int hp, rows_per_wg, n_rblocks, n_hgroups;     // dq grid (as the forward)
   int kv_blocks;                                 // dV, dK: 256-key blocks per sequence
   float scale, scale_log2;
@@ -95,8 +96,8 @@ __global__ __launch_bounds__(256) void fa_bwd_delta(BwdParams p) {
 // dV (MODE 0) or dK (MODE 1).  One workgroup: 8 waves x 32 keys of K/V head g
 // of sequence b.  The two gradients run as two kernels: fused, the four
 // products' operands and two accumulators exceed one wave's registers.
-//   MODE 0: S = Q K^T, P, dV^T += dO^T P          (tiles Q, dO^T; L)
-//   MODE 1: S, dP = dO V^T, dS, dK^T += Q^T dS    (tiles Q, dO, Q^T; L, D)
+//   MODE 0: S = Q K^T, P, dV^T += dO^T P          (tiles Q, dO; L)
+//   MODE 1: S, dP = dO V^T, dS, dK^T += Q^T dS    (tiles Q, dO; L, D)
 template <typename T, int D, bool CAUSAL, bool VARLEN, bool OUT_F32, int MODE>
 __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv(BwdParams p) {
   using vec8 = typename Ops<T>::vec8;
@@ -106,17 +107,13 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv(BwdParams p) {
   constexpr int TILE_BYTES = BR * RB;
   constexpr int HALF = 32 * RB;
   constexpr int LOADS = BR * CPR / NT;       // 16-byte loads per thread per tile
-  constexpr int DO_BYTES = MODE == 1 ? TILE_BYTES : 16;
   static_assert(LOADS >= 1 && BR * CPR == LOADS * NT, "tile fill");
 
-  // Per buffer: Q (row-major), dO (row-major, dK only), the transposed
-  // operand of the gradient product (dO^T for dV, Q^T for dK), L and D.
+  // Per buffer: Q and dO (row-major, rm_swz), L and D of the 64 rows.
   __shared__ __attribute__((aligned(16))) char q_l0[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char q_l1[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char do_l0[DO_BYTES];
-  __shared__ __attribute__((aligned(16))) char do_l1[DO_BYTES];
-  __shared__ __attribute__((aligned(16))) char t_l0[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char t_l1[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char do_l0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char do_l1[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) float ld_l0[2 * BR];   // L * log2(e), then D
   __shared__ __attribute__((aligned(16))) float ld_l1[2 * BR];
 
@@ -165,31 +162,30 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv(BwdParams p) {
     }
   }
 
-  // Tile fill offsets (as the forward: row-major swizzled, and packed).
-  uint32_t roff[LOADS], toff[LOADS];
+  // Tile fill offsets (row-major, rm_swz).
+  uint32_t roff[LOADS];
   const uint32_t q_rs_bytes = (uint32_t)p.q_rs * 2;
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int pch = tid + NT * i;
     const int r = pch / CPR, pc = pch % CPR;
-    roff[i] = r * q_rs_bytes + ((pc ^ k_swz<D>(r)) << 4);
-    const int tr = pch / 8, tc = pch % 8;
-    toff[i] = tr * 128 + ((tc ^ vt_swz(tr)) << 4);
+    roff[i] = r * q_rs_bytes + ((pc ^ rm_swz<D>(r)) << 4);
   }
-  // Operand read addresses (as the forward's K and V^T reads).
+  // Operand read addresses: by rows (query l32 of a 32-row block, 16-byte
+  // chunk 2 dc + hf) and transposed (column block db).
   int raddr[DC];
 #pragma unroll
-  for (int dc = 0; dc < DC; ++dc) raddr[dc] = l32 * RB + (((2 * dc + hf) ^ k_swz<D>(l32)) << 4);
-  int taddr[4];
+  for (int dc = 0; dc < DC; ++dc) raddr[dc] = l32 * RB + (((2 * dc + hf) ^ rm_swz<D>(l32)) << 4);
+  int tbase[DB];
 #pragma unroll
-  for (int qq = 0; qq < 4; ++qq) taddr[qq] = l32 * 128 + (((2 * qq + hf) ^ vt_swz(l32)) << 4);
+  for (int db = 0; db < DB; ++db) tbase[db] = tr_base<D>(lane, db);
 
   // Iterations: (query head hh of the group, 64-row query tile t).
   const int t_first = CAUSAL ? kwg / BR : 0;
   const int nt = (len + BR - 1) / BR - t_first;   // query tiles per head
   const int n_it = p.G * nt;
 
-  auto tile_load = [&](int hh, int t, char* ql, char* dol, char* tl, float* ldl)
+  auto tile_load = [&](int hh, int t, char* ql, char* dol, float* ldl)
       __attribute__((always_inline)) {
     const int h = g * p.G + hh;
     const int qb = t * BR;
@@ -199,18 +195,12 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv(BwdParams p) {
     const uint32_t rbytes = (uint32_t)rows * q_rs_bytes;
     const long long at = qbase + (long long)min(qb, len) * p.q_rs;
     const rsrc_t rq = make_rsrc((const T*)p.q + at, rbytes);
-    const long long tix = ((long long)(b * p.Hq + h) * p.ntiles + t) * TILE_BYTES;
-    const rsrc_t rt = make_rsrc((const char*)(MODE == 1 ? p.qt : p.dot) + tix, (uint32_t)TILE_BYTES);
+    const rsrc_t rdo = make_rsrc((const T*)p.dout + at, rbytes);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int o = (NT * i + 64 * wave) * 16;
       lds_load16(rq, ql + o, roff[i]);
-      lds_load16(rt, tl + o, toff[i]);
-    }
-    if (MODE == 1) {
-      const rsrc_t rdo = make_rsrc((const T*)p.dout + at, rbytes);
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) lds_load16(rdo, dol + (NT * i + 64 * wave) * 16, roff[i]);
+      lds_load16(rdo, dol + o, roff[i]);
     }
     // L and D of the 64 rows (128 floats) from wave 0: lanes 0-15 fetch L
     // into ldl[0, 64), lanes 16-31 D into ldl[64, 128) (the LDS-direct
@@ -233,8 +223,8 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv(BwdParams p) {
   const float sl2 = p.scale_log2;
 
   // One 32-row query block (half hb of the tile in the given buffers).
-  auto block = [&](int t, int hb, const char* ql, const char* dol, const char* tl,
-                   const float* ldl) __attribute__((always_inline)) {
+  auto block = [&](int t, int hb, const char* ql, const char* dol, const float* ldl)
+      __attribute__((always_inline)) {
     const int qr0 = t * BR + 32 * hb;          // first query row of the block
     // A block whose rows all precede this wave's keys (causal), or a wave
     // with no keys, adds nothing.
@@ -295,22 +285,26 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv(BwdParams p) {
     else
       form(BoolTag<false>{});
     __builtin_amdgcn_sched_barrier(0);
-    // dV^T += dO^T P, or dK^T += Q^T dS, over the block's two 16-row chunks.
+    // dV^T += dO^T P, or dK^T += Q^T dS, over the block's two 16-row chunks
+    // (dO or Q read transposed from its tile).
+    const char* tl = MODE == 1 ? ql : dol;
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       const u32x4 pb = {pk[4 * kc], pk[4 * kc + 1], pk[4 * kc + 2], pk[4 * kc + 3]};
       const vec8 pf = __builtin_bit_cast(vec8, pb);
+      const int r0 = 32 * hb + 16 * kc;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const vec8 ta = *(const vec8*)(tl + taddr[2 * hb + kc] + db * 32 * 128);
+        const vec8 ta = lds_read_tr<vec8>(tl + tbase[db] + r0 * RB,
+                                          tl + (tbase[db] ^ 32) + (r0 + 8) * RB);
         acc[db] = Ops<T>::mfma(ta, pf, acc[db]);
       }
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int i = 0; i < 2 * DB - 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -326,22 +320,22 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv(BwdParams p) {
   };
   int h0 = 0, t0 = t_first, h1 = 0, t1 = t_first;
   next(h1, t1);
-  if (n_it > 0) tile_load(h0, t0, q_l0, do_l0, t_l0, ld_l0);
+  if (n_it > 0) tile_load(h0, t0, q_l0, do_l0, ld_l0);
   for (int it = 0; it < n_it; it += 2) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
-    if (it + 1 < n_it) tile_load(h1, t1, q_l1, do_l1, t_l1, ld_l1);
-    block(t0, 0, q_l0, do_l0, t_l0, ld_l0);
-    block(t0, 1, q_l0, do_l0, t_l0, ld_l0);
+    if (it + 1 < n_it) tile_load(h1, t1, q_l1, do_l1, ld_l1);
+    block(t0, 0, q_l0, do_l0, ld_l0);
+    block(t0, 1, q_l0, do_l0, ld_l0);
     if (it + 1 >= n_it) break;
     h0 = h1;
     t0 = t1;
     next(h0, t0);                              // iteration it + 2
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
-    if (it + 2 < n_it) tile_load(h0, t0, q_l0, do_l0, t_l0, ld_l0);
-    block(t1, 0, q_l1, do_l1, t_l1, ld_l1);
-    block(t1, 1, q_l1, do_l1, t_l1, ld_l1);
+    if (it + 2 < n_it) tile_load(h0, t0, q_l0, do_l0, ld_l0);
+    block(t1, 0, q_l1, do_l1, ld_l1);
+    block(t1, 1, q_l1, do_l1, ld_l1);
     h1 = h0;
     t1 = t0;
     next(h1, t1);                              // iteration it + 3
@@ -370,8 +364,8 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv(BwdParams p) {
 
 // ---------------------------------------------------------------------------
 // dQ.  The forward kernel's layout: 8 waves, each 32 query rows of one head
-// (up to 4 heads of a K/V group per workgroup), 64-key tiles of K, V and
-// K^T double-buffered in LDS.
+// (up to 4 heads of a K/V group per workgroup), 64-key tiles of K and V
+// double-buffered in LDS; K^T is the K tile read transposed.
 template <typename T, int D, bool CAUSAL, bool VARLEN, bool OUT_F32>
 __global__ __launch_bounds__(512, 2) void fa_bwd_dq(BwdParams p) {
   using vec8 = typename Ops<T>::vec8;
@@ -386,8 +380,6 @@ __global__ __launch_bounds__(512, 2) void fa_bwd_dq(BwdParams p) {
   __shared__ __attribute__((aligned(16))) char k_l1[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char v_l0[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char v_l1[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char kt_l0[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char kt_l1[TILE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -441,51 +433,46 @@ __global__ __launch_bounds__(512, 2) void fa_bwd_dq(BwdParams p) {
     }
   }
 
-  const char* ktp = (const char*)p.kt + (long long)(b * p.Hkv + kvh) * p.ntiles * TILE_BYTES;
-  auto tile_load = [&](int t, char* kl, char* vl, char* ktl) __attribute__((always_inline)) {
+  auto tile_load = [&](int t, char* kl, char* vl) __attribute__((always_inline)) {
     // The per-lane fill offsets are recomputed at each tile (a few integer
     // instructions) rather than kept in registers across the loop, where
     // they would be spilled.
     int tid_t = tid;
     asm volatile("" : "+v"(tid_t));
-    uint32_t koff[LOADS], toff[LOADS];
+    uint32_t koff[LOADS];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int pch = tid_t + NT * i;
       const int r = pch / CPR, pc = pch % CPR;
-      koff[i] = r * kv_rs_bytes + ((pc ^ k_swz<D>(r)) << 4);
-      const int tr = pch / 8, tc = pch % 8;
-      toff[i] = tr * 128 + ((tc ^ vt_swz(tr)) << 4);
+      koff[i] = r * kv_rs_bytes + ((pc ^ rm_swz<D>(r)) << 4);
     }
     const int kb = t * BC;
     const int rows = __builtin_amdgcn_readfirstlane(max(0, min(len - kb, BC)));
     const long long at = (long long)min(kb, len) * p.kv_rs;
     const rsrc_t rk = make_rsrc((const T*)p.k + kvbase + at, (uint32_t)rows * kv_rs_bytes);
     const rsrc_t rv = make_rsrc((const T*)p.v + kvbase + at, (uint32_t)rows * kv_rs_bytes);
-    const int live = __builtin_amdgcn_readfirstlane(kb < len ? 1 : 0);
-    const rsrc_t rt = make_rsrc(ktp + (long long)min(t, p.ntiles) * TILE_BYTES,
-                                live ? (uint32_t)TILE_BYTES : 0u);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int o = (NT * i + 64 * wave) * 16;
       lds_load16(rk, kl + o, koff[i]);
       lds_load16(rv, vl + o, koff[i]);
-      lds_load16(rt, ktl + o, toff[i]);
     }
   };
+  // Operand read addresses: K and V by rows (key l32 of a 32-key block,
+  // 16-byte chunk 2 dc + hf), K transposed (column block db).
   int kaddr[DC];
 #pragma unroll
-  for (int dc = 0; dc < DC; ++dc) kaddr[dc] = l32 * RB + (((2 * dc + hf) ^ k_swz<D>(l32)) << 4);
-  int taddr[4];
+  for (int dc = 0; dc < DC; ++dc) kaddr[dc] = l32 * RB + (((2 * dc + hf) ^ rm_swz<D>(l32)) << 4);
+  int tbase[DB];
 #pragma unroll
-  for (int qq = 0; qq < 4; ++qq) taddr[qq] = l32 * 128 + (((2 * qq + hf) ^ vt_swz(l32)) << 4);
+  for (int db = 0; db < DB; ++db) tbase[db] = tr_base<D>(lane, db);
 
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
   const float sl2 = p.scale_log2;
 
-  auto block = [&](int t, int hb, const char* kl, const char* vl, const char* ktl)
+  auto block = [&](int t, int hb, const char* kl, const char* vl)
       __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
     const int kb = t * BC + 32 * hb;
@@ -530,41 +517,43 @@ __global__ __launch_bounds__(512, 2) void fa_bwd_dq(BwdParams p) {
       pk[e >> 1] = Ops<T>::pack(ds[0], ds[1]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // dQ^T += K^T dS^T.
+    // dQ^T += K^T dS^T (K read transposed from its tile).
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       const u32x4 sb = {pk[4 * kc], pk[4 * kc + 1], pk[4 * kc + 2], pk[4 * kc + 3]};
       const vec8 sf = __builtin_bit_cast(vec8, sb);
+      const int r0 = 32 * hb + 16 * kc;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const vec8 a = *(const vec8*)(ktl + taddr[2 * hb + kc] + db * 32 * 128);
+        const vec8 a = lds_read_tr<vec8>(kl + tbase[db] + r0 * RB,
+                                         kl + (tbase[db] ^ 32) + (r0 + 8) * RB);
         acc[db] = Ops<T>::mfma(a, sf, acc[db]);
       }
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int i = 0; i < 2 * DB - 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
 
   const int ntl = (kv_end + BC - 1) / BC;
-  tile_load(0, k_l0, v_l0, kt_l0);
+  tile_load(0, k_l0, v_l0);
   for (int t = 0; t < ntl; t += 2) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
-    if (t + 1 < ntl) tile_load(t + 1, k_l1, v_l1, kt_l1);
-    block(t, 0, k_l0, v_l0, kt_l0);
-    block(t, 1, k_l0, v_l0, kt_l0);
+    if (t + 1 < ntl) tile_load(t + 1, k_l1, v_l1);
+    block(t, 0, k_l0, v_l0);
+    block(t, 1, k_l0, v_l0);
     if (t + 1 >= ntl) break;
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
-    if (t + 2 < ntl) tile_load(t + 2, k_l0, v_l0, kt_l0);
-    block(t + 1, 0, k_l1, v_l1, kt_l1);
-    block(t + 1, 1, k_l1, v_l1, kt_l1);
+    if (t + 2 < ntl) tile_load(t + 2, k_l0, v_l0);
+    block(t + 1, 0, k_l1, v_l1);
+    block(t + 1, 1, k_l1, v_l1);
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
@@ -623,22 +612,19 @@ const DeltaVariant kDeltaVariants[] = {
 
 }  // namespace
 
-// Workspace layout of the backward pass: D and L * log2(e) (fp32 rows, each
-// padded to 256 B), then the packed Q^T, dO^T (B * Hq * tiles each) and K^T
-// (B * Hkv * tiles).
+// Workspace layout of the backward pass: D and L * log2(e), fp32 rows
+// [B][Hq][N], each padded to 256 B.
 struct BwdLayout {
-  uint64_t delta, lse2, qt, dot, kt, total;
+  uint64_t delta, lse2, total;
 };
 static BwdLayout bwd_layout(int B, int Hq, int Hkv, int N, int d) {
+  (void)Hkv;
+  (void)d;
   BwdLayout l;
   const uint64_t rows = (uint64_t)B * Hq * N;
-  const uint64_t tile = 128ull * d;
   l.delta = 0;
   l.lse2 = (rows * 4 + 255) & ~255ull;
-  l.qt = 2 * l.lse2;
-  l.dot = l.qt + (uint64_t)B * Hq * vt_tiles(N) * tile;
-  l.kt = l.dot + (uint64_t)B * Hq * vt_tiles(N) * tile;
-  l.total = l.kt + (uint64_t)B * Hkv * vt_tiles(N) * tile;
+  l.total = 2 * l.lse2;
   return l;
 }
 
@@ -666,11 +652,9 @@ int launch_bwd(const BwdArgs& a, void* stream) {
   p.q = a.q; p.k = a.k; p.v = a.v; p.o = a.o; p.dout = a.dout; p.lse = a.lse;
   p.delta = (float*)(ws + lay.delta);
   p.lse2 = (float*)(ws + lay.lse2);
-  p.qt = ws + lay.qt; p.dot = ws + lay.dot; p.kt = ws + lay.kt;
   p.dq = a.dq; p.dk = a.dk; p.dv = a.dv;
   p.cu_seqlens = a.cu_seqlens;
   p.B = a.B; p.N = a.N; p.Hq = a.Hq; p.Hkv = a.Hkv; p.G = a.Hq / a.Hkv;
-  p.ntiles = vt_tiles(a.N);
   const Plan plan = make_plan(a.B, a.Hq, a.Hkv, a.N, a.d, a.in_dtype);
   p.hp = plan.hp; p.rows_per_wg = plan.rows_per_wg; p.n_rblocks = plan.n_rblocks;
   p.n_hgroups = plan.n_hgroups;
@@ -690,12 +674,6 @@ int launch_bwd(const BwdArgs& a, void* stream) {
   if (hipLaunchKernel((const void*)dv->fn, dim3((unsigned)((rows + 7) / 8)), dim3(256), args, 0,
                       s) != hipSuccess)
     return FA_ERR_LAUNCH;
-  int st = launch_vt_pack(a.q, ws + lay.qt, a.B, a.Hq, a.N, a.d, a.cu_seqlens, a.in_dtype, stream);
-  if (st == FA_OK)
-    st = launch_vt_pack(a.dout, ws + lay.dot, a.B, a.Hq, a.N, a.d, a.cu_seqlens, a.in_dtype, stream);
-  if (st == FA_OK)
-    st = launch_vt_pack(a.k, ws + lay.kt, a.B, a.Hkv, a.N, a.d, a.cu_seqlens, a.in_dtype, stream);
-  if (st != FA_OK) return st;
   const unsigned g1 = (unsigned)((uint64_t)a.B * a.Hkv * p.kv_blocks);
   if (hipLaunchKernel((const void*)var->dv, dim3(g1), dim3(512), args, 0, s) != hipSuccess ||
       hipLaunchKernel((const void*)var->dk, dim3(g1), dim3(512), args, 0, s) != hipSuccess)

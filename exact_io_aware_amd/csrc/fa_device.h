@@ -107,6 +107,55 @@ __device__ __forceinline__ void lds_load16(rsrc_t r, char* lds_dst, uint32_t vof
 //    c ^ ((r / 2) % 8)
 template <bool B> struct BoolTag { static constexpr bool value = B; };
 
+// Row-major 16-bit tiles that are read both by rows (one 16-byte
+// ds_read_b128 per lane; 16 lanes, 16 consecutive rows, per cycle) and
+// transposed (ds_read_b64_tr_b16; 32 lanes per cycle, 64 bytes from each of
+// 4 consecutive rows): chunk c of row r is stored at chunk c ^ rm_swz(r),
+// which keeps both patterns free of bank conflicts:
+//   D = 128 (16 chunks per row): 4 * (r % 4) + (r / 4) % 4
+//   D = 64  (8 chunks per row):  with m = (r / 2) % 8, 4 * (m % 2) + m / 2
+// It has period 16 in r, and rm_swz(r + 8) = rm_swz(r) ^ 2 for r % 16 < 8.
+template <int D>
+__device__ __forceinline__ int rm_swz(int r) {
+  if (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+  const int m = (r >> 1) & 7;
+  return 4 * (m & 1) + (m >> 1);
+}
+
+// Transposed MFMA A operand from a row-major rm_swz tile: for a 16-row
+// chunk starting at row R (R % 16 == 0) and output columns 32 cb .. 32 cb
+// + 31, lane L gets column 32 cb + L % 32 at the chunk's rows in the order
+// of a 32x32x16 A operand's k index (k = 8 (L / 32) + j holds row
+// 8 (j / 4) + 4 (L / 32) + j % 4, the order in which a 32x32 accumulator
+// holds its rows).  ds_read_b64_tr_b16 gives output lane j of each 16-lane
+// group element k of source lane 4 k + j / 4, element j % 4 (probed on
+// gfx950), so source lane L reads 4 columns of row 4 (L / 32) + (L % 16) / 4
+// (+ 8 for the second read).  tr_base is the per-lane byte offset of the
+// first read for column block cb; the second read is at (tr_base ^ 32) + 8
+// rows (rm_swz(r + 8) = rm_swz(r) ^ 2 flips bit 1 of the chunk index).
+// The two transposing reads of one A operand (lo: first 8 rows, hi: the
+// next 8), concatenated.  Device pass only, as lds_load16.
+template <typename VEC8>
+__device__ __forceinline__ VEC8 lds_read_tr(const char* lo, const char* hi) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lo);
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)hi);
+  return __builtin_bit_cast(VEC8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+#else
+  (void)lo; (void)hi;
+  return VEC8{};
+#endif
+}
+
+template <int D>
+__device__ __forceinline__ int tr_base(int lane, int cb) {
+  constexpr int RB = 2 * D;
+  const int row_l = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int chunk_l = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  return row_l * RB + (((4 * cb + chunk_l) ^ rm_swz<D>(row_l)) << 4) + 8 * (lane & 1);
+}
+
 template <int D>
 __device__ __forceinline__ int k_swz(int r) {
   return D == 128 ? (r & 15) : ((r >> 1) & 7);

@@ -205,8 +205,8 @@ int fa_fwd_kv_split_packed(const void* q, const void* k, const void* vt, size_t 
  * written by the forward).  Outputs dq (q's layout), dk, dv (k's layout)
  * in grad_dtype (FA_F32 or in_dtype); they must not overlap any input, each
  * other or the workspace.  workspace: device memory of
- * fa_bwd_workspace_bytes() bytes, 16-byte aligned (row sums D, L * log2(e) and packed
- * transposes of Q, dO and K); contents on entry do not matter.  Allocates
+ * fa_bwd_workspace_bytes() bytes, 16-byte aligned (the rows' D and
+ * L * log2(e), fp32); contents on entry do not matter.  Allocates
  * nothing; errors as fa_fwd plus FA_ERR_WORKSPACE, FA_ERR_DTYPE for fp32
  * inputs. */
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int in_dtype);
