@@ -95,7 +95,13 @@ struct VtParams {
 
 template <typename T, int D, bool VARLEN>
 __global__ __launch_bounds__(256) void fa_vt_pack(VtParams p) {
-  // One workgroup per tile: blockIdx.x = (b * Hkv + kvh) * ntiles + t.
+  // One workgroup per tile: blockIdx.x = (b * Hkv + kvh) * ntiles + t.  The
+  // tile's 64 V rows go straight into LDS (row-major, rm_swz layout; rows
+  // past the sequence end read zeros); transposing LDS reads then give each
+  // lane 8 keys of one column in exactly the V^T row order (the order of the
+  // P.V operand), which it stores as one 16-byte chunk.
+  constexpr int CPR = D / 8, RB = 2 * D, DB = D / 32;
+  constexpr int LOADS = 64 * CPR / 256;
   const int t = blockIdx.x % p.ntiles;
   const int kvh = (blockIdx.x / p.ntiles) % p.Hkv;
   const int b = blockIdx.x / p.ntiles / p.Hkv;
@@ -106,33 +112,33 @@ __global__ __launch_bounds__(256) void fa_vt_pack(VtParams p) {
   }
   const int kb = t * 64;
   if (kb >= len) return;
-  __shared__ __attribute__((aligned(16))) T vt[64 * D];   // V rows of the tile
+  __shared__ __attribute__((aligned(16))) char vl[64 * RB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const T* src = (const T*)p.v + (VARLEN ? (long long)seq0 * p.kv_rs : (long long)b * p.kv_bs) +
-                 (long long)kvh * p.kv_hs;
-  constexpr int CPR = D / 8;
+                 (long long)kvh * p.kv_hs + (long long)kb * p.kv_rs;
+  const uint32_t rs_bytes = (uint32_t)p.kv_rs * 2;
+  const int rows = __builtin_amdgcn_readfirstlane(min(64, len - kb));
+  const rsrc_t r = make_rsrc(src, (uint32_t)rows * rs_bytes);
 #pragma unroll
-  for (int i = 0; i < 64 * CPR / 256; ++i) {
-    const int q = threadIdx.x + 256 * i;
-    const int r = q / CPR, c = q % CPR;
-    u32x4 x = {0, 0, 0, 0};
-    if (kb + r < len) x = *(const u32x4*)(src + (long long)(kb + r) * p.kv_rs + c * 8);
-    *(u32x4*)(vt + r * D + c * 8) = x;
+  for (int i = 0; i < LOADS; ++i) {
+    const int pch = tid + 256 * i;
+    const int row = pch / CPR, pc = pch % CPR;
+    lds_load16(r, vl + (256 * i + 64 * wave) * 16, row * rs_bytes + ((pc ^ rm_swz<D>(row)) << 4));
   }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
+  // Pair (16-key group g, column block cb): lane L holds column 32 cb + L % 32,
+  // positions 8 (L / 32) .. +7 of group g, i.e. chunk 2 g + L / 32 of that
+  // V^T row.
   char* dst = (char*)p.ws + (long long)blockIdx.x * (128LL * D);
 #pragma unroll
-  for (int i = 0; i < 8 * D / 256; ++i) {
-    const int q = threadIdx.x + 256 * i;
-    const int d = q % D, c = q / D;             // output row d, 16-byte chunk c
-    uint16_t v8[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int key = 16 * (c >> 1) + vt_key(8 * (c & 1) + j);
-      v8[j] = __builtin_bit_cast(uint16_t, vt[key * D + d]);
-    }
-    u32x4 w = {v8[0] | (uint32_t)v8[1] << 16, v8[2] | (uint32_t)v8[3] << 16,
-               v8[4] | (uint32_t)v8[5] << 16, v8[6] | (uint32_t)v8[7] << 16};
-    *(u32x4*)(dst + d * 128 + c * 16) = w;
+  for (int i = 0; i < DB; ++i) {
+    const int pair = wave + 4 * i;            // 4 * DB pairs over 4 waves
+    const int g = pair & 3, cb = pair >> 2;
+    const int tb = tr_base<D>(lane, cb);
+    const u32x4 x = lds_read_tr<u32x4>(vl + tb + 16 * g * RB, vl + (tb ^ 32) + (16 * g + 8) * RB);
+    *(u32x4*)(dst + (32 * cb + (lane & 31)) * 128 + (2 * g + (lane >> 5)) * 16) = x;
   }
 }
 
