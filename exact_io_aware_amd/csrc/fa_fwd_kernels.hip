@@ -633,15 +633,16 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
   using OT = typename std::conditional<OUT_F32, float, T>::type;
   constexpr int OB = sizeof(OT);
   constexpr int SLOT = 4 * TILE_BYTES / NW;          // staging bytes per wave
-  static_assert(NW == 8, "two staging slots per tile buffer");
+  constexpr int PER_BUF = TILE_BYTES / SLOT;         // staging slots per tile buffer
+  static_assert(NW % 4 == 0 && PER_BUF * SLOT == TILE_BYTES, "staging slots");
   constexpr int DBP = (DB < SLOT / (32 * 32 * OB)) ? DB : SLOT / (32 * 32 * OB);
   constexpr int RP = DBP * 32 * OB;                  // staged bytes per row
   constexpr int CPO = RP / 16;                       // 16-byte chunks per staged row
   constexpr int RPI = 64 / CPO;                      // rows per store instruction
   static_assert(DBP >= 1 && DB % DBP == 0 && 32 * RP <= SLOT, "staging slot size");
-  char* slot = (wave >> 1) == 0 ? k_lds0 : (wave >> 1) == 1 ? k_lds1
-             : (wave >> 1) == 2 ? v_lds0 : v_lds1;
-  slot += (wave & 1) * SLOT;
+  const int sbuf = wave / PER_BUF;
+  char* slot = sbuf == 0 ? k_lds0 : sbuf == 1 ? k_lds1 : sbuf == 2 ? v_lds0 : v_lds1;
+  slot += (wave % PER_BUF) * SLOT;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float ell_t = halves_sum(ell[qb]);
