@@ -417,15 +417,13 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
   auto mask = [&](int kb, f32x16 (&s)[QB]) __attribute__((always_inline)) {
     if ((CAUSAL && kb + 31 > row0 + off) || (kb + 32 > len_k)) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        // Element e holds key kb + 4*hf + 8*(e/4) + e%4; it is visible while
-        // that key is below len_k and, causal, at most the row's position.
-        const int qpos = row0 + 32 * qb + l32 + off;
-        const int lim = (CAUSAL ? min(len_k, qpos + 1) : len_k) - kb - 4 * hf;
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (8 * (e >> 2) + (e & 3) >= lim) s[qb][e] = -__builtin_inff();
-      }
+        for (int e = 0; e < 16; ++e) {
+          const int key = kb + 8 * (e >> 2) + 4 * hf + (e & 3);
+          if ((CAUSAL && key > row0 + 32 * qb + l32 + off) || key >= len_k)
+            s[qb][e] = -__builtin_inff();
+        }
     }
   };
 
