@@ -51,7 +51,7 @@ struct BwdParams {
   void* dq; void* dk; void* dv;
   const int* cu_seqlens;
   int B, N, Hq, Hkv, G;
-  int hp, rows_per_wg, n_rblocks, n_hgroups;     // dq grid (as the forward)
+  int hp, rows_per_wg, n_rblocks, n_hgroups, xcd_remap;   // dq grid (as the forward)
   int kv_blocks;                                 // dV, dK: 256-key blocks per sequence
   float scale, scale_log2;
   long long q_bs, q_hs, q_rs;     // q, o, dO, dQ element strides
@@ -386,8 +386,21 @@ __global__ __launch_bounds__(512, 2) void fa_bwd_dq(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
 
-  const int unit = blockIdx.x / p.n_rblocks;
-  int rb = blockIdx.x - unit * p.n_rblocks;
+  // Workgroups are dealt round-robin over the 8 XCDs (workgroup j on XCD
+  // j % 8).  With xcd_remap, XCD x takes the units u with u % 8 == x, each
+  // unit's row blocks consecutively (as the forward kernel): a unit's K/V
+  // stays in one XCD's L2, and every XCD gets the same mix of long and
+  // short causal row blocks.
+  int unit, rb;
+  if (p.xcd_remap) {
+    const int idx = blockIdx.x >> 3;
+    const int k = idx / p.n_rblocks;
+    rb = idx - k * p.n_rblocks;
+    unit = 8 * k + (blockIdx.x & 7);
+  } else {
+    unit = blockIdx.x / p.n_rblocks;
+    rb = blockIdx.x - unit * p.n_rblocks;
+  }
   if (CAUSAL) rb = p.n_rblocks - 1 - rb;     // longest row blocks first
   const int b = unit / p.n_hgroups;
   const int hgrp = unit - b * p.n_hgroups;
@@ -658,6 +671,7 @@ int launch_bwd(const BwdArgs& a, void* stream) {
   const Plan plan = make_plan(a.B, a.Hq, a.Hkv, a.N, a.d, a.in_dtype);
   p.hp = plan.hp; p.rows_per_wg = plan.rows_per_wg; p.n_rblocks = plan.n_rblocks;
   p.n_hgroups = plan.n_hgroups;
+  p.xcd_remap = ((uint64_t)a.B * plan.n_hgroups) % 8 == 0;
   p.kv_blocks = (a.N + 255) / 256;
   p.scale = a.scale; p.scale_log2 = a.scale * kLog2e;
   const long long d = a.d;
