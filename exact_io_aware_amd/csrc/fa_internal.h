@@ -105,13 +105,13 @@ struct LaunchArgs {
   int in_dtype, out_dtype;
   // Split-KV (16-bit inputs): n_splits > 1 writes partial results to o_part /
   // lse_part (split_workspace_bytes) and merges them into o / lse.
-  int n_splits;
-  float* o_part;
-  float* lse_part;
+  int n_splits = 0;
+  float* o_part = nullptr;
+  float* lse_part = nullptr;
   // Block-sparse (16-bit inputs): uint8 mask [mask_batches][mask_heads]
   // [ceil(N/64)][ceil(Nk/64)], or nullptr.
-  const uint8_t* block_mask;
-  int mask_batches, mask_heads;
+  const uint8_t* block_mask = nullptr;
+  int mask_batches = 0, mask_heads = 0;
 };
 
 // Bytes of the split-KV partials: n_splits x B x Hq x Nq rows of d fp32
