@@ -118,6 +118,42 @@ def cpu_baseline(w, heads: int):
                       f"{dt:.2f} s wall"}
 
 
+def cpu_baseline_bwd(w, heads: int):
+    """The oracle's backward (float64 numpy), as it stands, on the first
+    query heads of the first sequence (one K/V group at a time), over a
+    process pool; rate under the backward's FLOP convention (2.5 x the
+    forward's)."""
+    import numpy as np
+
+    import oracle
+    import workloads
+    G = w["Hq"] // w["Hkv"]
+    if heads <= 0:
+        heads = 2 * G
+    heads = max(G, min(w["Hq"], (heads // G) * G))
+    q, k, v = (workloads.to_f64(w[x], w["dtype"]) for x in "qkv")
+    if w["cu_seqlens"] is not None:
+        n0 = int(w["cu_seqlens"][1])
+        qs = np.ascontiguousarray(q[:n0, :heads].transpose(1, 0, 2)[None])
+        ks = np.ascontiguousarray(k[:n0, :heads // G].transpose(1, 0, 2)[None])
+        vs = np.ascontiguousarray(v[:n0, :heads // G].transpose(1, 0, 2)[None])
+    else:
+        n0 = w["N"]
+        qs = np.ascontiguousarray(q[:1, :heads])
+        ks = np.ascontiguousarray(k[:1, :heads // G])
+        vs = np.ascontiguousarray(v[:1, :heads // G])
+    do = np.random.default_rng(w["seed"] + 100).standard_normal(qs.shape)
+    workers = oracle.default_workers()
+    t0 = time.perf_counter()
+    oracle.attention_backward(qs, ks, vs, do, causal=w["causal"], scale=w["scale"],
+                              workers=workers)
+    dt = time.perf_counter() - t0
+    fl = 2.5 * heads * oracle.unit_flops(n0, w["d"], w["causal"])
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "sample": f"backward of 1 sequence ({n0} tokens) x {heads} query heads of "
+                      f"{w['name']}, float64 numpy, {dt:.2f} s wall"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -298,7 +334,9 @@ def main():
         torch.cuda.synchronize()
         rec["copy_calibration_bytes"] = n * 4
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_heads)
+        rec["cpu_baseline"] = (cpu_baseline_bwd(w, args.cpu_sample_heads)
+                               if args.which == "bwd" else
+                               cpu_baseline(w, args.cpu_sample_heads))
     print(json.dumps(rec), flush=True)
 
 
