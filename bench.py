@@ -308,7 +308,9 @@ def main():
                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                     "traffic": traffic_for(kname, w["name"]) if args.which == "fwd" else None}
     rec = {
-        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": (METRIC if args.which == "fwd" and w["name"] == "gqa_bf16" else
+                   f"attention {args.which} TFLOP/s at 1 MI355X (% of MFMA peak), {w['name']}"),
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w["dtype"], "data": "synthetic",
@@ -316,7 +318,7 @@ def main():
                    "N": w["N"], "Nk": Nk, "d": w["d"], "causal": w["causal"],
                    "out_dtype": args.out_dtype, "pass": args.which,
                    "kernel": kname if args.which == "fwd" else
-                   "fa_bwd (delta, transposes, dkdv, dq)",
+                   "fa_bwd (fa_bwd_delta, fa_bwd_dkdv dV and dK, fa_bwd_dq)",
                    "algorithmic_flop_per_step": flop},
         "roofline": roofline,
         "timing": {"attn_launch_ms_avg": round(avg_launch_ms, 4),
