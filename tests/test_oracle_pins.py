@@ -312,3 +312,14 @@ def test_bwd_pins_catch_planted_mistake(name, monkeypatch):
         if worst > C.TOL:
             break
     assert worst > C.TOL, f"no pin caught the planted mistake {name}"
+
+
+def test_flop_and_visibility_counts():
+    """unit_flops and visible_keys against counting the visible (query,
+    key) pairs one by one."""
+    for n in (1, 2, 7, 33):
+        for causal in (False, True):
+            vis = [[c <= r or not causal for c in range(n)] for r in range(n)]
+            for r in range(n):
+                assert oracle.visible_keys(r, n, causal) == sum(vis[r])
+            assert oracle.unit_flops(n, 64, causal) == 4.0 * 64 * sum(map(sum, vis))
