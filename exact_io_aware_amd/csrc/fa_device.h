@@ -49,6 +49,9 @@ template <> struct Ops<__bf16> {
     bf16x2 r = __builtin_convertvector(f, bf16x2);
     return __builtin_bit_cast(uint32_t, r);
   }
+  // Row sums of P are taken from the fp32 values (bf16 rounding is too
+  // coarse for the logsumexp).
+  static constexpr bool kSumRounded = false;
 };
 
 template <> struct Ops<_Float16> {
@@ -60,6 +63,13 @@ template <> struct Ops<_Float16> {
     f32x2 f = {lo, hi};
     f16x2 r = __builtin_convertvector(f, f16x2);
     return __builtin_bit_cast(uint32_t, r);
+  }
+  // Row sums of P may be taken from the packed fp16 values: acc + lo + hi
+  // in one v_dot2_f32_f16 (products with 1.0 are exact, the sum is fp32).
+  static constexpr bool kSumRounded = true;
+  static __device__ __forceinline__ float sum2(uint32_t packed, float acc) {
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed), ones, acc, false);
   }
 };
 

@@ -433,21 +433,37 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
   // maximum, O and ell are rescaled by exp2(m_old - m_new) and P is formed
   // again (settle).  The rescale is exact, so the result does not depend on
   // when m moves.
+  //
+  // The block's row sum: with bf16 P (8 significant bits) it is taken from
+  // the fp32 P, as a tree of adds (short dependency chains); with fp16 P it
+  // is taken from the rounded P itself, two values per v_dot2 (relative
+  // error at most 2^-11 per value, so L moves by at most ~4.9e-4, and O is
+  // the exact mean of V under the weights the P.V product uses).
   auto form_p = [&](const f32x16 (&s)[QB], uint32_t (&pk)[QB][8], float (&lsum)[QB],
                     bool live) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       // A block past the wave's last one gets m = +inf: P = 0 and sum 0.
       const float m = live ? m_run[qb] : __builtin_inff();
-      float acc = 0.0f;
+      float t[8];
 #pragma unroll
       for (int e = 0; e < 16; e += 2) {
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][e], sl2, -m));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][e + 1], sl2, -m));
-        acc += p0 + p1;
         pk[qb][e >> 1] = Ops<T>::pack(p0, p1);
+        if constexpr (!Ops<T>::kSumRounded) t[e >> 1] = p0 + p1;
       }
-      lsum[qb] = acc;
+      if constexpr (Ops<T>::kSumRounded) {
+        float a = 0.0f, c = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          a = Ops<T>::sum2(pk[qb][j], a);
+          c = Ops<T>::sum2(pk[qb][j + 1], c);
+        }
+        lsum[qb] = a + c;
+      } else {
+        lsum[qb] = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
+      }
     }
   };
   auto settle = [&](const f32x16 (&s)[QB], uint32_t (&pk)[QB][8], float (&lsum)[QB])
@@ -524,17 +540,21 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
     // MFMA (32 cycles in the matrix pipe) followed by a few independent
     // softmax instructions and the next reads, so the wave's exp/FMA work
     // runs while its own MFMAs execute.
+    // d = 64 has half the MFMAs per block for the same softmax work, so
+    // more vector instructions go with each MFMA.
+    constexpr int QK_VALU = D == 128 ? 2 : 5, QK_LDS = 2;
+    constexpr int PV_VALU = D == 128 ? 3 : 6;
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);       // 4 LDS reads
 #pragma unroll
     for (int i = 0; i < DC * QB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // 1 MFMA (scores)
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);     // 3 VALU
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);     // 3 LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x002, QK_VALU, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, QK_LDS, 0);
     }
 #pragma unroll
     for (int i = 0; i < 2 * DB * QB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // 1 MFMA (P.V)
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);     // 4 VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, PV_VALU, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // 1 LDS read
     }
     settle(s_cur, pk_cur, lsum);
