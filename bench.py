@@ -318,7 +318,7 @@ def main():
                    "N": w["N"], "Nk": Nk, "d": w["d"], "causal": w["causal"],
                    "out_dtype": args.out_dtype, "pass": args.which,
                    "kernel": kname if args.which == "fwd" else
-                   "fa_bwd (fa_bwd_delta, fa_bwd_dkdv dV and dK, fa_bwd_dq)",
+                   "fa_bwd (fa_bwd_delta, fa_bwd_dkdv, fa_bwd_dq)",
                    "algorithmic_flop_per_step": flop},
         "roofline": roofline,
         "timing": {"attn_launch_ms_avg": round(avg_launch_ms, 4),

@@ -12,18 +12,16 @@
 //
 // gfx950 mapping (our design):
 //  * fa_bwd_delta: D_r, one 32-lane group per row.
-//  * fa_bwd_dkdv<MODE>: a workgroup of 8 waves owns 256 keys of one K/V head
-//    (each wave 32 keys, its K (and V) rows in registers as MFMA B operands)
-//    and streams 64-row query tiles (Q and dO, row-major) of every query
-//    head of the group.  The dV kernel (MODE 0) reads Q by rows (A operand
-//    of S = Q K^T) and dO transposed (A operand of dV^T += dO^T P); the dK
-//    kernel (MODE 1) reads Q and dO by rows (S and dP = dO V^T) and Q
-//    transposed (dK^T += Q^T dS).  S's accumulator puts one key per lane
-//    column, which is exactly the B-operand layout of P and dS for the
-//    gradient products, and the transposing LDS reads deliver the query
-//    rows in that accumulator's order.  Split in two, S is formed twice but
-//    neither kernel runs out of registers (fused, K, V, two score blocks and
-//    two accumulators do).  No atomics.
+//  * fa_bwd_dkdv: a workgroup of 8 waves owns 256 keys of one K/V head
+//    (each wave 32 keys: its K rows in registers, its V rows in LDS, both
+//    read as MFMA B operands) and streams 64-row query tiles (Q and dO,
+//    row-major) of every query head of the group.  Per 32-row block it forms
+//    S = Q K^T and dP = dO V^T (Q, dO read by rows), P and dS, then
+//    dV^T += dO^T P and dK^T += Q^T dS (dO, Q read transposed).  S's
+//    accumulator puts one key per lane column, which is exactly the
+//    B-operand layout of P and dS for the gradient products, and the
+//    transposing LDS reads deliver the query rows in that accumulator's
+//    order.  No atomics.
 //  * fa_bwd_dq: the forward kernel's structure: a wave owns 32 query rows
 //    (Q and dO in registers), streams 64-key tiles of K and V (row-major),
 //    forms S^T = K Q^T and dP^T = V dO^T with one query per lane column, and
@@ -93,12 +91,12 @@ __global__ __launch_bounds__(256) void fa_bwd_delta(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dV (MODE 0) or dK (MODE 1).  One workgroup: 8 waves x 32 keys of K/V head g
-// of sequence b.  The two gradients run as two kernels: fused, the four
-// products' operands and two accumulators exceed one wave's registers.
-//   MODE 0: S = Q K^T, P, dV^T += dO^T P          (tiles Q, dO; L)
-//   MODE 1: S, dP = dO V^T, dS, dK^T += Q^T dS    (tiles Q, dO; L, D)
-template <typename T, int D, bool CAUSAL, bool VARLEN, bool OUT_F32, int MODE>
+// dV and dK in one pass.  One workgroup: 8 waves x 32 keys of K/V head g of
+// sequence b; per 32-row query block: S = Q K^T, P, dP = dO V^T, dS,
+// dV^T += dO^T P, dK^T += Q^T dS (tiles Q, dO; L, D).  With K rows, two
+// score blocks and two 32 x d accumulators in registers there is no room
+// for V as well, so each wave keeps its 32 V rows in LDS (rm_swz layout).
+template <typename T, int D, bool CAUSAL, bool VARLEN, bool OUT_F32>
 __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv(BwdParams p) {
   using vec8 = typename Ops<T>::vec8;
   constexpr int NW = 8, NT = 512;
@@ -116,6 +114,8 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv(BwdParams p) {
   __shared__ __attribute__((aligned(16))) char do_l1[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) float ld_l0[2 * BR];   // L * log2(e), then D
   __shared__ __attribute__((aligned(16))) float ld_l1[2 * BR];
+  // Each wave's 32 V rows.
+  __shared__ __attribute__((aligned(16))) char v_own[NW * 32 * RB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -142,9 +142,9 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv(BwdParams p) {
 
   const long long kvbase = (VARLEN ? (long long)seq0 * p.kv_rs : (long long)b * p.kv_bs) +
                            (long long)g * p.kv_hs;
-  // Own K (and V) rows as B operands: lane (l32, hf) holds row key,
-  // columns 16*dc + 8*hf .. +7.
-  vec8 kf[DC], vf[MODE == 1 ? DC : 1];
+  // Own K and V rows as B operands: lane (l32, hf) holds row key, columns
+  // 16*dc + 8*hf .. +7 (V only until it is stored to LDS).
+  vec8 kf[DC], vf[DC];
   {
     const int krows = __builtin_amdgcn_readfirstlane(max(0, min(32, len - kw0)));
     const long long at = kvbase + (long long)min(kw0, len) * p.kv_rs;
@@ -154,12 +154,10 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv(BwdParams p) {
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
       kf[dc] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(rk, ko + dc * 32, 0, 0));
-    if (MODE == 1) {
-      const rsrc_t rv = make_rsrc((const T*)p.v + at, bytes);
+    const rsrc_t rv = make_rsrc((const T*)p.v + at, bytes);
 #pragma unroll
-      for (int dc = 0; dc < DC; ++dc)
-        vf[dc] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(rv, ko + dc * 32, 0, 0));
-    }
+    for (int dc = 0; dc < DC; ++dc)
+      vf[dc] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(rv, ko + dc * 32, 0, 0));
   }
 
   // Tile fill offsets (row-major, rm_swz).
@@ -172,13 +170,18 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv(BwdParams p) {
     roff[i] = r * q_rs_bytes + ((pc ^ rm_swz<D>(r)) << 4);
   }
   // Operand read addresses: by rows (query l32 of a 32-row block, 16-byte
-  // chunk 2 dc + hf) and transposed (column block db).
-  int raddr[DC];
+  // chunk 2 dc + hf) and transposed (column block db).  The chunk index's dc
+  // (db) bits lie above the bits the lane's own terms set, so the address
+  // of chunk dc is raddr0 ^ 32 dc and that of column block db is
+  // tbase0 ^ 64 db: two registers instead of DC + DB.
+  const int raddr0 = l32 * RB + ((hf ^ rm_swz<D>(l32)) << 4);
+  const int tbase0 = tr_base<D>(lane, 0);
+  // The wave's V rows go to its LDS slot, row l32 chunk 2 dc + hf where a
+  // row read of a tile finds it; only this wave reads them, after the
+  // loop's first barrier.
+  char* const vw = v_own + wave * 32 * RB;
 #pragma unroll
-  for (int dc = 0; dc < DC; ++dc) raddr[dc] = l32 * RB + (((2 * dc + hf) ^ rm_swz<D>(l32)) << 4);
-  int tbase[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) tbase[db] = tr_base<D>(lane, db);
+  for (int dc = 0; dc < DC; ++dc) *(vec8*)(vw + (raddr0 ^ (32 * dc))) = vf[dc];
 
   // Iterations: (query head hh of the group, 64-row query tile t).
   const int t_first = CAUSAL ? kwg / BR : 0;
@@ -210,16 +213,20 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv(BwdParams p) {
       const rsrc_t rl = make_rsrc(p.lse2 + lrow, (uint32_t)rows * 4);
       if (lane < 16) {
         lds_load16(rl, (char*)ldl, lane * 16);
-      } else if (MODE == 1 && lane < 32) {
+      } else if (lane < 32) {
         const rsrc_t rd = make_rsrc(p.delta + lrow, (uint32_t)rows * 4);
         lds_load16(rd, (char*)ldl, (lane - 16) * 16);
       }
     }
   };
 
-  f32x16 acc[DB];
+  // dK^T and dV^T: column block db holds d rows 32 db .. 32 db + 31.
+  f32x16 acc_k[DB], acc_v[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  for (int db = 0; db < DB; ++db) {
+    acc_k[db] = f32x16{};
+    acc_v[db] = f32x16{};
+  }
   const float sl2 = p.scale_log2;
 
   // One 32-row query block (half hb of the tile in the given buffers).
@@ -230,42 +237,44 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv(BwdParams p) {
     // with no keys, adds nothing.
     if (!wave_live || (CAUSAL && qr0 + 31 < kw0)) return;
     __builtin_amdgcn_sched_barrier(0);
-    // S = Q K^T (and dP = dO V^T): element e of lane (key, hf) is query row
+    // Per-block copies of the address bases, opaque to the compiler, so the
+    // XOR-derived addresses are formed here and not kept across the loop.
+    int ra = raddr0, tb = tbase0;
+    asm volatile("" : "+v"(ra), "+v"(tb));
+    // S = Q K^T and dP = dO V^T: element e of lane (key, hf) is query row
     // qr0 + 8*(e/4) + 4*hf + e%4.
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
-      const vec8 a = *(const vec8*)(ql + hb * HALF + raddr[dc]);
+      const vec8 a = *(const vec8*)(ql + hb * HALF + (ra ^ (32 * dc)));
       s = Ops<T>::mfma(a, kf[dc], s);
     }
-    if (MODE == 1) {
 #pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-        const vec8 a = *(const vec8*)(dol + hb * HALF + raddr[dc]);
-        dp = Ops<T>::mfma(a, vf[dc], dp);
-      }
+    for (int dc = 0; dc < DC; ++dc) {
+      const vec8 a = *(const vec8*)(dol + hb * HALF + (ra ^ (32 * dc)));
+      const vec8 bv = *(const vec8*)(vw + (ra ^ (32 * dc)));
+      dp = Ops<T>::mfma(a, bv, dp);
     }
-    // Operand reads two MFMAs ahead of their use, one per MFMA.
-    constexpr int NM = MODE == 1 ? 2 * DC : DC;
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    // Operand reads two MFMAs ahead of their use (the dP MFMAs read two
+    // operands each).
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int i = 0; i < NM - 2; ++i) {
+    for (int i = 0; i < 2 * DC - 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_sched_barrier(0);
-    // P (and dS); the masks are tested only in blocks that cross the
-    // diagonal or an end of the sequence.
-    uint32_t pk[8];
+    // P and dS, packed to the input type (pkp, pkd); the masks are tested
+    // only in blocks that cross the diagonal or an end of the sequence.
+    uint32_t pkp[8], pkd[8];
     auto form = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int rl = 32 * hb + 8 * g4 + 4 * hf;   // row within the tile
         const f32x4 L4 = *(const f32x4*)(ldl + rl);
-        f32x4 D4 = f32x4{};
-        if (MODE == 1) D4 = *(const f32x4*)(ldl + BR + rl);
-        float pe[4];
+        const f32x4 D4 = *(const f32x4*)(ldl + BR + rl);
+        float pe[4], pp[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int e = 4 * g4 + j;
@@ -274,10 +283,13 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv(BwdParams p) {
             const int qr = qr0 + 8 * g4 + 4 * hf + j;
             if (qr >= len || key >= len || (CAUSAL && key > qr)) pv = 0.0f;
           }
-          pe[j] = MODE == 1 ? pv * (dp[e] - D4[j]) : pv;
+          pp[j] = pv;
+          pe[j] = pv * (dp[e] - D4[j]);
         }
-        pk[2 * g4] = Ops<T>::pack(pe[0], pe[1]);
-        pk[2 * g4 + 1] = Ops<T>::pack(pe[2], pe[3]);
+        pkp[2 * g4] = Ops<T>::pack(pp[0], pp[1]);
+        pkp[2 * g4 + 1] = Ops<T>::pack(pp[2], pp[3]);
+        pkd[2 * g4] = Ops<T>::pack(pe[0], pe[1]);
+        pkd[2 * g4 + 1] = Ops<T>::pack(pe[2], pe[3]);
       }
     };
     if (qr0 + 31 >= len || kw0 + 31 >= len || (CAUSAL && kw0 + 31 > qr0))
@@ -285,24 +297,27 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv(BwdParams p) {
     else
       form(BoolTag<false>{});
     __builtin_amdgcn_sched_barrier(0);
-    // dV^T += dO^T P, or dK^T += Q^T dS, over the block's two 16-row chunks
-    // (dO or Q read transposed from its tile).
-    const char* tl = MODE == 1 ? ql : dol;
+    // dK^T += Q^T dS and dV^T += dO^T P over the block's two 16-row chunks
+    // (Q and dO read transposed from their tiles).
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
-      const u32x4 pb = {pk[4 * kc], pk[4 * kc + 1], pk[4 * kc + 2], pk[4 * kc + 3]};
-      const vec8 pf = __builtin_bit_cast(vec8, pb);
+      const u32x4 db4 = {pkd[4 * kc], pkd[4 * kc + 1], pkd[4 * kc + 2], pkd[4 * kc + 3]};
+      const u32x4 pb4 = {pkp[4 * kc], pkp[4 * kc + 1], pkp[4 * kc + 2], pkp[4 * kc + 3]};
+      const vec8 dsf = __builtin_bit_cast(vec8, db4), pf = __builtin_bit_cast(vec8, pb4);
       const int r0 = 32 * hb + 16 * kc;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const vec8 ta = lds_read_tr<vec8>(tl + tbase[db] + r0 * RB,
-                                          tl + (tbase[db] ^ 32) + (r0 + 8) * RB);
-        acc[db] = Ops<T>::mfma(ta, pf, acc[db]);
+        const int t0 = tb ^ (64 * db), t1 = tb ^ (64 * db + 32);
+        const vec8 qa = lds_read_tr<vec8>(ql + t0 + r0 * RB, ql + t1 + (r0 + 8) * RB);
+        acc_k[db] = Ops<T>::mfma(qa, dsf, acc_k[db]);
+        const vec8 da = lds_read_tr<vec8>(dol + t0 + r0 * RB, dol + t1 + (r0 + 8) * RB);
+        acc_v[db] = Ops<T>::mfma(da, pf, acc_v[db]);
       }
     }
+    // Gradient MFMAs, two transposing reads each.
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int i = 0; i < 2 * DB - 2; ++i) {
+    for (int i = 0; i < 4 * DB - 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
@@ -342,23 +357,25 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv(BwdParams p) {
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
-  // dK = scale * (dK^T)^T, or dV: lane = key, rows 32*db + 8*g4 + 4*hf + 0..3.
-  if (key < len) {
+  // dK = scale * (dK^T)^T and dV: lane = key, rows 32*db + 8*g4 + 4*hf + 0..3.
+  auto store = [&](const f32x16 (&a)[DB], void* out, float f) __attribute__((always_inline)) {
     const long long row = kvbase + (long long)key * p.kv_rs;
-    void* out = MODE == 1 ? p.dk : p.dv;
-    const float f = MODE == 1 ? p.scale : 1.0f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = 32 * db + 8 * g4 + 4 * hf;
-        const float a0 = acc[db][4 * g4] * f, a1 = acc[db][4 * g4 + 1] * f;
-        const float a2 = acc[db][4 * g4 + 2] * f, a3 = acc[db][4 * g4 + 3] * f;
+        const float a0 = a[db][4 * g4] * f, a1 = a[db][4 * g4 + 1] * f;
+        const float a2 = a[db][4 * g4 + 2] * f, a3 = a[db][4 * g4 + 3] * f;
         if (OUT_F32)
           *(f32x4*)((float*)out + row + d0) = f32x4{a0, a1, a2, a3};
         else
           *(u32x2*)((T*)out + row + d0) = u32x2{Ops<T>::pack(a0, a1), Ops<T>::pack(a2, a3)};
       }
+  };
+  if (key < len) {
+    store(acc_k, p.dk, p.scale);
+    store(acc_v, p.dv, 1.0f);
   }
 }
 
@@ -593,12 +610,11 @@ typedef void (*BwdFn)(BwdParams);
 
 struct BwdVariant {
   int in_dtype, d, causal, varlen, grad_f32;
-  BwdFn dv, dk, dq;
+  BwdFn dkdv, dq;
 };
 
 #define FA_BV(T, DT, D, C, VL, OF)                                                     \
-  {DT, D, C, VL, OF, fa_bwd_dkdv<T, D, (C != 0), (VL != 0), (OF != 0), 0>,               \
-   fa_bwd_dkdv<T, D, (C != 0), (VL != 0), (OF != 0), 1>,                                 \
+  {DT, D, C, VL, OF, fa_bwd_dkdv<T, D, (C != 0), (VL != 0), (OF != 0)>,                  \
    fa_bwd_dq<T, D, (C != 0), (VL != 0), (OF != 0)>}
 #define FA_BV_ALL(T, DT, D)                                                             \
   FA_BV(T, DT, D, 0, 0, 0), FA_BV(T, DT, D, 0, 0, 1), FA_BV(T, DT, D, 0, 1, 0),           \
@@ -689,8 +705,7 @@ int launch_bwd(const BwdArgs& a, void* stream) {
                       s) != hipSuccess)
     return FA_ERR_LAUNCH;
   const unsigned g1 = (unsigned)((uint64_t)a.B * a.Hkv * p.kv_blocks);
-  if (hipLaunchKernel((const void*)var->dv, dim3(g1), dim3(512), args, 0, s) != hipSuccess ||
-      hipLaunchKernel((const void*)var->dk, dim3(g1), dim3(512), args, 0, s) != hipSuccess)
+  if (hipLaunchKernel((const void*)var->dkdv, dim3(g1), dim3(512), args, 0, s) != hipSuccess)
     return FA_ERR_LAUNCH;
   if (hipLaunchKernel((const void*)var->dq, dim3((unsigned)plan.total_wg), dim3(512), args, 0,
                       s) != hipSuccess)
