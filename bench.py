@@ -188,8 +188,9 @@ def main():
     bm_np = w.get("block_mask")
     flop = fa.flops(w["Hq"], w["d"], lengths, w["causal"], lengths_k, block_mask=bm_np)
     dt_code = {"fp32": fa.FA_F32, "fp16": fa.FA_F16, "bf16": fa.FA_BF16}[w["dtype"]]
-    kname = fa.kernel_name(dt_code, w["d"], w["causal"], cu is not None,
-                           fa.FA_F32 if args.out_dtype == "fp32" else dt_code)
+    kname = fa.kernel_name_kv(dt_code, w["d"], w["causal"], cu is not None,
+                              fa.FA_F32 if args.out_dtype == "fp32" else dt_code,
+                              w["Hq"], w["Hkv"], w["N"])
     stream = torch.cuda.current_stream(dev)
     packed = w["dtype"] != "fp32"
     # Decode: the packed V^T is the KV cache's layout, filled once when the

@@ -6,7 +6,7 @@ There is no CPU or PyTorch fallback: if the library is missing or the device
 is not gfx950, calls raise.
 """
 from ._lib import (  # noqa: F401
-    FA_BF16, FA_F16, FA_F32, STATUS, kernel_name, load, status_string,
+    FA_BF16, FA_F16, FA_F32, STATUS, kernel_name, kernel_name_kv, load, status_string,
     bwd_workspace_bytes, num_splits, split_workspace_bytes, supported, version,
     workspace_bytes,
 )

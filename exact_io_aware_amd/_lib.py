@@ -65,6 +65,8 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_check.restype = i
     lib.fa_kernel_name.argtypes = [i, i, i, i, i]
     lib.fa_kernel_name.restype = ctypes.c_char_p
+    lib.fa_kernel_name_kv.argtypes = [i, i, i, i, i, i, i, i]
+    lib.fa_kernel_name_kv.restype = ctypes.c_char_p
     lib.fa_supported.argtypes = [i, i, i]
     lib.fa_supported.restype = i
     lib.fa_status_string.argtypes = [i]
@@ -85,6 +87,13 @@ def version() -> int:
 
 def kernel_name(in_dtype: int, d: int, causal: bool, varlen: bool, out_dtype: int):
     s = load().fa_kernel_name(in_dtype, d, int(causal), int(varlen), out_dtype)
+    return None if s is None else s.decode()
+
+
+def kernel_name_kv(in_dtype: int, d: int, causal: bool, varlen: bool, out_dtype: int,
+                   Hq: int, Hkv: int, Nq: int):
+    """fa_kernel_name_kv: the kernel fa_fwd_kv runs for this query count."""
+    s = load().fa_kernel_name_kv(in_dtype, d, int(causal), int(varlen), out_dtype, Hq, Hkv, Nq)
     return None if s is None else s.decode()
 
 

@@ -245,6 +245,12 @@ const char* fa_kernel_name(int in_dtype, int d, int causal, int varlen,
   return fa::kernel_name(in_dtype, d, causal, varlen, out_dtype);
 }
 
+const char* fa_kernel_name_kv(int in_dtype, int d, int causal, int varlen, int out_dtype,
+                              int Hq, int Hkv, int Nq) {
+  if (Hkv < 1 || Hq < 1 || Nq < 1) return nullptr;
+  return fa::kernel_name_kv(in_dtype, d, causal, varlen, out_dtype, Hq, Hkv, Nq);
+}
+
 int fa_supported(int in_dtype, int d, int causal) {
   const bool dt = in_dtype == FA_F32 || in_dtype == FA_F16 || in_dtype == FA_BF16;
   return dt && (d == 64 || d == 128) && (causal == 0 || causal == 1);

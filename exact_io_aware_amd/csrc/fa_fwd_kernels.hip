@@ -710,6 +710,306 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
 }
 
 // ---------------------------------------------------------------------------
+// Decode: few query rows per sequence (G * nq <= 32) against a long key /
+// value cache.  The G query heads of a K/V head and their nq rows form one
+// 32-row MFMA block (packed row r = hh * nq + i: head g * G + hh, query i),
+// so one wave covers the whole group for the keys it streams, and the
+// workgroup's 4 waves (one per SIMD, with the whole register file) share
+// out the unit's 64-key tiles (wave w takes tiles w, w + 4, ...).  The work
+// is HBM-bound, so the loads are built for bandwidth: each wave reads its
+// tiles (32 KiB: 64 K rows and the packed V^T tile, both contiguous) with
+// 1 KiB non-temporal loads into registers, one tile ahead, and passes each
+// tile through its own LDS slot to put it in the MFMA operand layouts; no
+// workgroup barrier inside the loop.  Per 32-key block: S^T =
+// K Q^T (Q shared in LDS), the lazy online softmax of fa_fwd_mfma, O^T +=
+// V^T P^T.  At the end the waves' (m, l, O) states are merged through LDS.
+template <typename T, int D, bool CAUSAL, bool VARLEN, bool OUT_F32>
+__global__ __launch_bounds__(256, 1) void fa_decode_mfma(FwdParams p) {
+  using vec8 = typename Ops<T>::vec8;
+  constexpr int NW = 4;
+  constexpr int DB = D / 32, DC = D / 16, CPR = D / 8, RB = D * 2;
+  constexpr int TILE_BYTES = 64 * RB;        // 64 K rows, or one packed V^T tile
+  constexpr int STAGE = 2 * TILE_BYTES;      // K rows then V^T
+  constexpr int LOADS = STAGE / 1024;        // 1 KiB loads per tile
+  constexpr int OS = D + 4;                  // floats per staged O row
+  static_assert(NW * 32 * OS * 4 <= NW * STAGE, "merge area fits the slots");
+  // One tile per wave; after the loop, the waves' O.
+  __shared__ __attribute__((aligned(16))) char slots[NW * STAGE];
+  __shared__ __attribute__((aligned(16))) char q_lds[32 * RB];
+  __shared__ float m_s[NW][32], l_s[NW][32];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hf = lane >> 5;
+
+  int wg = blockIdx.x, split = 0;
+  if (p.n_splits > 1) {
+    split = wg % p.n_splits;
+    wg /= p.n_splits;
+  }
+  const int b = wg / p.Hkv;
+  const int g = wg - b * p.Hkv;
+  int seq0 = 0, len = p.N, seq0_k = 0, len_k = p.Nk;
+  if (VARLEN) {
+    seq0 = p.cu_seqlens[b];
+    len = p.cu_seqlens[b + 1] - seq0;
+    seq0_k = p.cu_seqlens_k[b];
+    len_k = p.cu_seqlens_k[b + 1] - seq0_k;
+  }
+  if (len <= 0) return;                      // uniform: no rows
+  const int nrows = p.G * len;               // packed rows in use (<= 32)
+  const int off = len_k - len;               // row i sees keys c <= i + off
+
+  // Tiles of this workgroup: [t0, t0 + ntl), 64 keys each (the split range
+  // starts on a tile; keys at or past k_stop are masked).
+  const int t0 = split * p.split_tiles;
+  const int k_stop = min(len_k, (split + 1) * p.split_tiles * 64);
+  const int ntl = max(0, (k_stop - 64 * t0 + 63) / 64);
+  const int my_tiles = ntl > wave ? (ntl - wave + NW - 1) / NW : 0;   // wave-uniform
+
+  const long long kvbase = (VARLEN ? (long long)seq0_k * p.kv_rs : (long long)b * p.kv_bs) +
+                           (long long)g * p.kv_hs;
+  const uint32_t kv_rs_bytes = (uint32_t)p.kv_rs * 2;
+  const char* kp = (const char*)((const T*)p.k + kvbase);
+  const char* vtp = (const char*)p.vt + (long long)(b * p.Hkv + g) * p.vt_ntiles * TILE_BYTES;
+
+  // Q block into LDS: thread t fills rows t / CPR (+ 256 / CPR), chunk
+  // t % CPR, with rm_swz (zeros past the group's nrows).
+  for (int q = tid; q < 32 * CPR; q += NW * 64) {
+    const int rr = q / CPR, c = q % CPR;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (rr < nrows) {
+      const int hh = rr / len, i = rr - hh * len;
+      const long long qo = (VARLEN ? (long long)(seq0 + i) * p.q_rs
+                                   : (long long)b * p.q_bs + (long long)i * p.q_rs) +
+                           (long long)(g * p.G + hh) * p.q_hs + 8 * c;
+      v = *(const u32x4*)((const T*)p.q + qo);
+    }
+    *(u32x4*)(q_lds + rr * RB + ((c ^ rm_swz<D>(rr)) << 4)) = v;
+  }
+  __syncthreads();                           // Q block written
+
+  // The cache is read once per call: non-temporal loads (cache policy NT),
+  // which stream through the caches at a higher HBM rate than ordinary
+  // loads (measured on MI355X: ~7.1 against ~6.0 TB/s for a plain read).
+  constexpr int kNT = 2;
+  // Tile j of the wave in registers: load i brings 1 KiB chunk i (lane L:
+  // bytes 16 L of it), first the 64 K rows (row r = position / CPR, chunk
+  // pc), then the V^T tile (row vr = position / 8 of 128 B, chunk vc).
+  // Rows past the sequence end, and tiles past the wave's last, read zeros
+  // (bounded buffers); the loads are issued unconditionally so every path
+  // keeps the same loads in flight.
+  struct Stage { u32x4 x[LOADS]; };
+  auto gload = [&](int j, Stage& st) __attribute__((always_inline)) {
+    const int t = t0 + wave + NW * j;
+    const int kb = 64 * t;
+    const bool in = j < my_tiles;
+    const int rows = __builtin_amdgcn_readfirstlane(in ? max(0, min(len_k - kb, 64)) : 0);
+    const rsrc_t rk = make_rsrc(kp + (long long)min(kb, len_k) * kv_rs_bytes,
+                                (uint32_t)rows * kv_rs_bytes);
+    const rsrc_t rv = make_rsrc(vtp + (long long)(in ? t : 0) * TILE_BYTES,
+                                in ? (uint32_t)TILE_BYTES : 0u);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int q = 64 * i + lane;
+      if (i < TILE_BYTES / 1024) {
+        const int r = q / CPR, pc = q % CPR;
+        st.x[i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, r * kv_rs_bytes + 16 * pc, 0, kNT));
+      } else {
+        st.x[i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, 16 * (q - TILE_BYTES / 16), 0, kNT));
+      }
+    }
+  };
+  // ... and into the wave's LDS slot, swizzled for the operand reads: K
+  // chunk pc of row r at position pc ^ k_swz(r) (rows of RB bytes); V^T
+  // chunk vc of row vr at vc ^ vt_swz(vr) (rows of 128 bytes).
+  char* const my_slot = slots + wave * STAGE;
+  auto swrite = [&](const Stage& st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int q = 64 * i + lane;
+      if (i < TILE_BYTES / 1024) {
+        const int r = q / CPR, pc = q % CPR;
+        *(u32x4*)(my_slot + r * RB + ((pc ^ k_swz<D>(r)) << 4)) = st.x[i];
+      } else {
+        const int qv = q - TILE_BYTES / 16;
+        const int vr = qv >> 3, vc = qv & 7;
+        *(u32x4*)(my_slot + TILE_BYTES + vr * 128 + ((vc ^ vt_swz(vr)) << 4)) = st.x[i];
+      }
+    }
+  };
+
+  // This lane's packed row (the S^T accumulator column): query qi of head
+  // g * G + (l32 / len); rows past nrows compute on zero Q and are never
+  // stored.
+  const int qi = l32 - (l32 / len) * len;
+  const float sl2 = p.scale_log2;
+  // Read offsets: Q^T chunk dc (B operand, row l32, chunk 2 dc + hf), K
+  // chunk dc (A operand, row 32 h + l32 of the tile, chunk 2 dc + hf), V^T
+  // row 32 db + l32, keys chunk 4 h + 2 kc + hf.
+  const int qaddr0 = l32 * RB + ((hf ^ rm_swz<D>(l32)) << 4);
+  const int kaddr0 = l32 * RB + ((hf ^ k_swz<D>(l32)) << 4);
+  const int vaddr0 = TILE_BYTES + l32 * 128 + ((hf ^ vt_swz(l32)) << 4);
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+  float m_run = kNoMax, ell = 0.0f;
+
+  // Key block h (32 keys from kb) of the tile in the slot.
+  auto compute = [&](int kb, int h) __attribute__((always_inline)) {
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      const vec8 kf = *(const vec8*)(my_slot + 32 * h * RB + (kaddr0 ^ (32 * dc)));
+      const vec8 qf = *(const vec8*)(q_lds + (qaddr0 ^ (32 * dc)));
+      s = Ops<T>::mfma(kf, qf, s);
+    }
+    // Mask where the block crosses the sequence end or (causal) the first
+    // row's last visible key.
+    if (kb + 32 > len_k || (CAUSAL && kb + 31 > off)) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kb + 8 * (e >> 2) + 4 * hf + (e & 3);
+        if (key >= len_k || (CAUSAL && key > qi + off)) s[e] = -__builtin_inff();
+      }
+    }
+    // Lazy online softmax, as in fa_fwd_mfma (P against the reference
+    // maximum; move it only when a lane's partial sum leaves [0, 2^15]).
+    uint32_t pk[8];
+    float lsum;
+    auto form = [&]() __attribute__((always_inline)) {
+      float t[8];
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], sl2, -m_run));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e + 1], sl2, -m_run));
+        pk[e >> 1] = Ops<T>::pack(p0, p1);
+        t[e >> 1] = p0 + p1;
+      }
+      lsum = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
+    };
+    form();
+    if (__any(!(lsum <= kSumLimit))) {
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
+      const float m_new = fmaxf(m_run, halves_max(mx) * sl2);
+      const float alpha = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      ell *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+      m_run = m_new;
+      form();
+    }
+    ell += lsum;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const u32x4 pb = {pk[4 * kc], pk[4 * kc + 1], pk[4 * kc + 2], pk[4 * kc + 3]};
+      const vec8 pf = __builtin_bit_cast(vec8, pb);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const vec8 vf = *(const vec8*)(my_slot + db * 32 * 128 + (vaddr0 ^ (32 * (2 * h + kc))));
+        oacc[db] = Ops<T>::mfma(vf, pf, oacc[db]);
+      }
+    }
+  };
+
+  // Tile j + 1 loads into the registers while tile j, written to the slot,
+  // is computed (its second half only when it holds keys before k_stop).
+  Stage st;
+  gload(0, st);
+  for (int j = 0; j < my_tiles; ++j) {
+    swrite(st);
+    gload(j + 1, st);
+    const int kb = 64 * (t0 + wave + NW * j);
+    compute(kb, 0);
+    if (kb + 32 < k_stop) compute(kb + 32, 1);
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));        // the trailing (zero) loads
+
+  // Merge the waves: each stages its O^T (fp32, row l32, columns
+  // 32 db + 8 g4 + 4 hf + 0..3), m and l per row; the slots are free once
+  // every wave has left the loop.
+  const float ell_t = halves_sum(ell);
+  __syncthreads();
+  auto ostage = [&](int w) __attribute__((always_inline)) -> float* {
+    return (float*)slots + w * 32 * OS;
+  };
+  float* const os_me = ostage(wave);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4)
+      *(f32x4*)(os_me + l32 * OS + 32 * db + 8 * g4 + 4 * hf) =
+          f32x4{oacc[db][4 * g4], oacc[db][4 * g4 + 1], oacc[db][4 * g4 + 2], oacc[db][4 * g4 + 3]};
+  if (hf == 0) {
+    m_s[wave][l32] = m_run;
+    l_s[wave][l32] = ell_t;
+  }
+  __syncthreads();
+  // Thread t: row t / 8, columns (t % 8) * D / 8 ..: L = M + log2 l,
+  // O = sum_w 2^(m_w - M) O_w / l, with M the largest m_w (a wave that saw
+  // no key of the row has l_w = 0 and adds nothing).
+  constexpr int CW = D / 8;
+  const int rr = tid >> 3, c0 = (tid & 7) * CW;
+  if (rr >= nrows) return;
+  float M = kNoMax;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, m_s[w][rr]);
+  float wt[NW], l = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    wt[w] = l_s[w][rr] > 0.0f ? __builtin_amdgcn_exp2f(m_s[w][rr] - M) : 0.0f;
+    l += wt[w] * l_s[w][rr];
+  }
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  float ov[CW];
+#pragma unroll
+  for (int c = 0; c < CW; ++c) ov[c] = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+#pragma unroll
+    for (int c = 0; c < CW; c += 4) {
+      const f32x4 x = *(const f32x4*)(ostage(w) + rr * OS + c0 + c);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ov[c + u] += wt[w] * x[u];
+    }
+  const int hh = rr / len, i = rr - hh * len;
+  if (i >= p.N) return;                      // (a sequence longer than N: not stored)
+  const int h = g * p.G + hh;
+  const float lse_row = l > 0.0f ? (M + __builtin_amdgcn_logf(l)) * kLn2 : -__builtin_inff();
+  if (p.n_splits > 1) {
+    const long long prow = (((long long)split * p.B + b) * p.Hq + h) * p.N + i;
+#pragma unroll
+    for (int c = 0; c < CW; c += 4)
+      *(f32x4*)(p.o_part + prow * D + c0 + c) =
+          f32x4{ov[c] * inv, ov[c + 1] * inv, ov[c + 2] * inv, ov[c + 3] * inv};
+    if ((tid & 7) == 0) p.lse_part[prow] = lse_row;
+    return;
+  }
+  const long long qbase = (VARLEN ? (long long)seq0 * p.q_rs : (long long)b * p.q_bs) +
+                          (long long)h * p.q_hs + (long long)i * p.q_rs + c0;
+  using OT = typename std::conditional<OUT_F32, float, T>::type;
+  OT* dst = (OT*)p.o + qbase;
+#pragma unroll
+  for (int c = 0; c < CW; c += 4) {
+    if (OUT_F32) {
+      *(f32x4*)((float*)dst + c) = f32x4{ov[c] * inv, ov[c + 1] * inv, ov[c + 2] * inv, ov[c + 3] * inv};
+    } else {
+      *(u32x2*)(dst + c) = u32x2{Ops<T>::pack(ov[c] * inv, ov[c + 1] * inv),
+                                 Ops<T>::pack(ov[c + 2] * inv, ov[c + 3] * inv)};
+    }
+  }
+  if ((tid & 7) == 0) p.lse[((long long)b * p.Hq + h) * p.N + i] = lse_row;
+}
+
+// ---------------------------------------------------------------------------
 // Split-KV merge.  Each split s of a row holds O_s (normalised over its keys)
 // and L_s = ln(sum of its exp-scores); the row's result is
 //   L = ln sum_s exp(L_s),   O = sum_s exp(L_s - L) O_s,
@@ -939,6 +1239,33 @@ const Variant kVariants[] = {
     FA_V32(128, 0, 0), FA_V32(128, 0, 1), FA_V32(128, 1, 0), FA_V32(128, 1, 1),
 };
 
+// Decode kernels (16-bit inputs, G * Nq <= 32).
+struct DecodeVariant {
+  int in_dtype, d, causal, varlen, out_dtype;
+  KernelFn fn;
+  const char* name;
+};
+#define FA_VD(T, TN, DT, D, C, VL, OF)                                            \
+  {DT, D, C, VL, (OF) ? FA_F32 : DT, fa_decode_mfma<T, D, (C != 0), (VL != 0), (OF != 0)>, \
+   "fa_decode_mfma_" TN "_d" #D FA_CAT(FA_SFX_C_, C) FA_CAT(FA_SFX_V_, VL)          \
+       FA_CAT(FA_SFX_O_, OF)}
+#define FA_VD_ALL(T, TN, DT, D)                                                   \
+  FA_VD(T, TN, DT, D, 0, 0, 0), FA_VD(T, TN, DT, D, 0, 0, 1),                      \
+  FA_VD(T, TN, DT, D, 0, 1, 0), FA_VD(T, TN, DT, D, 0, 1, 1),                      \
+  FA_VD(T, TN, DT, D, 1, 0, 0), FA_VD(T, TN, DT, D, 1, 0, 1),                      \
+  FA_VD(T, TN, DT, D, 1, 1, 0), FA_VD(T, TN, DT, D, 1, 1, 1)
+const DecodeVariant kDecodeVariants[] = {
+    FA_VD_ALL(__bf16, "bf16", FA_BF16, 64), FA_VD_ALL(__bf16, "bf16", FA_BF16, 128),
+    FA_VD_ALL(_Float16, "f16", FA_F16, 64), FA_VD_ALL(_Float16, "f16", FA_F16, 128),
+};
+const DecodeVariant* find_decode(int in_dtype, int d, int causal, int varlen, int out_dtype) {
+  for (const DecodeVariant& v : kDecodeVariants)
+    if (v.in_dtype == in_dtype && v.d == d && v.causal == causal && v.varlen == varlen &&
+        v.out_dtype == out_dtype)
+      return &v;
+  return nullptr;
+}
+
 const Variant* find_variant(int in_dtype, int d, int causal, int varlen, int out_dtype,
                             int sparse = 0) {
   for (const Variant& v : kVariants)
@@ -992,12 +1319,25 @@ const char* kernel_name(int in_dtype, int d, int causal, int varlen, int out_dty
   return v ? v->name : nullptr;
 }
 
+const char* kernel_name_kv(int in_dtype, int d, int causal, int varlen, int out_dtype, int Hq,
+                           int Hkv, int Nq) {
+  if (use_decode(in_dtype, Hq, Hkv, Nq, false)) {
+    const DecodeVariant* v = find_decode(in_dtype, d, causal != 0, varlen != 0, out_dtype);
+    return v ? v->name : nullptr;
+  }
+  return kernel_name(in_dtype, d, causal, varlen, out_dtype);
+}
+
 int launch_fwd(const LaunchArgs& a, void* stream) {
   const bool varlen = a.cu_seqlens != nullptr;
   const bool sparse = a.block_mask != nullptr;
   if (sparse && a.in_dtype == FA_F32) return FA_ERR_DTYPE;
   const Variant* var = find_variant(a.in_dtype, a.d, a.causal, varlen, a.out_dtype, sparse);
   if (!var) return FA_ERR_DTYPE;
+  const bool decode = use_decode(a.in_dtype, a.Hq, a.Hkv, a.N, sparse);
+  const DecodeVariant* dvar = decode ? find_decode(a.in_dtype, a.d, a.causal, varlen, a.out_dtype)
+                                     : nullptr;
+  if (decode && !dvar) return FA_ERR_DTYPE;
   const Plan plan = make_plan(a.B, a.Hq, a.Hkv, a.N, a.d, a.in_dtype);
 
   FwdParams p;
@@ -1030,10 +1370,15 @@ int launch_fwd(const LaunchArgs& a, void* stream) {
     p.kv_rs = d; p.kv_hs = (long long)a.Nk * d; p.kv_bs = (long long)a.Hkv * a.Nk * d;
   }
   void* args[] = {&p};
-  const hipError_t e = hipLaunchKernel((const void*)var->fn,
-                                       dim3((unsigned)(plan.total_wg * (uint64_t)n_splits)),
-                                       dim3(64 * waves_per_wg(a.in_dtype)), args, 0,
-                                       (hipStream_t)stream);
+  // Decode: one 4-wave workgroup per (sequence, K/V head, split).
+  const hipError_t e =
+      decode ? hipLaunchKernel((const void*)dvar->fn,
+                               dim3((unsigned)((uint64_t)a.B * a.Hkv * (uint64_t)n_splits)),
+                               dim3(256), args, 0, (hipStream_t)stream)
+             : hipLaunchKernel((const void*)var->fn,
+                               dim3((unsigned)(plan.total_wg * (uint64_t)n_splits)),
+                               dim3(64 * waves_per_wg(a.in_dtype)), args, 0,
+                               (hipStream_t)stream);
   if (e != hipSuccess) return FA_ERR_LAUNCH;
   if (n_splits == 1) return FA_OK;
   const MergeFn mf = find_merge(a.out_dtype, a.d, varlen);
@@ -1048,11 +1393,13 @@ int suggest_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int in_dtype, 
   if (in_dtype == FA_F32 || Nq > 64 || cus <= 0) return 1;
   const Plan plan = make_plan(B, Hq, Hkv, Nq, d, in_dtype);
   // One workgroup fills a compute unit (its eight waves take the VGPRs of
-  // two per SIMD); split only grids smaller than one per compute unit.
+  // two per SIMD, and the decode kernel's merge area most of the LDS); split
+  // only grids smaller than one per compute unit.
   const uint64_t want = (uint64_t)cus;
-  if (plan.total_wg >= want) return 1;
+  const uint64_t wgs = use_decode(in_dtype, Hq, Hkv, Nq, false) ? (uint64_t)B * Hkv : plan.total_wg;
+  if (wgs >= want) return 1;
   const int tiles = vt_tiles(Nk);
-  uint64_t n = (want + plan.total_wg - 1) / plan.total_wg;
+  uint64_t n = (want + wgs - 1) / wgs;
   const uint64_t max_by_len = (uint64_t)tiles / 4;     // at least 4 tiles (256 keys) a split
   if (n > max_by_len) n = max_by_len;
   if (n > 64) n = 64;

@@ -123,6 +123,14 @@ inline uint64_t split_workspace_bytes(int B, int Hq, int Nq, int d, int n_splits
   return rows > UINT64_MAX / per ? UINT64_MAX : rows * per;
 }
 
+// Shapes that run the decode kernel: 16-bit inputs, dense, and the G query
+// heads of a K/V head times the query rows per sequence fit one 32-row
+// MFMA block.
+inline bool use_decode(int in_dtype, int Hq, int Hkv, int Nq, bool sparse) {
+  return in_dtype != FA_F32 && !sparse && Hkv > 0 && Nq >= 1 &&
+         (long long)(Hq / Hkv) * Nq <= 32;
+}
+
 // A split count that fills the GPU when the grid alone would not: used for
 // decode-like shapes (few query rows per sequence).  1 = no split.
 int suggest_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int in_dtype, int cus);
@@ -152,6 +160,10 @@ int launch_bwd(const BwdArgs& a, void* stream);
 
 // Static name of the kernel instance for these settings, or nullptr.
 const char* kernel_name(int in_dtype, int d, int causal, int varlen, int out_dtype);
+// The same for fa_fwd_kv with Hq, Hkv and the query count Nq (the decode
+// kernel where use_decode holds).
+const char* kernel_name_kv(int in_dtype, int d, int causal, int varlen, int out_dtype, int Hq,
+                           int Hkv, int Nq);
 
 }  // namespace fa
 

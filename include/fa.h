@@ -261,9 +261,19 @@ int fa_fwd_check(const void* q, const void* k, const void* v, const void* o,
 /* Name of the kernel fa_fwd launches for these settings, or NULL if they are
  * unsupported.  Lets a caller confirm that this library, not a fallback, ran
  * (the Kotaemon page's caveats recommend checking that the fast attention
- * path is really active).  The string is static; do not free it. */
+ * path is really active).  The string is static; do not free it.  This is
+ * the kernel for query counts N with (Hq / Hkv) * N > 32; below that
+ * fa_kernel_name_kv names the decode kernel that runs instead. */
 const char* fa_kernel_name(int in_dtype, int d, int causal, int varlen,
                            int out_dtype);
+
+/* Name of the kernel fa_fwd_kv (and fa_fwd, with Nq = N) launches for these
+ * settings, head counts and query count Nq (the longest sequence's): for
+ * 16-bit inputs with (Hq / Hkv) * Nq <= 32 the decode kernel, which packs
+ * the query heads of a K/V head into one 32-row block, else as
+ * fa_kernel_name.  NULL if unsupported (or Hkv < 1). */
+const char* fa_kernel_name_kv(int in_dtype, int d, int causal, int varlen, int out_dtype,
+                              int Hq, int Hkv, int Nq);
 
 /* 1 if fa_fwd supports (in_dtype, d, causal), else 0 — so a caller can pick
  * another attention path when this one does not apply. */

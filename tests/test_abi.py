@@ -64,6 +64,24 @@ def test_version_and_support():
     assert fa.kernel_name(fa.FA_F32, 64, False, False, fa.FA_BF16) is None
 
 
+def test_kernel_name_kv_routing():
+    """The decode kernel runs exactly where the G query heads of a K/V head
+    times the query rows fit one 32-row block (16-bit inputs); elsewhere the
+    prefill kernel of fa_kernel_name."""
+    pre = fa.kernel_name(fa.FA_BF16, 128, True, False, fa.FA_F32)
+    assert fa.kernel_name_kv(fa.FA_BF16, 128, True, False, fa.FA_F32, 32, 8, 8) == \
+        "fa_decode_mfma_bf16_d128_causal_of32"                          # G=4, 4*8 = 32
+    assert fa.kernel_name_kv(fa.FA_BF16, 128, True, False, fa.FA_F32, 32, 8, 9) == pre
+    assert fa.kernel_name_kv(fa.FA_F16, 64, False, True, fa.FA_F16, 8, 8, 32) == \
+        "fa_decode_mfma_f16_d64_varlen"                                  # G=1
+    assert fa.kernel_name_kv(fa.FA_F16, 64, False, True, fa.FA_F16, 8, 8, 33) == \
+        fa.kernel_name(fa.FA_F16, 64, False, True, fa.FA_F16)
+    assert fa.kernel_name_kv(fa.FA_F32, 64, False, False, fa.FA_F32, 8, 8, 1) == \
+        fa.kernel_name(fa.FA_F32, 64, False, False, fa.FA_F32)          # fp32: no decode kernel
+    assert fa.kernel_name_kv(fa.FA_BF16, 96, True, False, fa.FA_F32, 8, 8, 1) is None
+    assert fa.kernel_name_kv(fa.FA_BF16, 128, True, False, fa.FA_F32, 8, 0, 1) is None
+
+
 # Fake, aligned, non-overlapping addresses: the checks never dereference them.
 BASE = dict(q=0x100000, k=0x200000, v=0x300000, o=0x400000, lse=0x500000,
             B=2, Hq=8, Hkv=2, N=64, d=128, causal=1, scale=0.125, cu_seqlens=None,

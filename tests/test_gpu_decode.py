@@ -39,6 +39,12 @@ DECODE = [
     ("fp16", 64, 3, 8, 8, 1, 777, True),
     ("bf16", 128, 5, 8, 2, [1, 1, 1, 1, 1], [100, 3000, 1, 64, 777], True),
     ("fp16", 128, 3, 4, 1, [2, 1, 3], [513, 2, 1000], False),
+    # Shapes of the decode kernel's edges (G * nq <= 32 rows in one block):
+    ("bf16", 128, 2, 32, 4, 4, 700, True),        # G * nq = 32, a full block
+    ("fp16", 128, 3, 16, 2, [1, 3, 2], [1, 60, 130], True),   # one key; one partial tile
+    ("bf16", 64, 3, 8, 4, [2, 2, 1], [0, 5, 64], True),       # a sequence with no keys
+    ("fp16", 64, 2, 8, 8, 3, 2, True),            # fewer keys than queries: row 0 sees none
+    ("bf16", 128, 2, 8, 2, 5, 1000, False),
 ]
 
 
