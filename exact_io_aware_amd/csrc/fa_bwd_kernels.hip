@@ -11,7 +11,7 @@
 // ever stored; grouped-query K/V gradients sum over the group's query heads.
 //
 // gfx950 mapping (our design):
-//  * fa_bwd_delta: D_r, one 32-lane group per row.
+//  * fa_bwd_delta: D_r, D/8 lanes per row (8 columns each).
 //  * fa_bwd_dkdv: a workgroup of 8 waves owns 256 keys of one K/V head
 //    (each wave 32 keys: its K rows in registers, its V rows in LDS, both
 //    read as MFMA B operands) and streams 64-row query tiles (Q and dO,
@@ -58,11 +58,16 @@ struct BwdParams {
 
 // ---------------------------------------------------------------------------
 // D_r = sum_j dO_rj * O_rj (fp32), and L_r * log2(e) (the exponent offset
-// of the base-2 exponentials).  32 lanes per row, D/32 columns each.
+// of the base-2 exponentials).  D/8 lanes per row, 8 columns each: one
+// 16-byte load of dO and one or two of O per lane.  HBM-bound (O and dO
+// are read once), so the loads are non-temporal, the cache policy that
+// streams fastest.
 template <typename T, typename OT, int D, bool VARLEN>
 __global__ __launch_bounds__(256) void fa_bwd_delta(BwdParams p) {
-  constexpr int PER = D / 32;
-  const int row_id = blockIdx.x * 8 + (threadIdx.x >> 5);     // (b, h, r)
+  constexpr int LPR = D / 8;                 // lanes per row
+  constexpr int RPB = 256 / LPR;             // rows per workgroup
+  const int row_id = blockIdx.x * RPB + (int)threadIdx.x / LPR;    // (b, h, r)
+  const int sub = threadIdx.x % LPR;
   if (row_id >= p.B * p.Hq * p.N) return;
   const int r = row_id % p.N;
   const int bh = row_id / p.N;
@@ -75,15 +80,23 @@ __global__ __launch_bounds__(256) void fa_bwd_delta(BwdParams p) {
   if (r >= len) return;
   const long long off = (VARLEN ? (long long)(seq0 + r) * p.q_rs
                                 : (long long)b * p.q_bs + (long long)r * p.q_rs) +
-                        (long long)h * p.q_hs + (threadIdx.x & 31) * PER;
-  const T* dop = (const T*)p.dout + off;
-  const OT* op = (const OT*)p.o + off;
+                        (long long)h * p.q_hs + 8 * sub;
+  using vec8 = typename Ops<T>::vec8;
+  const vec8 dv = __builtin_bit_cast(vec8, __builtin_nontemporal_load((const u32x4*)((const T*)p.dout + off)));
   float acc = 0.0f;
+  if constexpr (std::is_same<OT, float>::value) {
+    const f32x4* op = (const f32x4*)((const float*)p.o + off);
+    const f32x4 o0 = __builtin_nontemporal_load(op), o1 = __builtin_nontemporal_load(op + 1);
 #pragma unroll
-  for (int j = 0; j < PER; ++j) acc += (float)dop[j] * (float)op[j];
+    for (int j = 0; j < 4; ++j) acc += (float)dv[j] * o0[j] + (float)dv[j + 4] * o1[j];
+  } else {
+    const vec8 ov = __builtin_bit_cast(vec8, __builtin_nontemporal_load((const u32x4*)((const T*)p.o + off)));
 #pragma unroll
-  for (int m = 16; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 32);
-  if ((threadIdx.x & 31) == 0) {
+    for (int j = 0; j < 8; ++j) acc += (float)dv[j] * (float)ov[j];
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
+  if (sub == 0) {
     const long long li = ((long long)b * p.Hq + h) * p.N + r;
     p.delta[li] = acc;
     p.lse2[li] = p.lse[li] * kLog2e;
@@ -701,8 +714,9 @@ int launch_bwd(const BwdArgs& a, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   void* args[] = {&p};
   const uint64_t rows = (uint64_t)a.B * a.Hq * a.N;
-  if (hipLaunchKernel((const void*)dv->fn, dim3((unsigned)((rows + 7) / 8)), dim3(256), args, 0,
-                      s) != hipSuccess)
+  const uint64_t rpb = 256 / (a.d / 8);      // fa_bwd_delta: rows per workgroup
+  if (hipLaunchKernel((const void*)dv->fn, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256),
+                      args, 0, s) != hipSuccess)
     return FA_ERR_LAUNCH;
   const unsigned g1 = (unsigned)((uint64_t)a.B * a.Hkv * p.kv_blocks);
   if (hipLaunchKernel((const void*)var->dkdv, dim3(g1), dim3(512), args, 0, s) != hipSuccess)

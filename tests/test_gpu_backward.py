@@ -37,7 +37,7 @@ def _make(case, seed):
     return w
 
 
-def _gpu(w, grad_dtype=None):
+def _gpu(w, grad_dtype=None, out_dtype=None):
     import torch
 
     import exact_io_aware_amd as fa
@@ -45,7 +45,8 @@ def _gpu(w, grad_dtype=None):
     q, k, v, do = (G.to_device(w[x], w["dtype"], dev) for x in ("q", "k", "v", "dout"))
     cu = None if w["cu_seqlens"] is None else torch.from_numpy(w["cu_seqlens"]).to(dev)
     ms = w["N"] if cu is not None else None
-    o, lse = fa.fwd(q, k, v, causal=w["causal"], scale=w["scale"], cu_seqlens=cu, max_seqlen=ms)
+    o, lse = fa.fwd(q, k, v, causal=w["causal"], scale=w["scale"], cu_seqlens=cu, max_seqlen=ms,
+                    out_dtype=out_dtype or torch.float32)
     dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=w["causal"], scale=w["scale"],
                         cu_seqlens=cu, max_seqlen=ms,
                         grad_dtype=grad_dtype or torch.float32)
@@ -71,6 +72,23 @@ def test_backward_parity(i):
         err = np.abs(a - r)
         G.say(f"  {name}: max err {err.max():.3e}, max |ref| {np.abs(r).max():.3e}, "
               f"rel {err.max() / np.abs(r).max():.3e}")
+        assert np.isfinite(a).all()
+        assert err.max() <= G.grad_bar(w["dtype"]) * np.abs(r).max(), name
+
+
+@pytest.mark.parametrize("case", [("bf16", 128, 2, 8, 2, 200, True),
+                                  ("fp16", 64, 2, 4, 2, [129, 64], False)],
+                         ids=["bf16-d128", "fp16-d64-varlen"])
+def test_backward_from_16bit_o(case):
+    """O stored in the input type (the forward's 16-bit output) feeds the D
+    rows: the same bar, with O's rounding (half an ulp) inside it."""
+    w = _make(case, seed=960)
+    ref = _oracle(w)
+    G.say(f"backward from 16-bit O, case {case}")
+    got = _gpu(w, out_dtype=G.torch_dtype(w["dtype"]))
+    for name, a, r in zip(("dq", "dk", "dv"), got, ref):
+        err = np.abs(a - r)
+        G.say(f"  {name}: max err {err.max():.3e}, max |ref| {np.abs(r).max():.3e}")
         assert np.isfinite(a).all()
         assert err.max() <= G.grad_bar(w["dtype"]) * np.abs(r).max(), name
 
