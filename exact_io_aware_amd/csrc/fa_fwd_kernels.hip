@@ -701,7 +701,9 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
         const int orow_i = row0 + 32 * qb + r;
         if (orow_i < len) {
           char* dst = (char*)((OT*)p.o + qbase + (long long)orow_i * p.q_rs) + pass * RP + c * 16;
-          *(u32x4*)dst = v;
+          // O is written once and not read back here: a non-temporal store
+          // (whole row segments) keeps it from displacing K/V in the caches.
+          __builtin_nontemporal_store(v, (u32x4*)dst);
         }
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);      // reads done before the slot is rewritten

@@ -45,6 +45,8 @@ DECODE = [
     ("bf16", 64, 3, 8, 4, [2, 2, 1], [0, 5, 64], True),       # a sequence with no keys
     ("fp16", 64, 2, 8, 8, 3, 2, True),            # fewer keys than queries: row 0 sees none
     ("bf16", 128, 2, 8, 2, 5, 1000, False),
+    ("bf16", 128, 2, 32, 1, 1, 3000, True),       # one K/V head for 32 query heads
+    ("fp16", 64, 2, 16, 1, 2, 900, True),         # G = 16, two queries: 32 rows
 ]
 
 
