@@ -50,6 +50,7 @@ struct BwdParams {
   const int* cu_seqlens;
   int B, N, Hq, Hkv, G;
   int hp, rows_per_wg, n_rblocks, n_hgroups, xcd_remap;   // dq grid (as the forward)
+  int rb_major, n_units;                         // dq order (as the forward)
   int kv_blocks;                                 // dV, dK: 256-key blocks per sequence
   float scale, scale_log2;
   long long q_bs, q_hs, q_rs;     // q, o, dO, dQ element strides
@@ -420,18 +421,19 @@ __global__ __launch_bounds__(512, 2) void fa_bwd_dq(BwdParams p) {
   // j % 8).  With xcd_remap, XCD x takes the units u with u % 8 == x, each
   // unit's row blocks consecutively (as the forward kernel): a unit's K/V
   // stays in one XCD's L2, and every XCD gets the same mix of long and
-  // short causal row blocks.
-  int unit, rb;
-  if (p.xcd_remap) {
-    const int idx = blockIdx.x >> 3;
-    const int k = idx / p.n_rblocks;
-    rb = idx - k * p.n_rblocks;
-    unit = 8 * k + (blockIdx.x & 7);
+  // short causal row blocks.  With rb_major, row-block slot s of every unit
+  // comes before slot s + 1 of any (longest row blocks of all units first).
+  const int idx = p.xcd_remap ? blockIdx.x >> 3 : blockIdx.x;
+  const int nu = p.xcd_remap ? p.n_units >> 3 : p.n_units;
+  int k, rb;
+  if (p.rb_major) {
+    rb = idx / nu;
+    k = idx - rb * nu;
   } else {
-    unit = blockIdx.x / p.n_rblocks;
-    rb = blockIdx.x - unit * p.n_rblocks;
+    k = idx / p.n_rblocks;
+    rb = idx - k * p.n_rblocks;
   }
-  if (CAUSAL) rb = p.n_rblocks - 1 - rb;     // longest row blocks first
+  const int unit = p.xcd_remap ? 8 * k + (blockIdx.x & 7) : k;
   const int b = unit / p.n_hgroups;
   const int hgrp = unit - b * p.n_hgroups;
   const int h = hgrp * p.hp + (wave % p.hp);
@@ -441,8 +443,11 @@ __global__ __launch_bounds__(512, 2) void fa_bwd_dq(BwdParams p) {
     seq0 = p.cu_seqlens[b];
     len = p.cu_seqlens[b + 1] - seq0;
   }
+  // Longest row blocks first: the sequence's last ones (slot s is row
+  // block nrb - 1 - s).
+  if (CAUSAL) rb = (VARLEN ? (len + p.rows_per_wg - 1) / p.rows_per_wg : p.n_rblocks) - 1 - rb;
   const int wg_row0 = rb * p.rows_per_wg;
-  if (wg_row0 >= len) return;
+  if (rb < 0 || wg_row0 >= len) return;
   const int row0 = wg_row0 + (wave / p.hp) * 32;
   const int kv_end = CAUSAL ? min(wg_row0 + p.rows_per_wg, len) : len;
   const bool active = row0 < len;
@@ -701,6 +706,10 @@ int launch_bwd(const BwdArgs& a, void* stream) {
   p.hp = plan.hp; p.rows_per_wg = plan.rows_per_wg; p.n_rblocks = plan.n_rblocks;
   p.n_hgroups = plan.n_hgroups;
   p.xcd_remap = ((uint64_t)a.B * plan.n_hgroups) % 8 == 0;
+  p.n_units = a.B * plan.n_hgroups;
+  // Row-block-major only while all K/V fits in half of the last-level cache
+  // (as the forward).
+  p.rb_major = a.causal && 4LL * a.B * a.Hkv * a.N * a.d <= (128LL << 20) ? 1 : 0;
   p.kv_blocks = (a.N + 255) / 256;
   p.scale = a.scale; p.scale_log2 = a.scale * kLog2e;
   const long long d = a.d;

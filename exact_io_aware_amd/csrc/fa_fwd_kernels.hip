@@ -56,6 +56,9 @@ struct FwdParams {
   const int* cu_seqlens_k; // key/value offsets (varlen)
   int N, Nk, Hq, G;        // max query count, max key count, query heads, Hq / Hkv
   int hp, rows_per_wg, n_rblocks, n_hgroups, total_wg, xcd_remap;
+  // rb_major (causal): row-block slot s of every unit is launched before slot
+  // s + 1 of any, slot s being a sequence's s-th longest row block.
+  int rb_major, n_units;
   float scale_log2;        // scale * log2(e)
   const void* vt;          // packed V^T tiles (16-bit inputs), see fa_vt_pack
   int Hkv, vt_ntiles;      // K/V heads; V^T tiles per (sequence, K/V head)
@@ -196,17 +199,23 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
     split = wg % p.n_splits;
     wg /= p.n_splits;
   }
-  int unit, rb;
-  if (p.xcd_remap) {
-    const int idx = wg >> 3;
-    const int k = idx / p.n_rblocks;
-    rb = idx - k * p.n_rblocks;
-    unit = 8 * k + (wg & 7);
+  //
+  // Under the causal mask row blocks differ in length.  Dispatched
+  // unit by unit, the last units' long row blocks start when most CUs are
+  // already busy, and they set the launch's end; with rb_major the
+  // longest row blocks of all units go first (each unit still on its XCD)
+  // and the short ones fill the tail.
+  const int idx = p.xcd_remap ? wg >> 3 : wg;
+  const int nu = p.xcd_remap ? p.n_units >> 3 : p.n_units;  // units in this order
+  int k, rb;
+  if (p.rb_major) {
+    rb = idx / nu;
+    k = idx - rb * nu;
   } else {
-    unit = wg / p.n_rblocks;
-    rb = wg - unit * p.n_rblocks;
+    k = idx / p.n_rblocks;
+    rb = idx - k * p.n_rblocks;
   }
-  if (CAUSAL) rb = p.n_rblocks - 1 - rb;     // longest row blocks first
+  const int unit = p.xcd_remap ? 8 * k + (wg & 7) : k;
   const int b = unit / p.n_hgroups;
   const int hgrp = unit - b * p.n_hgroups;
   const int h = hgrp * p.hp + (wave % p.hp);
@@ -222,9 +231,12 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(Fwd
     seq0_k = p.cu_seqlens_k[b];
     len_k = p.cu_seqlens_k[b + 1] - seq0_k;
   }
+  // Longest row blocks first: under the causal mask those are the last
+  // ones of the sequence (slot s is row block nrb - 1 - s).
+  if (CAUSAL) rb = (VARLEN ? (len + p.rows_per_wg - 1) / p.rows_per_wg : p.n_rblocks) - 1 - rb;
   const int off = len_k - len;
   const int wg_row0 = rb * p.rows_per_wg;
-  if (wg_row0 >= len) return;                 // uniform over the workgroup
+  if (rb < 0 || wg_row0 >= len) return;      // uniform over the workgroup
   const int row0 = wg_row0 + (wave / p.hp) * WR;
   const int wg_rows_end = min(wg_row0 + p.rows_per_wg, len);
   const int kv_end = CAUSAL ? max(0, min(wg_rows_end + off, len_k)) : len_k;
@@ -1349,6 +1361,12 @@ int launch_fwd(const LaunchArgs& a, void* stream) {
   p.hp = plan.hp; p.rows_per_wg = plan.rows_per_wg; p.n_rblocks = plan.n_rblocks;
   p.n_hgroups = plan.n_hgroups; p.total_wg = (int)plan.total_wg;
   p.xcd_remap = (a.in_dtype != FA_F32) && ((uint64_t)a.B * plan.n_hgroups) % 8 == 0;
+  p.n_units = a.B * plan.n_hgroups;
+  // Row-block-major order keeps every unit's K/V in use at once: only when
+  // all of it (the largest sequence length for every sequence) fits in half
+  // of the 256 MB last-level cache, else the re-reads of each unit's K/V
+  // by its row blocks go to HBM and unit-major order is faster.
+  p.rb_major = a.causal && 4LL * a.B * a.Hkv * a.Nk * a.d <= (128LL << 20) ? 1 : 0;
   p.scale_log2 = a.scale * kLog2e;
   p.vt = a.vt; p.Hkv = a.Hkv; p.vt_ntiles = vt_tiles(a.Nk);
   const int n_splits = (a.in_dtype != FA_F32 && !sparse && a.n_splits > 1) ? a.n_splits : 1;
