@@ -702,7 +702,7 @@ int launch_bwd(const BwdArgs& a, void* stream) {
   p.dq = a.dq; p.dk = a.dk; p.dv = a.dv;
   p.cu_seqlens = a.cu_seqlens;
   p.B = a.B; p.N = a.N; p.Hq = a.Hq; p.Hkv = a.Hkv; p.G = a.Hq / a.Hkv;
-  const Plan plan = make_plan(a.B, a.Hq, a.Hkv, a.N, a.d, a.in_dtype);
+  const Plan plan = make_plan_nw(a.B, a.Hq, a.Hkv, a.N, a.in_dtype, 8);  // the dQ kernel's 8 waves
   p.hp = plan.hp; p.rows_per_wg = plan.rows_per_wg; p.n_rblocks = plan.n_rblocks;
   p.n_hgroups = plan.n_hgroups;
   p.xcd_remap = ((uint64_t)a.B * plan.n_hgroups) % 8 == 0;

@@ -159,9 +159,9 @@ __global__ __launch_bounds__(256) void fa_vt_pack(VtParams p) {
 // workgroup streams only the key tiles that some wave's mask row admits, in
 // key order; a wave whose own row does not admit a tile forms P = 0 for it.
 template <typename T, int D, bool CAUSAL, bool VARLEN, bool OUT_F32, bool SPARSE>
-__global__ __launch_bounds__(64 * waves_per_wg(FA_BF16), 2) void fa_fwd_mfma(FwdParams p) {
+__global__ __launch_bounds__(64 * waves_per_wg(FA_BF16, D, CAUSAL), 2) void fa_fwd_mfma(FwdParams p) {
   using vec8 = typename Ops<T>::vec8;
-  constexpr int NW = waves_per_wg(FA_BF16);        // waves per workgroup
+  constexpr int NW = waves_per_wg(FA_BF16, D, CAUSAL);  // waves per workgroup
   constexpr int NT = 64 * NW;                      // threads per workgroup
   constexpr int QB = rows_per_wave(FA_BF16) / 32;  // 32-row query blocks per wave
   constexpr int WR = 32 * QB;                // query rows per wave
@@ -1352,7 +1352,7 @@ int launch_fwd(const LaunchArgs& a, void* stream) {
   const DecodeVariant* dvar = decode ? find_decode(a.in_dtype, a.d, a.causal, varlen, a.out_dtype)
                                      : nullptr;
   if (decode && !dvar) return FA_ERR_DTYPE;
-  const Plan plan = make_plan(a.B, a.Hq, a.Hkv, a.N, a.d, a.in_dtype);
+  const Plan plan = make_plan(a.B, a.Hq, a.Hkv, a.N, a.d, a.in_dtype, a.causal);
 
   FwdParams p;
   p.q = a.q; p.k = a.k; p.v = a.v; p.o = a.o; p.lse = a.lse;
@@ -1397,7 +1397,7 @@ int launch_fwd(const LaunchArgs& a, void* stream) {
                                dim3(256), args, 0, (hipStream_t)stream)
              : hipLaunchKernel((const void*)var->fn,
                                dim3((unsigned)(plan.total_wg * (uint64_t)n_splits)),
-                               dim3(64 * waves_per_wg(a.in_dtype)), args, 0,
+                               dim3(64 * waves_per_wg(a.in_dtype, a.d, a.causal)), args, 0,
                                (hipStream_t)stream);
   if (e != hipSuccess) return FA_ERR_LAUNCH;
   if (n_splits == 1) return FA_OK;
@@ -1411,7 +1411,9 @@ int launch_fwd(const LaunchArgs& a, void* stream) {
 
 int suggest_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int in_dtype, int cus) {
   if (in_dtype == FA_F32 || Nq > 64 || cus <= 0) return 1;
-  const Plan plan = make_plan(B, Hq, Hkv, Nq, d, in_dtype);
+  // The 8-wave plan (a causal d = 64 launch has up to twice the
+  // workgroups, of half the size).
+  const Plan plan = make_plan(B, Hq, Hkv, Nq, d, in_dtype, false);
   // One workgroup fills a compute unit (its eight waves take the VGPRs of
   // two per SIMD, and the decode kernel's merge area most of the LDS); split
   // only grids smaller than one per compute unit.

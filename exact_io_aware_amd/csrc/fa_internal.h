@@ -13,9 +13,16 @@ namespace fa {
 // share every K/V operand read from LDS).
 constexpr int rows_per_wave(int in_dtype) { return in_dtype == FA_F32 ? 32 : 32; }
 
-// Waves per workgroup: 8 for 16-bit inputs (two per SIMD; all eight share
-// each K/V tile in LDS), 4 for fp32 inputs.
-constexpr int waves_per_wg(int in_dtype) { return in_dtype == FA_F32 ? 4 : 8; }
+// Waves per workgroup of the forward attention kernels.  16-bit inputs: 8
+// (all eight share each K/V tile in LDS), except 4 at d = 64 under the
+// causal mask.  There a workgroup's K/V walk is short next to its fixed
+// costs (Q load, prologue, epilogue) and row blocks differ in length:
+// smaller workgroups, more of them per CU, overlap one's prologue with
+// another's main loop and even out the launch's end.  Without the mask,
+// 8 waves' sharing of each tile is worth more.  fp32 inputs: 4.
+constexpr int waves_per_wg(int in_dtype, int d, bool causal) {
+  return in_dtype == FA_F32 || (d == 64 && causal) ? 4 : 8;
+}
 
 // Block-sparse attention: query rows and keys per block of a block mask,
 // and the most 64-key tiles one sequence may have (the attention kernel
@@ -36,17 +43,22 @@ struct Plan {
   uint64_t total_wg; // B * n_hgroups * n_rblocks
 };
 
-inline Plan make_plan(int B, int Hq, int Hkv, int N, int d, int in_dtype) {
-  (void)d;
+// nw: waves per workgroup of the kernel the plan is for.
+inline Plan make_plan_nw(int B, int Hq, int Hkv, int N, int in_dtype, int nw) {
   Plan p;
   const int G = Hq / Hkv;
   if (in_dtype == FA_F32) p.hp = 1;
   else p.hp = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
-  p.rows_per_wg = waves_per_wg(in_dtype) * rows_per_wave(in_dtype) / p.hp;
+  p.rows_per_wg = nw * rows_per_wave(in_dtype) / p.hp;
   p.n_rblocks = (N + p.rows_per_wg - 1) / p.rows_per_wg;
   p.n_hgroups = Hq / p.hp;
   p.total_wg = (uint64_t)B * (uint64_t)p.n_hgroups * (uint64_t)p.n_rblocks;
   return p;
+}
+
+// The forward attention kernels' plan.
+inline Plan make_plan(int B, int Hq, int Hkv, int N, int d, int in_dtype, bool causal) {
+  return make_plan_nw(B, Hq, Hkv, N, in_dtype, waves_per_wg(in_dtype, d, causal));
 }
 
 // 64-key V^T tiles per (sequence, K/V head) in the packed-V workspace.
@@ -62,7 +74,8 @@ inline uint64_t workspace_bytes(int B, int Hkv, int N, int d, int in_dtype) {
 }
 
 inline uint64_t grid_size(int B, int Hq, int Hkv, int N, int d, int in_dtype) {
-  return make_plan(B, Hq, Hkv, N, d, in_dtype).total_wg;
+  // The larger of the two forward grids (with and without the mask).
+  return make_plan(B, Hq, Hkv, N, d, in_dtype, true).total_wg;
 }
 
 // Checks of the attention arguments (Nq queries, Nk keys per sequence; the
