@@ -707,9 +707,18 @@ int launch_bwd(const BwdArgs& a, void* stream) {
   p.n_hgroups = plan.n_hgroups;
   p.xcd_remap = ((uint64_t)a.B * plan.n_hgroups) % 8 == 0;
   p.n_units = a.B * plan.n_hgroups;
-  // Row-block-major only while all K/V fits in half of the last-level cache
-  // (as the forward).
-  p.rb_major = a.causal && 4LL * a.B * a.Hkv * a.N * a.d <= (128LL << 20) ? 1 : 0;
+  // Row-block-major only for a launch a few rounds deep whose K/V all fits
+  // in half of the last-level cache (the forward's rule).
+  p.rb_major = 0;
+  if (a.causal && 4LL * a.B * a.Hkv * a.N * a.d <= (128LL << 20)) {
+    int dev = -1, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)var->dq, 512, 0) ==
+            hipSuccess &&
+        cus > 0 && per_cu > 0)
+      p.rb_major = plan.total_wg <= 4ull * (uint64_t)cus * (uint64_t)per_cu;
+  }
   p.kv_blocks = (a.N + 255) / 256;
   p.scale = a.scale; p.scale_log2 = a.scale * kLog2e;
   const long long d = a.d;

@@ -1362,15 +1362,30 @@ int launch_fwd(const LaunchArgs& a, void* stream) {
   p.n_hgroups = plan.n_hgroups; p.total_wg = (int)plan.total_wg;
   p.xcd_remap = (a.in_dtype != FA_F32) && ((uint64_t)a.B * plan.n_hgroups) % 8 == 0;
   p.n_units = a.B * plan.n_hgroups;
-  // Row-block-major order keeps every unit's K/V in use at once: only when
-  // all of it (the largest sequence length for every sequence) fits in half
-  // of the 256 MB last-level cache, else the re-reads of each unit's K/V
-  // by its row blocks go to HBM and unit-major order is faster.
-  p.rb_major = a.causal && 4LL * a.B * a.Hkv * a.Nk * a.d <= (128LL << 20) ? 1 : 0;
   p.scale_log2 = a.scale * kLog2e;
   p.vt = a.vt; p.Hkv = a.Hkv; p.vt_ntiles = vt_tiles(a.Nk);
   const int n_splits = (a.in_dtype != FA_F32 && !sparse && a.n_splits > 1) ? a.n_splits : 1;
   p.n_splits = n_splits;
+  // Row-block-major order pays when the launch is a few rounds of
+  // workgroups deep (at most 4 per resident slot): then unit-major order
+  // starts the last units' long row blocks late and they set the launch's
+  // end.  With more rounds unit-major is already close to longest-first,
+  // and it keeps one unit's K/V at a time in the XCD's L2, where
+  // row-block-major spreads each XCD over all its units (more L2 misses).
+  // It also needs all K/V (the largest sequence length for every sequence)
+  // to fit in half of the 256 MB last-level cache, else each unit's K/V
+  // re-reads by its row blocks go to HBM.
+  p.rb_major = 0;
+  if (a.causal && !decode && 4LL * a.B * a.Hkv * a.Nk * a.d <= (128LL << 20)) {
+    int dev = -1, cus = 0, per_cu = 0;
+    const int threads = 64 * waves_per_wg(a.in_dtype, a.d, a.causal);
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)var->fn, threads, 0) ==
+            hipSuccess &&
+        cus > 0 && per_cu > 0)
+      p.rb_major = plan.total_wg * (uint64_t)n_splits <= 4ull * (uint64_t)cus * (uint64_t)per_cu;
+  }
   p.split_tiles = n_splits > 1 ? (p.vt_ntiles + n_splits - 1) / n_splits : p.vt_ntiles + 1;
   p.B = a.B; p.o_part = a.o_part; p.lse_part = a.lse_part;
   p.block_mask = a.block_mask;
