@@ -1131,15 +1131,32 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_f32(FwdParams p) {
   for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
   float m_run = kNoMax, ell = 0.0f;
 
+  // K/V tile j + 1 is fetched into registers while tile j is computed, so
+  // each tile's HBM round trip overlaps the previous tile's work.  Element
+  // e = tid + 256 i of a tile is row e / D, column e % D (rows past the end
+  // repeat the last key; their scores are masked).
+  constexpr int PER_T = BC * D / 256;
+  float kpre[PER_T], vpre[PER_T];
+  auto fetch = [&](int j) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int e = tid + 256 * i, r = e / D, c = e % D;
+      const long long row = (long long)min(j * BC + r, len_k - 1) * p.kv_rs;
+      kpre[i] = kp[row + c];
+      vpre[i] = vp[row + c];
+    }
+  };
+  if (ntiles > 0) fetch(0);
   for (int j = 0; j < ntiles; ++j) {
     const int kb = j * BC;
-    for (int e = tid; e < BC * D; e += 256) {
-      const int r = e / D, c = e % D;
-      const long long row = (long long)min(kb + r, len_k - 1) * p.kv_rs;
-      ks[r * KP + c] = kp[row + c];
-      vs[r * D + c] = vp[row + c];
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int e = tid + 256 * i, r = e / D, c = e % D;
+      ks[r * KP + c] = kpre[i];
+      vs[r * D + c] = vpre[i];
     }
     __syncthreads();
+    if (j + 1 < ntiles) fetch(j + 1);
     if (j < wave_ntiles) {
       f32x16 s = f32x16{};
 #pragma unroll
