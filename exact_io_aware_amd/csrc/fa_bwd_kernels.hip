@@ -398,9 +398,11 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv(BwdParams p) {
 // (up to 4 heads of a K/V group per workgroup), 64-key tiles of K and V
 // double-buffered in LDS; K^T is the K tile read transposed.
 template <typename T, int D, bool CAUSAL, bool VARLEN, bool OUT_F32>
-__global__ __launch_bounds__(512, 2) void fa_bwd_dq(BwdParams p) {
+__global__ __launch_bounds__(64 * waves_per_wg(FA_BF16, D, CAUSAL), 2) void fa_bwd_dq(BwdParams p) {
   using vec8 = typename Ops<T>::vec8;
-  constexpr int NT = 512;                    // 8 waves
+  // 8 waves (4 at d = 64 under the causal mask: the forward kernel's
+  // choice, for the same reasons).
+  constexpr int NT = 64 * waves_per_wg(FA_BF16, D, CAUSAL);
   constexpr int BC = 64;
   constexpr int DB = D / 32, DC = D / 16, CPR = D / 8, RB = D * 2;
   constexpr int TILE_BYTES = BC * RB;
@@ -702,7 +704,8 @@ int launch_bwd(const BwdArgs& a, void* stream) {
   p.dq = a.dq; p.dk = a.dk; p.dv = a.dv;
   p.cu_seqlens = a.cu_seqlens;
   p.B = a.B; p.N = a.N; p.Hq = a.Hq; p.Hkv = a.Hkv; p.G = a.Hq / a.Hkv;
-  const Plan plan = make_plan_nw(a.B, a.Hq, a.Hkv, a.N, a.in_dtype, 8);  // the dQ kernel's 8 waves
+  const int dq_threads = 64 * waves_per_wg(a.in_dtype, a.d, a.causal);  // as the dQ kernel
+  const Plan plan = make_plan_nw(a.B, a.Hq, a.Hkv, a.N, a.in_dtype, dq_threads / 64);
   p.hp = plan.hp; p.rows_per_wg = plan.rows_per_wg; p.n_rblocks = plan.n_rblocks;
   p.n_hgroups = plan.n_hgroups;
   p.xcd_remap = ((uint64_t)a.B * plan.n_hgroups) % 8 == 0;
@@ -714,7 +717,7 @@ int launch_bwd(const BwdArgs& a, void* stream) {
     int dev = -1, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)var->dq, 512, 0) ==
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)var->dq, dq_threads, 0) ==
             hipSuccess &&
         cus > 0 && per_cu > 0)
       p.rb_major = plan.total_wg <= 4ull * (uint64_t)cus * (uint64_t)per_cu;
@@ -739,7 +742,7 @@ int launch_bwd(const BwdArgs& a, void* stream) {
   const unsigned g1 = (unsigned)((uint64_t)a.B * a.Hkv * p.kv_blocks);
   if (hipLaunchKernel((const void*)var->dkdv, dim3(g1), dim3(512), args, 0, s) != hipSuccess)
     return FA_ERR_LAUNCH;
-  if (hipLaunchKernel((const void*)var->dq, dim3((unsigned)plan.total_wg), dim3(512), args, 0,
+  if (hipLaunchKernel((const void*)var->dq, dim3((unsigned)plan.total_wg), dim3(dq_threads), args, 0,
                       s) != hipSuccess)
     return FA_ERR_LAUNCH;
   return FA_OK;

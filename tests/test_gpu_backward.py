@@ -20,6 +20,8 @@ CASES = [
     ("bf16", 128, 3, 8, 2, [70, 1, 190], True),
     ("fp16", 64, 2, 4, 2, [129, 64], False),
     ("bf16", 128, 3, 8, 2, [70, 0, 33], True),        # an empty sequence
+    ("fp16", 64, 2, 8, 2, 300, True),                 # d = 64 causal, 4 heads per workgroup
+    ("bf16", 64, 2, 4, 2, [100, 257], True),          # d = 64 causal varlen, 2 heads per workgroup
 ]
 
 
