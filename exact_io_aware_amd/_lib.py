@@ -12,7 +12,7 @@ STATUS = {
     "FA_OK": 0, "FA_ERR_NULL": -1, "FA_ERR_SHAPE": -2, "FA_ERR_HEADDIM": -3,
     "FA_ERR_GQA": -4, "FA_ERR_DTYPE": -5, "FA_ERR_ALIGN": -6, "FA_ERR_ALIAS": -7,
     "FA_ERR_SCALE": -8, "FA_ERR_DEVICE": -9, "FA_ERR_LAUNCH": -10,
-    "FA_ERR_WORKSPACE": -11, "FA_ERR_ALLOC": -12,
+    "FA_ERR_WORKSPACE": -11, "FA_ERR_ALLOC": -12, "FA_ERR_SEQLENS": -13,
 }
 
 _lib = None
@@ -50,6 +50,9 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_kv_split_packed.argtypes = [vp, vp, vp, z, vp, vp, i, i, i, i, i, i, i, f, vp,
                                            vp, i, vp, z, vp, i, i]
     lib.fa_fwd_kv_split_packed.restype = i
+    lib.fa_fwd_kv_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, i, vp,
+                                    z, vp, i, i]
+    lib.fa_fwd_kv_split.restype = i
     lib.fa_fwd_sparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, vp, i, i,
                                   vp, i, i]
     lib.fa_fwd_sparse.restype = i
@@ -67,6 +70,10 @@ def load() -> ctypes.CDLL:
     lib.fa_kernel_name.restype = ctypes.c_char_p
     lib.fa_kernel_name_kv.argtypes = [i, i, i, i, i, i, i, i]
     lib.fa_kernel_name_kv.restype = ctypes.c_char_p
+    lib.fa_kernel_name_ex.argtypes = [i, i, i, i, i, i, i, i, i, i]
+    lib.fa_kernel_name_ex.restype = ctypes.c_char_p
+    lib.fa_check_seqlens.argtypes = [vp, i, i]
+    lib.fa_check_seqlens.restype = i
     lib.fa_supported.argtypes = [i, i, i]
     lib.fa_supported.restype = i
     lib.fa_status_string.argtypes = [i]
@@ -95,6 +102,24 @@ def kernel_name_kv(in_dtype: int, d: int, causal: bool, varlen: bool, out_dtype:
     """fa_kernel_name_kv: the kernel fa_fwd_kv runs for this query count."""
     s = load().fa_kernel_name_kv(in_dtype, d, int(causal), int(varlen), out_dtype, Hq, Hkv, Nq)
     return None if s is None else s.decode()
+
+
+def kernel_name_ex(in_dtype: int, d: int, causal: bool, varlen: bool, out_dtype: int,
+                   Hq: int, Hkv: int, Nq: int, sparse: bool = False, vt_packed: bool = False):
+    """fa_kernel_name_ex: the kernel a given entry point runs (block-sparse
+    and/or packed V)."""
+    s = load().fa_kernel_name_ex(in_dtype, d, int(causal), int(varlen), out_dtype, Hq, Hkv, Nq,
+                                 int(sparse), int(vt_packed))
+    return None if s is None else s.decode()
+
+
+def check_seqlens(cu_seqlens_host, B: int, n_max: int) -> int:
+    """fa_check_seqlens on a host int32 array (a numpy array or None)."""
+    if cu_seqlens_host is None:
+        return load().fa_check_seqlens(None, B, n_max)
+    import numpy as np
+    a = np.ascontiguousarray(cu_seqlens_host, dtype=np.int32)
+    return load().fa_check_seqlens(a.ctypes.data, B, n_max)
 
 
 def supported(in_dtype: int, d: int, causal: bool) -> bool:
@@ -163,6 +188,14 @@ def fwd_kv_split_packed_raw(q, k, vt, vt_bytes, o, lse, B, Hq, Hkv, Nq, Nk, d, c
     return load().fa_fwd_kv_split_packed(q, k, vt, vt_bytes, o, lse, B, Hq, Hkv, Nq, Nk, d,
                                          int(causal), scale, cu_q, cu_k, n_splits, part,
                                          part_bytes, stream, in_dtype, out_dtype)
+
+
+def fwd_kv_split_raw(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, cu_q, cu_k,
+                     n_splits, part, part_bytes, stream, in_dtype, out_dtype) -> int:
+    """fa_fwd_kv_split with raw integer device addresses."""
+    return load().fa_fwd_kv_split(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, int(causal), scale,
+                                  cu_q, cu_k, n_splits, part, part_bytes, stream, in_dtype,
+                                  out_dtype)
 
 
 def bwd_workspace_bytes(B, Hq, Hkv, N, d, in_dtype) -> int:

@@ -58,20 +58,23 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
         scale = 1.0 / math.sqrt(d)
     dt = _DT[q.dtype]
     need = _lib.bwd_workspace_bytes(B, Hq, Hkv, N, d, dt)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    elif workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous uint8 device tensor")
-    dq = torch.empty(q.shape, dtype=grad_dtype, device=q.device)
-    dk = torch.empty(k.shape, dtype=grad_dtype, device=q.device)
-    dv = torch.empty(v.shape, dtype=grad_dtype, device=q.device)
-    st = (stream or torch.cuda.current_stream(q.device)).cuda_stream
-    with torch.cuda.device(q.device):
+    stream = stream or torch.cuda.current_stream(q.device)
+    # Tensors made here belong to `stream` (the caching allocator then never
+    # hands their memory to other work before the kernels using it are done).
+    with torch.cuda.device(q.device), torch.cuda.stream(stream):
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        elif (workspace.dtype != torch.uint8 or not workspace.is_cuda
+              or not workspace.is_contiguous()):
+            raise ValueError("workspace must be a contiguous uint8 device tensor")
+        dq = torch.empty(q.shape, dtype=grad_dtype, device=q.device)
+        dk = torch.empty(k.shape, dtype=grad_dtype, device=q.device)
+        dv = torch.empty(v.shape, dtype=grad_dtype, device=q.device)
         status = _lib.bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                               dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                               dv.data_ptr(), B, Hq, Hkv, N, d, causal, float(scale), cu_ptr,
-                              workspace.data_ptr(), workspace.numel(), st, dt, _DT[o.dtype],
-                              _DT[grad_dtype])
+                              workspace.data_ptr(), workspace.numel(), stream.cuda_stream, dt,
+                              _DT[o.dtype], _DT[grad_dtype])
     if status != _lib.FA_OK:
         raise RuntimeError(f"fa_bwd failed ({status}): {_lib.status_string(status)}")
     return dq, dk, dv

@@ -2,6 +2,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -34,6 +35,25 @@ int device_status() {
                     std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
   });
   return g_dev_ok[dev] ? FA_OK : FA_ERR_DEVICE;
+}
+
+// FA_DEBUG=1 in the environment (read once): packed offset arrays are
+// checked on the device before any attention kernel runs.
+bool debug_mode() {
+  static const bool on = [] {
+    const char* e = std::getenv("FA_DEBUG");
+    return e != nullptr && std::strcmp(e, "1") == 0;
+  }();
+  return on;
+}
+
+// The debug check of the query and key offsets of a packed launch (no-op
+// outside debug mode or for fixed-length layouts).
+int debug_seqlens(const int* cu_q, const int* cu_k, int B, int Nq, int Nk, void* stream) {
+  if (!debug_mode() || cu_q == nullptr) return FA_OK;
+  int st = fa::debug_check_seqlens(cu_q, B, Nq, stream);
+  if (st == FA_OK && cu_k != cu_q) st = fa::debug_check_seqlens(cu_k, B, Nk, stream);
+  return st;
 }
 
 }  // namespace
@@ -72,6 +92,8 @@ int fa_fwd_kv_packed(const void* q, const void* k, const void* vt, size_t vt_byt
   if (st != FA_OK) return st;
   st = device_status();
   if (st != FA_OK) return st;
+  st = debug_seqlens(cu_seqlens_q, cu_seqlens_k, B, Nq, Nk, stream);
+  if (st != FA_OK) return st;
   fa::LaunchArgs a{q, k, nullptr, o, lse, vt, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, Nq, Nk,
                    d, causal, scale, in_dtype, out_dtype};
   return fa::launch_fwd(a, stream);
@@ -103,6 +125,8 @@ int fa_fwd_kv_split_packed(const void* q, const void* k, const void* vt, size_t 
   if (st != FA_OK) return st;
   st = device_status();
   if (st != FA_OK) return st;
+  st = debug_seqlens(cu_seqlens_q, cu_seqlens_k, B, Nq, Nk, stream);
+  if (st != FA_OK) return st;
   fa::LaunchArgs a{q, k, nullptr, o, lse, vt, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, Nq, Nk,
                    d, causal, scale, in_dtype, out_dtype};
   if (num_splits > 1) {
@@ -124,38 +148,42 @@ int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
               const int* cu_seqlens_q, const int* cu_seqlens_k, void* stream,
               int in_dtype, int out_dtype) {
+  // One kernel launch reading q, k, v and writing o, lse; no workspace.
   int st = fa::check_args(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale,
                           cu_seqlens_q, cu_seqlens_k, in_dtype, out_dtype);
   if (st != FA_OK) return st;
   st = device_status();
   if (st != FA_OK) return st;
+  st = debug_seqlens(cu_seqlens_q, cu_seqlens_k, B, Nq, Nk, stream);
+  if (st != FA_OK) return st;
   fa::LaunchArgs a{q, k, v, o, lse, nullptr, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, Nq, Nk,
                    d, causal, scale, in_dtype, out_dtype};
-  if (in_dtype == FA_F32) return fa::launch_fwd(a, stream);
-  // 16-bit inputs: pack V^T into a stream-ordered workspace (plus split-KV
-  // partials for decode-like shapes), run, release.
-  const uint64_t need = fa::workspace_bytes(B, Hkv, Nk, d, in_dtype);
-  if (need / (128ull * (uint64_t)d) > (uint64_t)INT32_MAX || need > (uint64_t)SIZE_MAX)
-    return FA_ERR_SHAPE;
-  const int n_splits = fa::suggest_splits(B, Hq, Hkv, Nq, Nk, d, in_dtype, device_cus());
-  const uint64_t part = n_splits > 1 ? fa::split_workspace_bytes(B, Hq, Nq, d, n_splits) : 0;
-  const uint64_t vt_pad = (need + 255) & ~255ull;
-  if (part > (uint64_t)SIZE_MAX - vt_pad) return FA_ERR_SHAPE;
-  void* ws = nullptr;
-  if (hipMallocAsync(&ws, (size_t)(vt_pad + part), (hipStream_t)stream) != hipSuccess || !ws)
-    return FA_ERR_ALLOC;
-  st = fa::launch_vt_pack(v, ws, B, Hkv, Nk, d, cu_seqlens_k, in_dtype, stream);
-  if (st == FA_OK) {
-    a.vt = ws;
-    if (n_splits > 1) {
-      a.n_splits = n_splits;
-      a.o_part = (float*)((char*)ws + vt_pad);
-      a.lse_part = (float*)((char*)ws + vt_pad + (size_t)n_splits * B * Hq * Nq * d * 4);
-    }
-    st = fa::launch_fwd(a, stream);
+  return fa::launch_fwd(a, stream);
+}
+
+int fa_fwd_kv_split(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                    int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int num_splits,
+                    void* part, size_t part_bytes, void* stream, int in_dtype, int out_dtype) {
+  int st = fa::check_args(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale,
+                          cu_seqlens_q, cu_seqlens_k, in_dtype, out_dtype);
+  if (st != FA_OK) return st;
+  if (in_dtype == FA_F32) return FA_ERR_DTYPE;
+  st = fa::check_split_args(part, part_bytes, o, lse, B, Hq, Hkv, Nq, Nk, d, num_splits,
+                            in_dtype, out_dtype, cu_seqlens_q != nullptr);
+  if (st != FA_OK) return st;
+  st = device_status();
+  if (st != FA_OK) return st;
+  st = debug_seqlens(cu_seqlens_q, cu_seqlens_k, B, Nq, Nk, stream);
+  if (st != FA_OK) return st;
+  fa::LaunchArgs a{q, k, v, o, lse, nullptr, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, Nq, Nk,
+                   d, causal, scale, in_dtype, out_dtype};
+  if (num_splits > 1) {
+    a.n_splits = num_splits;
+    a.o_part = (float*)part;
+    a.lse_part = (float*)((char*)part + (size_t)num_splits * B * Hq * Nq * d * 4);
   }
-  if (hipFreeAsync(ws, (hipStream_t)stream) != hipSuccess && st == FA_OK) st = FA_ERR_LAUNCH;
-  return st;
+  return fa::launch_fwd(a, stream);
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -179,6 +207,8 @@ int fa_fwd_sparse_packed(const void* q, const void* k, const void* vt, size_t vt
   if (st != FA_OK) return st;
   st = device_status();
   if (st != FA_OK) return st;
+  st = debug_seqlens(cu_seqlens_q, cu_seqlens_k, B, Nq, Nk, stream);
+  if (st != FA_OK) return st;
   fa::LaunchArgs a{q, k, nullptr, o, lse, vt, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, Nq, Nk,
                    d, causal, scale, in_dtype, out_dtype};
   a.block_mask = block_mask;
@@ -200,23 +230,14 @@ int fa_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* l
   if (st != FA_OK) return st;
   st = device_status();
   if (st != FA_OK) return st;
-  const uint64_t need = fa::workspace_bytes(B, Hkv, Nk, d, in_dtype);
-  if (need / (128ull * (uint64_t)d) > (uint64_t)INT32_MAX || need > (uint64_t)SIZE_MAX)
-    return FA_ERR_SHAPE;
-  void* ws = nullptr;
-  if (hipMallocAsync(&ws, (size_t)need, (hipStream_t)stream) != hipSuccess || !ws)
-    return FA_ERR_ALLOC;
-  st = fa::launch_vt_pack(v, ws, B, Hkv, Nk, d, cu_seqlens_k, in_dtype, stream);
-  if (st == FA_OK) {
-    fa::LaunchArgs a{q, k, v, o, lse, ws, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, Nq, Nk,
-                     d, causal, scale, in_dtype, out_dtype};
-    a.block_mask = block_mask;
-    a.mask_batches = mask_batches;
-    a.mask_heads = mask_heads;
-    st = fa::launch_fwd(a, stream);
-  }
-  if (hipFreeAsync(ws, (hipStream_t)stream) != hipSuccess && st == FA_OK) st = FA_ERR_LAUNCH;
-  return st;
+  st = debug_seqlens(cu_seqlens_q, cu_seqlens_k, B, Nq, Nk, stream);
+  if (st != FA_OK) return st;
+  fa::LaunchArgs a{q, k, v, o, lse, nullptr, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, Nq, Nk,
+                   d, causal, scale, in_dtype, out_dtype};
+  a.block_mask = block_mask;
+  a.mask_batches = mask_batches;
+  a.mask_heads = mask_heads;
+  return fa::launch_fwd(a, stream);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int in_dtype) {
@@ -237,6 +258,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   if (st != FA_OK) return st;
   st = device_status();
   if (st != FA_OK) return st;
+  st = debug_seqlens(cu_seqlens, cu_seqlens, B, N, N, stream);
+  if (st != FA_OK) return st;
   return fa::launch_bwd(a, stream);
 }
 
@@ -249,6 +272,18 @@ const char* fa_kernel_name_kv(int in_dtype, int d, int causal, int varlen, int o
                               int Hq, int Hkv, int Nq) {
   if (Hkv < 1 || Hq < 1 || Nq < 1) return nullptr;
   return fa::kernel_name_kv(in_dtype, d, causal, varlen, out_dtype, Hq, Hkv, Nq);
+}
+
+const char* fa_kernel_name_ex(int in_dtype, int d, int causal, int varlen, int out_dtype,
+                              int Hq, int Hkv, int Nq, int sparse, int vt_packed) {
+  if (Hkv < 1 || Hq < 1 || Nq < 1) return nullptr;
+  return fa::kernel_name_kv(in_dtype, d, causal, varlen, out_dtype, Hq, Hkv, Nq, sparse,
+                            vt_packed);
+}
+
+int fa_check_seqlens(const int* cu_seqlens, int B, int n_max) {
+  if (B < 0) return FA_ERR_SHAPE;
+  return fa::check_seqlens(cu_seqlens, B, n_max);
 }
 
 int fa_supported(int in_dtype, int d, int causal) {
@@ -266,15 +301,16 @@ const char* fa_status_string(int status) {
     case FA_ERR_DTYPE: return "bad dtype: in_dtype F32/F16/BF16, out_dtype F32 or in_dtype";
     case FA_ERR_ALIGN: return "misaligned pointer: q, k, v, o need 16 bytes, lse and cu_seqlens 4";
     case FA_ERR_ALIAS: return "o overlaps q, k, v or lse";
-    case FA_ERR_SCALE: return "scale must be finite and > 0";
+    case FA_ERR_SCALE: return "scale must be finite (and > 0 for the backward)";
     case FA_ERR_DEVICE: return "no usable device: the current HIP device is not gfx950";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_WORKSPACE: return "workspace too small: see fa_workspace_bytes";
-    case FA_ERR_ALLOC: return "could not allocate the device workspace";
+    case FA_ERR_ALLOC: return "could not allocate device memory (no entry point allocates)";
+    case FA_ERR_SEQLENS: return "corrupt cu_seqlens: cu[0] != 0, decreasing, or a length above N";
     default: return "unknown status";
   }
 }
 
-int fa_version(void) { return 1 * 10000 + 1 * 100 + 0; }
+int fa_version(void) { return 1 * 10000 + 2 * 100 + 0; }
 
 }  // extern "C"

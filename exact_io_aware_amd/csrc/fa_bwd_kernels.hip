@@ -677,10 +677,6 @@ static BwdLayout bwd_layout(int B, int Hq, int Hkv, int N, int d) {
   return l;
 }
 
-uint64_t bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
-  return bwd_layout(B, Hq, Hkv, N, d).total;
-}
-
 int launch_bwd(const BwdArgs& a, void* stream) {
   const bool varlen = a.cu_seqlens != nullptr;
   const BwdVariant* var = nullptr;

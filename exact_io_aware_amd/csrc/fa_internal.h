@@ -7,7 +7,32 @@
 
 #include "fa.h"
 
+// Functions also compiled for the device where hipcc builds them (plain C++
+// elsewhere, e.g. the host-only sanitizer build of the argument checks).
+#if defined(__HIPCC__)
+#define FA_HD __host__ __device__
+#else
+#define FA_HD
+#endif
+
 namespace fa {
+
+// Entry i (0 .. B) of a packed offset array is valid if cu[0] = 0 and
+// 0 <= cu[i] - cu[i-1] <= n_max (offsets non-decreasing, no sequence longer
+// than the bound that sized the launch).  prev = cu[i-1] (unused for i = 0).
+FA_HD inline bool seqlens_entry_ok(int i, int prev, int cur, int n_max) {
+  if (i == 0) return cur == 0;
+  const long long len = (long long)cur - (long long)prev;
+  return len >= 0 && len <= (long long)n_max;
+}
+
+// The whole array (host memory): FA_OK or FA_ERR_SEQLENS.
+inline int check_seqlens(const int* cu, int B, int n_max) {
+  if (!cu) return FA_ERR_NULL;
+  for (int i = 0; i <= B; ++i)
+    if (!seqlens_entry_ok(i, i > 0 ? cu[i - 1] : 0, cu[i], n_max)) return FA_ERR_SEQLENS;
+  return FA_OK;
+}
 
 // Query rows each wave owns (multiples of 32; with 64 the two 32-row blocks
 // share every K/V operand read from LDS).
@@ -50,7 +75,7 @@ inline Plan make_plan_nw(int B, int Hq, int Hkv, int N, int in_dtype, int nw) {
   if (in_dtype == FA_F32) p.hp = 1;
   else p.hp = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
   p.rows_per_wg = nw * rows_per_wave(in_dtype) / p.hp;
-  p.n_rblocks = (N + p.rows_per_wg - 1) / p.rows_per_wg;
+  p.n_rblocks = (int)(((long long)N + p.rows_per_wg - 1) / p.rows_per_wg);
   p.n_hgroups = Hq / p.hp;
   p.total_wg = (uint64_t)B * (uint64_t)p.n_hgroups * (uint64_t)p.n_rblocks;
   return p;
@@ -62,7 +87,12 @@ inline Plan make_plan(int B, int Hq, int Hkv, int N, int d, int in_dtype, bool c
 }
 
 // 64-key V^T tiles per (sequence, K/V head) in the packed-V workspace.
-inline int vt_tiles(int N) { return (N + 63) / 64; }
+inline int vt_tiles(int N) { return (int)(((long long)N + 63) / 64); }
+
+// Longest sequence (query or key count) the kernels take: their int index
+// arithmetic (a row or key plus a tile or block size) stays far from
+// overflow below it.
+constexpr int kMaxSeqLen = 1 << 30;
 
 // Bytes of the packed V^T workspace: B * Hkv * vt_tiles(N) tiles of d rows x
 // 64 keys in 16 bits.  fp32 inputs need none.  Saturates at UINT64_MAX.
@@ -74,13 +104,16 @@ inline uint64_t workspace_bytes(int B, int Hkv, int N, int d, int in_dtype) {
 }
 
 inline uint64_t grid_size(int B, int Hq, int Hkv, int N, int d, int in_dtype) {
-  // The larger of the two forward grids (with and without the mask).
+  // The larger of the two forward grids (with and without the mask);
+  // UINT64_MAX (never a valid grid) for sizes the plan is not defined for.
+  if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || Hq % Hkv != 0) return UINT64_MAX;
   return make_plan(B, Hq, Hkv, N, d, in_dtype, true).total_wg;
 }
 
 // Checks of the attention arguments (Nq queries, Nk keys per sequence; the
 // fa_fwd form has Nq = Nk and one offset array).  v_bytes is the extent of
-// v used for the overlap test with o (0: the size of V itself).
+// v used for the overlap test with o (0: the size of V itself).  Any finite
+// scale is accepted.
 int check_args(const void* q, const void* k, const void* v, const void* o,
                const float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
                int causal, float scale, const int* cu_seqlens_q, const int* cu_seqlens_k,
@@ -167,16 +200,34 @@ struct BwdArgs {
   int in_dtype, o_dtype, grad_dtype;
   void* workspace;
 };
-uint64_t bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
+// Bytes of the backward's workspace: the rows' D and L * log2(e), fp32
+// [B][Hq][N] each, each padded to 256 bytes (as laid out by the backward's
+// launch).  Saturates at UINT64_MAX; 0 for non-positive sizes.
+inline uint64_t bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
+  (void)Hkv;
+  (void)d;
+  if (B < 1 || Hq < 1 || N < 1) return 0;
+  const uint64_t rows = (uint64_t)B * (uint64_t)Hq * (uint64_t)N;   // < 2^93: checked below
+  if ((uint64_t)B * (uint64_t)Hq > UINT64_MAX / (uint64_t)N || rows > (UINT64_MAX - 512) / 8)
+    return UINT64_MAX;
+  return 2 * ((rows * 4 + 255) & ~255ull);
+}
 int check_bwd_args(const BwdArgs& a, uint64_t ws_bytes);
 int launch_bwd(const BwdArgs& a, void* stream);
 
 // Static name of the kernel instance for these settings, or nullptr.
 const char* kernel_name(int in_dtype, int d, int causal, int varlen, int out_dtype);
 // The same for fa_fwd_kv with Hq, Hkv and the query count Nq (the decode
-// kernel where use_decode holds).
+// kernel where use_decode holds), block-sparse or not, and with V packed
+// (vpack) or row-major.
 const char* kernel_name_kv(int in_dtype, int d, int causal, int varlen, int out_dtype, int Hq,
-                           int Hkv, int Nq);
+                           int Hkv, int Nq, int sparse = 0, int vpack = 0);
+
+// Debug mode (FA_DEBUG=1): check a packed offset array (B + 1 entries in
+// device memory) on `stream` and wait for the verdict: FA_OK,
+// FA_ERR_SEQLENS if an entry fails seqlens_entry_ok, or FA_ERR_LAUNCH.
+// Synchronises `stream`; calls are serialised.
+int debug_check_seqlens(const int* cu, int B, int n_max, void* stream);
 
 }  // namespace fa
 

@@ -32,12 +32,13 @@ int check_args(const void* q, const void* k, const void* v, const void* o,
   if ((cu_seqlens_q == nullptr) != (cu_seqlens_k == nullptr)) return FA_ERR_NULL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || (causal != 0 && causal != 1))
     return FA_ERR_SHAPE;
+  if (Nq > kMaxSeqLen || Nk > kMaxSeqLen) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
   if (Hq % Hkv != 0) return FA_ERR_GQA;
   if (in_dtype != FA_F32 && in_dtype != FA_F16 && in_dtype != FA_BF16)
     return FA_ERR_DTYPE;
   if (out_dtype != FA_F32 && out_dtype != in_dtype) return FA_ERR_DTYPE;
-  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_SCALE;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
 
   // Element counts; the packed layout's token counts are bounded by B * Nq
   // and B * Nk.
@@ -154,6 +155,8 @@ int check_bwd_args(const BwdArgs& a, uint64_t ws_bytes) {
   const int st = check_args(a.q, a.k, a.v, a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.N, a.d, a.causal,
                             a.scale, a.cu_seqlens, a.cu_seqlens, a.in_dtype, a.o_dtype);
   if (st != FA_OK) return st;
+  // The backward kernels take the scale as given (no sign folding).
+  if (!(a.scale > 0.0f)) return FA_ERR_SCALE;
   if (a.in_dtype == FA_F32) return FA_ERR_DTYPE;
   if (a.grad_dtype != FA_F32 && a.grad_dtype != a.in_dtype) return FA_ERR_DTYPE;
   auto mis = [](const void* p, uintptr_t al) { return ((uintptr_t)p) % al != 0; };
@@ -190,7 +193,7 @@ int check_bwd_args(const BwdArgs& a, uint64_t ws_bytes) {
 int check_pack_args(const void* v, const void* vt, uint64_t vt_bytes, int B, int Hkv, int N,
                     int d, const int* cu_seqlens, int in_dtype) {
   if (!v || !vt) return FA_ERR_NULL;
-  if (B < 1 || Hkv < 1 || N < 1) return FA_ERR_SHAPE;
+  if (B < 1 || Hkv < 1 || N < 1 || N > kMaxSeqLen) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
   if (in_dtype != FA_F16 && in_dtype != FA_BF16) return FA_ERR_DTYPE;
   uint64_t rows, vn;

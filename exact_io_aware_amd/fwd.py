@@ -31,8 +31,9 @@ def pack_v(v: torch.Tensor, *, cu_seqlens: Optional[torch.Tensor] = None,
            max_seqlen: Optional[int] = None, out: Optional[torch.Tensor] = None,
            stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
     """fa_pack_v: V (float16/bfloat16, layout as in ``fwd``) transposed into
-    64-key tiles, the form ``fwd(..., vt=...)`` reads.  Returns the packed
-    uint8 workspace (``out`` if given; it must hold fa_workspace_bytes)."""
+    64-key tiles, the form ``fwd(..., vt=...)`` reads (a decode cache's
+    layout).  Returns the packed uint8 tensor (``out`` if given; it must hold
+    fa_workspace_bytes)."""
     if v.dtype not in (torch.float16, torch.bfloat16):
         raise ValueError("pack_v takes float16 or bfloat16 values")
     if not v.is_cuda or not v.is_contiguous():
@@ -51,14 +52,16 @@ def pack_v(v: torch.Tensor, *, cu_seqlens: Optional[torch.Tensor] = None,
         N = _max_seqlen(cu_seqlens, max_seqlen)
         cu_ptr = cu_seqlens.data_ptr()
     nbytes = _lib.workspace_bytes(B, Hkv, N, d, _DT[v.dtype])
-    if out is None:
-        out = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=v.device)
-    elif out.dtype != torch.uint8 or not out.is_cuda or not out.is_contiguous():
-        raise ValueError("out must be a contiguous uint8 device tensor")
-    st = (stream or torch.cuda.current_stream(v.device)).cuda_stream
-    with torch.cuda.device(v.device):
+    stream = stream or torch.cuda.current_stream(v.device)
+    # Tensors made here belong to `stream` (the caching allocator then never
+    # hands their memory to other work before the kernel reading it is done).
+    with torch.cuda.device(v.device), torch.cuda.stream(stream):
+        if out is None:
+            out = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=v.device)
+        elif out.dtype != torch.uint8 or not out.is_cuda or not out.is_contiguous():
+            raise ValueError("out must be a contiguous uint8 device tensor")
         status = _lib.pack_v_raw(v.data_ptr(), out.data_ptr(), out.numel(), B, Hkv, N, d,
-                                 cu_ptr, st, _DT[v.dtype])
+                                 cu_ptr, stream.cuda_stream, _DT[v.dtype])
     if status != _lib.FA_OK:
         raise RuntimeError(f"fa_pack_v failed ({status}): {_lib.status_string(status)}")
     return out
@@ -69,7 +72,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor], *, causal: 
         max_seqlen: Optional[int] = None, out_dtype: torch.dtype = torch.float32,
         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
         stream: Optional[torch.cuda.Stream] = None, vt: Optional[torch.Tensor] = None,
-        library_workspace: bool = False, cu_seqlens_k: Optional[torch.Tensor] = None,
+        cu_seqlens_k: Optional[torch.Tensor] = None,
         max_seqlen_k: Optional[int] = None, num_splits: Optional[int] = None,
         split_workspace: Optional[torch.Tensor] = None,
         block_mask: Optional[torch.Tensor] = None):
@@ -85,27 +88,27 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor], *, causal: 
     When a sequence has fewer queries than keys, the queries are its last
     tokens (chunked prefill): with ``causal`` query row r sees keys
     ``c <= r + nk - nq``.
-    ``lse`` is float32 ``[B, Hq, Nq]``.  ``scale`` defaults to 1/sqrt(d).
-    ``out``/``lse`` may be given to write into existing buffers.
-    The kernels are enqueued on ``stream`` (default: the current stream).
+    ``lse`` is float32 ``[B, Hq, Nq]``.  ``scale`` defaults to 1/sqrt(d);
+    any finite value is accepted.  ``out``/``lse`` may be given to write into
+    existing buffers.  The kernels are enqueued on ``stream`` (default: the
+    current stream), and tensors made here belong to that stream.
 
-    16-bit inputs: V is first packed (``pack_v``) into a workspace from
-    torch's allocator, then fa_fwd_packed (fa_fwd_kv_packed) runs.  ``vt``
-    passes V already packed by ``pack_v`` (``v`` may then be None).
-    ``library_workspace`` calls fa_fwd (fa_fwd_kv) instead, which allocates
-    its own stream-ordered workspace.
+    The default path is fa_fwd (fa_fwd_kv): one launch, no workspace.
+    ``vt`` passes V already packed by ``pack_v`` (``v`` may then be None):
+    the *_packed entry points.
 
-    Split-KV (16-bit, packed path): ``num_splits`` ranges of keys per unit,
-    merged with their logsumexps (fa_fwd_kv_split_packed); default
-    fa_num_splits, which splits only decode-like shapes (at most 64 query
-    rows per sequence) that would not fill the GPU.  ``split_workspace``
-    (uint8, fa_split_workspace_bytes) may be passed to avoid an allocation.
+    Split-KV (16-bit): ``num_splits`` ranges of keys per unit, merged with
+    their logsumexps (fa_fwd_kv_split, or fa_fwd_kv_split_packed with
+    ``vt``); default fa_num_splits, which splits only decode-like shapes (at
+    most 64 query rows per sequence) that would not fill the GPU.  The
+    partials go to ``split_workspace`` (uint8, fa_split_workspace_bytes) or
+    to a tensor made here.  ``num_splits=1`` never splits.
 
     Block-sparse (16-bit): ``block_mask`` is a contiguous uint8 device
     tensor ``[1 or B, 1 or Hq, ceil(Nq/64), ceil(Nk/64)]``; a nonzero entry
     (b, h, i, j) admits query rows [64i, 64i+64) of sequence b, head h
-    against keys [64j, 64j+64) (fa_fwd_sparse_packed, or fa_fwd_sparse with
-    ``library_workspace``).  Rows that see no key get O = 0, L = -inf.
+    against keys [64j, 64j+64) (fa_fwd_sparse, or fa_fwd_sparse_packed with
+    ``vt``).  Rows that see no key get O = 0, L = -inf.
     """
     if v is None and vt is None:
         raise ValueError("v is needed unless a packed vt is given")
@@ -154,44 +157,43 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor], *, causal: 
     same = Nk == N and cuk_ptr == cu_ptr
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
-    elif out.dtype != out_dtype or out.shape != q.shape or not out.is_contiguous():
-        raise ValueError("out has the wrong dtype, shape or layout")
-    if lse is None:
-        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    elif lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, N) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor [B, Hq, Nq]")
-    stream = stream or torch.cuda.current_stream(q.device)
-    st = stream.cuda_stream
-    packed = q.dtype != torch.float32 and not library_workspace
-    if vt is not None and not packed:
-        raise ValueError("vt is used for 16-bit inputs without library_workspace only")
-    if packed and vt is None:
-        vt = pack_v(v, cu_seqlens=cu_seqlens_k if cu_seqlens_k is not None else cu_seqlens,
-                    max_seqlen=Nk if cu_seqlens is not None else None, stream=stream)
+    packed = vt is not None
+    if packed and q.dtype == torch.float32:
+        raise ValueError("vt (packed V) is for float16/bfloat16 inputs")
     if packed and (vt.dtype != torch.uint8 or not vt.is_cuda or not vt.is_contiguous()):
         raise ValueError("vt must be the contiguous uint8 device tensor pack_v returns")
     dt, odt = _DT[q.dtype], _DT[out_dtype]
-    if block_mask is not None:
-        if q.dtype == torch.float32:
-            raise ValueError("block_mask needs float16 or bfloat16 inputs")
-        nqb, nkb = -(-N // 64), -(-Nk // 64)
-        if (block_mask.dtype != torch.uint8 or not block_mask.is_cuda
-                or not block_mask.is_contiguous() or block_mask.dim() != 4
-                or block_mask.shape[0] not in (1, B) or block_mask.shape[1] not in (1, Hq)
-                or tuple(block_mask.shape[2:]) != (nqb, nkb)):
-            raise ValueError(f"block_mask must be a contiguous uint8 device tensor "
-                             f"[1 or {B}, 1 or {Hq}, {nqb}, {nkb}]")
-        if num_splits not in (None, 1):
-            raise ValueError("block-sparse attention does not split over keys")
-        mb, mh = int(block_mask.shape[0]), int(block_mask.shape[1])
-        with torch.cuda.device(q.device):
+    stream = stream or torch.cuda.current_stream(q.device)
+    st = stream.cuda_stream
+    with torch.cuda.device(q.device), torch.cuda.stream(stream):
+        if out is None:
+            out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+        elif out.dtype != out_dtype or out.shape != q.shape or not out.is_contiguous():
+            raise ValueError("out has the wrong dtype, shape or layout")
+        if lse is None:
+            lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+        elif (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, N)
+              or not lse.is_contiguous()):
+            raise ValueError("lse must be a contiguous float32 tensor [B, Hq, Nq]")
+        vtp, vtn = (vt.data_ptr(), vt.numel()) if packed else (0, 0)
+        if block_mask is not None:
+            if q.dtype == torch.float32:
+                raise ValueError("block_mask needs float16 or bfloat16 inputs")
+            nqb, nkb = -(-N // 64), -(-Nk // 64)
+            if (block_mask.dtype != torch.uint8 or not block_mask.is_cuda
+                    or not block_mask.is_contiguous() or block_mask.dim() != 4
+                    or block_mask.shape[0] not in (1, B) or block_mask.shape[1] not in (1, Hq)
+                    or tuple(block_mask.shape[2:]) != (nqb, nkb)):
+                raise ValueError(f"block_mask must be a contiguous uint8 device tensor "
+                                 f"[1 or {B}, 1 or {Hq}, {nqb}, {nkb}]")
+            if num_splits not in (None, 1):
+                raise ValueError("block-sparse attention does not split over keys")
+            mb, mh = int(block_mask.shape[0]), int(block_mask.shape[1])
             if packed:
                 name = "fa_fwd_sparse_packed"
                 status = _lib.fwd_sparse_packed_raw(
-                    q.data_ptr(), k.data_ptr(), vt.data_ptr(), vt.numel(), out.data_ptr(),
-                    lse.data_ptr(), B, Hq, Hkv, N, Nk, d, causal, float(scale), cu_ptr, cuk_ptr,
+                    q.data_ptr(), k.data_ptr(), vtp, vtn, out.data_ptr(), lse.data_ptr(), B, Hq,
+                    Hkv, N, Nk, d, causal, float(scale), cu_ptr, cuk_ptr,
                     block_mask.data_ptr(), mb, mh, st, dt, odt)
             else:
                 name = "fa_fwd_sparse"
@@ -199,38 +201,43 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor], *, causal: 
                     q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B,
                     Hq, Hkv, N, Nk, d, causal, float(scale), cu_ptr, cuk_ptr,
                     block_mask.data_ptr(), mb, mh, st, dt, odt)
-        if status != _lib.FA_OK:
-            raise RuntimeError(f"{name} failed ({status}): {_lib.status_string(status)}")
-        return out, lse
-    n_splits = 1
-    if packed:
-        with torch.cuda.device(q.device):
+            if status != _lib.FA_OK:
+                raise RuntimeError(f"{name} failed ({status}): {_lib.status_string(status)}")
+            return out, lse
+        n_splits = 1
+        if q.dtype != torch.float32:
             n_splits = (_lib.num_splits(B, Hq, Hkv, N, Nk, d, dt) if num_splits is None
                         else int(num_splits))
-    with torch.cuda.device(q.device):
-        if packed and n_splits > 1:
-            name = "fa_fwd_kv_split_packed"
+        if n_splits > 1:
             need = _lib.split_workspace_bytes(B, Hq, N, d, n_splits)
             if split_workspace is None:
                 split_workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
             elif (split_workspace.dtype != torch.uint8 or not split_workspace.is_cuda
                   or not split_workspace.is_contiguous()):
                 raise ValueError("split_workspace must be a contiguous uint8 device tensor")
-            status = _lib.fwd_kv_split_packed_raw(
-                q.data_ptr(), k.data_ptr(), vt.data_ptr(), vt.numel(), out.data_ptr(),
-                lse.data_ptr(), B, Hq, Hkv, N, Nk, d, causal, float(scale), cu_ptr, cuk_ptr,
-                n_splits, split_workspace.data_ptr(), split_workspace.numel(), st, dt, odt)
+            if packed:
+                name = "fa_fwd_kv_split_packed"
+                status = _lib.fwd_kv_split_packed_raw(
+                    q.data_ptr(), k.data_ptr(), vtp, vtn, out.data_ptr(), lse.data_ptr(), B, Hq,
+                    Hkv, N, Nk, d, causal, float(scale), cu_ptr, cuk_ptr, n_splits,
+                    split_workspace.data_ptr(), split_workspace.numel(), st, dt, odt)
+            else:
+                name = "fa_fwd_kv_split"
+                status = _lib.fwd_kv_split_raw(
+                    q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B,
+                    Hq, Hkv, N, Nk, d, causal, float(scale), cu_ptr, cuk_ptr, n_splits,
+                    split_workspace.data_ptr(), split_workspace.numel(), st, dt, odt)
         elif packed and same:
             name = "fa_fwd_packed"
-            status = _lib.fwd_packed_raw(q.data_ptr(), k.data_ptr(), vt.data_ptr(), vt.numel(),
-                                         out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, N, d,
-                                         causal, float(scale), cu_ptr, st, dt, odt)
+            status = _lib.fwd_packed_raw(q.data_ptr(), k.data_ptr(), vtp, vtn, out.data_ptr(),
+                                         lse.data_ptr(), B, Hq, Hkv, N, d, causal, float(scale),
+                                         cu_ptr, st, dt, odt)
         elif packed:
             name = "fa_fwd_kv_packed"
-            status = _lib.fwd_kv_packed_raw(q.data_ptr(), k.data_ptr(), vt.data_ptr(),
-                                            vt.numel(), out.data_ptr(), lse.data_ptr(), B, Hq,
-                                            Hkv, N, Nk, d, causal, float(scale), cu_ptr,
-                                            cuk_ptr, st, dt, odt)
+            status = _lib.fwd_kv_packed_raw(q.data_ptr(), k.data_ptr(), vtp, vtn,
+                                            out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, N, Nk,
+                                            d, causal, float(scale), cu_ptr, cuk_ptr, st, dt,
+                                            odt)
         elif same:
             name = "fa_fwd"
             status = _lib.fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),

@@ -43,18 +43,19 @@
  * written in out_dtype, which is FA_F32 or in_dtype.  Scores, softmax
  * statistics and accumulators are fp32; P is rounded to in_dtype (round to
  * nearest even) for the P.V contraction; the normaliser is summed from the
- * unrounded fp32 P.
+ * unrounded fp32 P (bf16) or from the rounded P the P.V contraction uses
+ * (fp16).
  *
  * Supported: d in {64, 128}; B, Hq, Hkv, N >= 1; Hq % Hkv == 0; causal in
- * {0, 1}; scale finite and > 0.  No dropout, no arbitrary mask.
+ * {0, 1}; any finite scale (scale < 0 is computed as |scale| with Q
+ * negated, scale = 0 as Q = 0: both exact).  No dropout, no arbitrary mask.
  *
  * Ownership and threading: every pointer is a device pointer owned by the
- * caller.  For 16-bit inputs fa_fwd takes a stream-ordered device workspace
- * of fa_workspace_bytes() bytes (hipMallocAsync / hipFreeAsync on `stream`)
- * for a transposed copy of V; callers that manage memory themselves call
- * fa_pack_v and fa_fwd_packed with a workspace of their own instead, and the
- * library then allocates nothing.  The library keeps no per-call state and
- * never synchronises.  The work is enqueued on `stream` (a hipStream_t;
+ * caller.  fa_fwd (and fa_fwd_kv, fa_fwd_sparse) is one kernel launch that
+ * reads q, k, v and writes o and lse: it allocates nothing, keeps no
+ * workspace and no per-call state, never splits the keys over workgroups
+ * and never synchronises (V is read transposed on chip, so no transposed
+ * copy of it is made).  The work is enqueued on `stream` (a hipStream_t;
  * NULL is the default stream) and fa_fwd returns at once.  Calls are
  * thread-safe; calls on different streams may run concurrently.  o must not
  * overlap q, k, v or lse.
@@ -63,9 +64,18 @@
  * nothing is launched and a negative fa_status is returned.  Pointers q, k,
  * v, o must be 16-byte aligned, lse and cu_seqlens 4-byte aligned.  A device
  * that is not gfx950 gives FA_ERR_DEVICE; a launch failure gives
- * FA_ERR_LAUNCH.  Corrupt cu_seqlens contents (decreasing offsets, a length
- * above N, offsets past the buffers) are not detected: the caller must pass
- * valid offsets.  Nothing is printed and no exception crosses the ABI.
+ * FA_ERR_LAUNCH.  Corrupt cu_seqlens contents (cu[0] != 0, decreasing
+ * offsets, a length above N) are not detected in normal operation, where
+ * checking them would need a device-to-host read: the caller must pass valid
+ * offsets.  With the environment variable FA_DEBUG=1 (read once per
+ * process) every entry point that takes packed offsets first checks them
+ * on the device and waits for the verdict: corrupt offsets give
+ * FA_ERR_SEQLENS and no attention kernel runs.  That mode synchronises the
+ * stream (it cannot be captured into a graph) and serialises the checks of
+ * concurrent calls.  The Kotaemon page's caveats warn that a misconfigured
+ * fast path fails silently; this mode makes that failure loud.  Offsets
+ * past the caller's buffers cannot be detected (their extent is not
+ * passed).  Nothing is printed and no exception crosses the ABI.
  */
 #ifndef FA_H
 #define FA_H
@@ -87,11 +97,12 @@ typedef enum {
   FA_ERR_DTYPE = -5,    /* unknown in_dtype, or out_dtype not in {FA_F32, in_dtype} */
   FA_ERR_ALIGN = -6,    /* pointer misaligned */
   FA_ERR_ALIAS = -7,    /* o overlaps q, k, v or lse */
-  FA_ERR_SCALE = -8,    /* scale not finite or not > 0 */
+  FA_ERR_SCALE = -8,    /* scale not finite (backward: or not > 0) */
   FA_ERR_DEVICE = -9,   /* current device is not gfx950, or no device */
   FA_ERR_LAUNCH = -10,  /* the kernel launch failed */
-  FA_ERR_WORKSPACE = -11, /* vt_bytes below fa_workspace_bytes() */
-  FA_ERR_ALLOC = -12    /* fa_fwd could not allocate its workspace */
+  FA_ERR_WORKSPACE = -11, /* a caller workspace below its stated size */
+  FA_ERR_ALLOC = -12,   /* reserved: no entry point allocates memory */
+  FA_ERR_SEQLENS = -13  /* FA_DEBUG=1 only: corrupt cu_seqlens contents */
 } fa_status;
 
 /* Exact attention forward (see the header comment).  q, k, v: inputs in
@@ -101,17 +112,17 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int Hq, int Hkv, int N, int d, int causal, float scale,
            const int* cu_seqlens, void* stream, int in_dtype, int out_dtype);
 
-/* Bytes of the packed-V workspace that fa_pack_v fills and fa_fwd_packed
- * reads, for 16-bit inputs: B * Hkv * ceil(N / 64) tiles of d * 64 values
- * (d * 128 bytes each).  0 for fp32 inputs (which need none) and for
- * unsupported d or dtype.
+/* Bytes of the packed-V layout that fa_pack_v fills and the *_packed entry
+ * points read, for 16-bit inputs: B * Hkv * ceil(N / 64) tiles of d * 64
+ * values (d * 128 bytes each).  0 for fp32 inputs and for unsupported d or
+ * dtype.
  *
  * Why (a gfx950 design choice, not from the pages): the P.V product of each
- * key block takes V^T as its matrix operand.  Transposing V once per forward
- * pass, in a streaming pre-pass that reads and writes V once, lets the
- * attention kernel, which brings every V block on chip once per query
- * block, read it with plain 16-byte LDS reads instead of slower transposing
- * reads. */
+ * key block takes V^T as its matrix operand.  fa_fwd reads V's rows into
+ * on-chip memory and transposes them there (two transposing reads per
+ * operand).  A decode loop, which keeps its K/V cache from call to call, can
+ * keep V in this packed form instead (the operand is then one 16-byte read)
+ * and re-pack only the tile holding each new token. */
 size_t fa_workspace_bytes(int B, int Hkv, int N, int d, int in_dtype);
 
 /* Pack V (layout as for fa_fwd, in_dtype FA_F16 or FA_BF16) into vt: for
@@ -130,8 +141,8 @@ int fa_pack_v(const void* v, void* vt, size_t vt_bytes, int B, int Hkv, int N, i
 /* fa_fwd for 16-bit inputs with V given as fa_pack_v's output vt (packed
  * with the same B, Hkv, N, d, cu_seqlens and in_dtype, and enqueued before
  * this call on the same stream, or otherwise complete).  Same results as
- * fa_fwd; allocates nothing.  Errors as fa_fwd, plus FA_ERR_WORKSPACE, and
- * FA_ERR_DTYPE for fp32 inputs. */
+ * fa_fwd, bit for bit; allocates nothing.  Errors as fa_fwd, plus
+ * FA_ERR_WORKSPACE, and FA_ERR_DTYPE for fp32 inputs. */
 int fa_fwd_packed(const void* q, const void* k, const void* vt, size_t vt_bytes, void* o,
                   float* lse, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                   const int* cu_seqlens, void* stream, int in_dtype, int out_dtype);
@@ -178,13 +189,20 @@ int fa_fwd_kv_packed(const void* q, const void* k, const void* vt, size_t vt_byt
  * no split; only shapes with at most 64 query rows per sequence split).
  * fa_split_workspace_bytes: bytes of `part` for num_splits (0 if < 2):
  * num_splits * B * Hq * Nq * (d + 1) * 4.
- * fa_fwd_kv_split_packed: fa_fwd_kv_packed with num_splits in [1, 256]
- * (1 = plain fa_fwd_kv_packed; `part` may then be NULL); `part` is device
- * memory, 16-byte aligned, clear of o and lse; contents on entry do not
- * matter.  16-bit inputs only.  Allocates nothing.  fa_fwd_kv (and so
- * fa_fwd) applies fa_num_splits by itself, inside its own workspace. */
+ * fa_fwd_kv_split: fa_fwd_kv with num_splits in [1, 256] (1 = plain
+ * fa_fwd_kv; `part` may then be NULL); `part` is device memory of
+ * fa_split_workspace_bytes() bytes, 16-byte aligned, clear of o and lse;
+ * contents on entry do not matter.  16-bit inputs only (FA_ERR_DTYPE for
+ * fp32).  Two launches (the split kernel, then the merge); allocates
+ * nothing.
+ * fa_fwd_kv_split_packed: the same with V packed by fa_pack_v.
+ * fa_fwd and fa_fwd_kv never split. */
 int fa_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int in_dtype);
 size_t fa_split_workspace_bytes(int B, int Hq, int Nq, int d, int num_splits);
+int fa_fwd_kv_split(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                    int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int num_splits,
+                    void* part, size_t part_bytes, void* stream, int in_dtype, int out_dtype);
 int fa_fwd_kv_split_packed(const void* q, const void* k, const void* vt, size_t vt_bytes,
                            void* o, float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
                            int causal, float scale, const int* cu_seqlens_q,
@@ -202,7 +220,8 @@ int fa_fwd_kv_split_packed(const void* q, const void* k, const void* vt, size_t 
  *
  * Inputs: q, k, v (in_dtype FA_F16 or FA_BF16), o (the forward's output in
  * o_dtype, FA_F32 or in_dtype), dout (in_dtype, o's layout), lse (fp32, as
- * written by the forward).  Outputs dq (q's layout), dk, dv (k's layout)
+ * written by the forward); scale finite and > 0 (FA_ERR_SCALE otherwise).
+ * Outputs dq (q's layout), dk, dv (k's layout)
  * in grad_dtype (FA_F32 or in_dtype); they must not overlap any input, each
  * other or the workspace.  workspace: device memory of
  * fa_bwd_workspace_bytes() bytes, 16-byte aligned (the rows' D and
@@ -233,11 +252,10 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
  * ceil(Nq/64) * ceil(Nk/64) bytes).
  *
  * 16-bit inputs only (FA_ERR_DTYPE for fp32); ceil(Nk/64) <= 4096 (keys per
- * sequence <= 262144, else FA_ERR_SHAPE); never split over keys.
- * fa_fwd_sparse allocates its V^T workspace as fa_fwd does;
- * fa_fwd_sparse_packed reads V packed by fa_pack_v (called with N = Nk and
- * cu_seqlens = cu_seqlens_k) and allocates nothing.  Other arguments and
- * errors as fa_fwd_kv. */
+ * sequence <= 262144, else FA_ERR_SHAPE); never split over keys; one launch,
+ * no allocation.  fa_fwd_sparse_packed reads V packed by fa_pack_v (called
+ * with N = Nk and cu_seqlens = cu_seqlens_k).  Other arguments and errors
+ * as fa_fwd_kv. */
 int fa_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
                   int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                   const int* cu_seqlens_q, const int* cu_seqlens_k,
@@ -274,6 +292,17 @@ const char* fa_kernel_name(int in_dtype, int d, int causal, int varlen,
  * fa_kernel_name.  NULL if unsupported (or Hkv < 1). */
 const char* fa_kernel_name_kv(int in_dtype, int d, int causal, int varlen, int out_dtype,
                               int Hq, int Hkv, int Nq);
+
+/* fa_kernel_name_kv for a given path: sparse = 1 for fa_fwd_sparse*,
+ * vt_packed = 1 for the *_packed entry points (V packed by fa_pack_v). */
+const char* fa_kernel_name_ex(int in_dtype, int d, int causal, int varlen, int out_dtype,
+                              int Hq, int Hkv, int Nq, int sparse, int vt_packed);
+
+/* The check FA_DEBUG=1 applies to a packed offset array, on HOST memory:
+ * FA_OK if cu_seqlens[0] == 0 and 0 <= cu_seqlens[i] - cu_seqlens[i-1] <=
+ * n_max for i = 1 .. B; FA_ERR_SEQLENS otherwise; FA_ERR_NULL for NULL and
+ * FA_ERR_SHAPE for B < 0.  Makes no HIP call. */
+int fa_check_seqlens(const int* cu_seqlens, int B, int n_max);
 
 /* 1 if fa_fwd supports (in_dtype, d, causal), else 0 — so a caller can pick
  * another attention path when this one does not apply. */

@@ -26,7 +26,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     assert {"fa_fwd", "fa_fwd_check", "fa_kernel_name", "fa_supported",
             "fa_status_string", "fa_version", "fa_workspace_bytes", "fa_pack_v",
-            "fa_fwd_packed"} <= set(names)
+            "fa_fwd_packed", "fa_fwd_kv", "fa_fwd_kv_split", "fa_fwd_kv_split_packed",
+            "fa_fwd_sparse", "fa_bwd", "fa_kernel_name_ex", "fa_check_seqlens"} <= set(names)
 
 
 def test_library_exports_every_declared_symbol():
@@ -49,7 +50,7 @@ def test_status_codes_match_header():
 
 
 def test_version_and_support():
-    assert fa.version() == 10100
+    assert fa.version() == 10200
     for dt in (fa.FA_F32, fa.FA_F16, fa.FA_BF16):
         for d in (64, 128):
             for c in (False, True):
@@ -80,6 +81,43 @@ def test_kernel_name_kv_routing():
         fa.kernel_name(fa.FA_F32, 64, False, False, fa.FA_F32)          # fp32: no decode kernel
     assert fa.kernel_name_kv(fa.FA_BF16, 96, True, False, fa.FA_F32, 8, 8, 1) is None
     assert fa.kernel_name_kv(fa.FA_BF16, 128, True, False, fa.FA_F32, 8, 0, 1) is None
+
+
+def test_kernel_name_ex_paths():
+    """fa_kernel_name_ex names the instance each entry point runs: the default
+    (row-major V) kernels carry no suffix, the *_packed ones "_vtpacked", the
+    block-sparse ones "_sparse" (never the decode kernel)."""
+    ex = fa.kernel_name_ex
+    assert ex(fa.FA_BF16, 128, True, False, fa.FA_F32, 32, 8, 4096) == \
+        fa.kernel_name(fa.FA_BF16, 128, True, False, fa.FA_F32)
+    assert ex(fa.FA_BF16, 128, True, False, fa.FA_F32, 32, 8, 4096, vt_packed=True) == \
+        "fa_fwd_mfma_bf16_d128_causal_of32_vtpacked"
+    assert ex(fa.FA_F16, 64, False, True, fa.FA_F16, 8, 2, 300, sparse=True) == \
+        "fa_fwd_mfma_f16_d64_varlen_sparse"
+    assert ex(fa.FA_BF16, 128, True, False, fa.FA_F32, 32, 8, 1, sparse=True) == \
+        "fa_fwd_mfma_bf16_d128_causal_of32_sparse"
+    assert ex(fa.FA_BF16, 128, True, False, fa.FA_F32, 32, 8, 1, vt_packed=True) == \
+        "fa_decode_mfma_bf16_d128_causal_of32_vtpacked"
+    assert ex(fa.FA_BF16, 128, True, False, fa.FA_F32, 32, 8, 1) == \
+        "fa_decode_mfma_bf16_d128_causal_of32"
+    assert ex(fa.FA_F32, 64, False, False, fa.FA_F32, 2, 2, 256, vt_packed=True) == \
+        "fa_fwd_f32_d64"                       # fp32 has no packed path: the plain kernel
+    assert ex(fa.FA_BF16, 96, True, False, fa.FA_F32, 8, 8, 1) is None
+
+
+@pytest.mark.parametrize("cu,B,n,code", [
+    ([0], 0, 1, "FA_OK"),
+    ([0, 5, 5, 12], 3, 7, "FA_OK"),
+    ([0, 5, 5, 12], 3, 6, "FA_ERR_SEQLENS"),         # a length above the bound
+    ([1, 5, 9], 2, 8, "FA_ERR_SEQLENS"),             # cu[0] != 0
+    ([0, 5, 4], 2, 8, "FA_ERR_SEQLENS"),             # decreasing
+    ([0, 2**31 - 1, -2**31], 2, 2**31 - 1, "FA_ERR_SEQLENS"),   # no overflow in the difference
+    (None, 2, 8, "FA_ERR_NULL"),
+    ([0], -1, 8, "FA_ERR_SHAPE"),
+])
+def test_check_seqlens(cu, B, n, code):
+    """The predicate FA_DEBUG=1 applies on the device, run on host memory."""
+    assert fa.check_seqlens(cu, B, n) == S[code]
 
 
 # Fake, aligned, non-overlapping addresses: the checks never dereference them.
@@ -115,7 +153,8 @@ S = _lib.STATUS
     ({"out_dtype": fa.FA_F16}, "FA_ERR_DTYPE"),
     ({"in_dtype": fa.FA_F32, "out_dtype": fa.FA_BF16}, "FA_ERR_DTYPE"),
     ({"scale": float("nan")}, "FA_ERR_SCALE"), ({"scale": float("inf")}, "FA_ERR_SCALE"),
-    ({"scale": 0.0}, "FA_ERR_SCALE"), ({"scale": -0.1}, "FA_ERR_SCALE"),
+    ({"scale": float("-inf")}, "FA_ERR_SCALE"),
+    ({"scale": 0.0}, "FA_OK"), ({"scale": -0.1}, "FA_OK"), ({"scale": -0.0}, "FA_OK"),
     ({"q": 0x100008}, "FA_ERR_ALIGN"), ({"o": 0x400004}, "FA_ERR_ALIGN"),
     ({"lse": 0x500002}, "FA_ERR_ALIGN"), ({"cu_seqlens": 0x600001}, "FA_ERR_ALIGN"),
     ({"o": 0x100000}, "FA_ERR_ALIAS"),
@@ -130,7 +169,8 @@ def test_argument_checks(kw, code):
 def test_fwd_rejects_before_any_device_call():
     # fa_fwd runs the same checks first: bad arguments never reach HIP.
     for kw, code in [({"q": None}, "FA_ERR_NULL"), ({"d": 96}, "FA_ERR_HEADDIM"),
-                     ({"scale": -1.0}, "FA_ERR_SCALE"), ({"o": 0x100000}, "FA_ERR_ALIAS")]:
+                     ({"scale": float("nan")}, "FA_ERR_SCALE"),
+                     ({"o": 0x100000}, "FA_ERR_ALIAS")]:
         a = dict(BASE, **kw)
         st = _lib.fwd_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"],
                           a["Hkv"], a["N"], a["d"], a["causal"], a["scale"], None, None,
@@ -191,7 +231,7 @@ def pack(**kw):
     ({"vt": VT + 8}, "FA_ERR_ALIGN"),
     ({"in_dtype": fa.FA_F32}, "FA_ERR_DTYPE"),
     ({"d": 96}, "FA_ERR_HEADDIM"), ({"Hq": 6, "Hkv": 4}, "FA_ERR_GQA"),
-    ({"scale": 0.0}, "FA_ERR_SCALE"),
+    ({"scale": float("inf")}, "FA_ERR_SCALE"),
     ({"o": VT}, "FA_ERR_ALIAS"), ({"o": VT + WS - 16}, "FA_ERR_ALIAS"),
 ])
 def test_fwd_packed_rejects_before_any_device_call(kw, code):
@@ -243,6 +283,16 @@ def split(**kw):
                                         a["part_bytes"], None, a["in_dtype"], a["out_dtype"])
 
 
+def split_rm(**kw):
+    a = dict(BASE, Nk=64, n=4, part=0x800000, part_bytes=1 << 24)
+    a.update(kw)
+    return _lib.fwd_kv_split_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"],
+                                 a["Hkv"], a["N"], a["Nk"], a["d"], a["causal"], a["scale"],
+                                 a["cu_seqlens"], a.get("cu_k", a["cu_seqlens"]), a["n"],
+                                 a["part"], a["part_bytes"], None, a["in_dtype"],
+                                 a["out_dtype"])
+
+
 def test_split_workspace_bytes():
     assert fa.split_workspace_bytes(2, 8, 64, 128, 4) == 4 * 2 * 8 * 64 * 129 * 4
     assert fa.split_workspace_bytes(2, 8, 64, 128, 1) == 0
@@ -257,6 +307,7 @@ def test_split_workspace_bytes():
 ])
 def test_split_rejects_before_any_device_call(kw, code):
     assert split(**kw) == S[code]
+    assert split_rm(**kw) == S[code]        # the row-major-V form checks the same
 
 
 BWD = dict(q=0x100000, k=0x200000, v=0x300000, o=0x400000, do=0x600000, lse=0x500000,
@@ -290,6 +341,8 @@ def test_bwd_workspace_bytes():
     ({"dq": 0x100000}, "FA_ERR_ALIAS"), ({"dk": 0x1000000 + 4096}, "FA_ERR_ALIAS"),
     ({"dv": 0x4000000 + 64}, "FA_ERR_ALIAS"),
     ({"d": 96}, "FA_ERR_HEADDIM"), ({"Hq": 6, "Hkv": 4}, "FA_ERR_GQA"),
+    ({"scale": 0.0}, "FA_ERR_SCALE"), ({"scale": -0.5}, "FA_ERR_SCALE"),   # backward: > 0
+    ({"scale": float("nan")}, "FA_ERR_SCALE"),
 ])
 def test_bwd_rejects_before_any_device_call(kw, code):
     assert bwd(**kw) == S[code]
@@ -333,7 +386,7 @@ def test_sparse_valid_arguments_reach_the_device_check():
     for packed_vt in (True, False):
         for mb, mh in ((1, 1), (2, 8), (1, 8), (2, 1)):
             st = sparse(packed_vt, mb=mb, mh=mh)
-            assert st in (S["FA_ERR_DEVICE"], S["FA_OK"]) or st == S["FA_ERR_ALLOC"], st
+            assert st in (S["FA_ERR_DEVICE"], S["FA_OK"]), st
 
 
 def test_sparse_flops_count_admitted_pairs():

@@ -14,7 +14,7 @@ from tests.test_gpu_prefill import _make, _oracle
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, num_splits=None, out_dtype=None):
+def _run(w, num_splits=None, out_dtype=None, packed=False):
     import torch
 
     import exact_io_aware_amd as fa
@@ -25,7 +25,12 @@ def _run(w, num_splits=None, out_dtype=None):
         cu = torch.from_numpy(w["cu_seqlens"]).to(dev)
         cuk = torch.from_numpy(w["cu_seqlens_k"]).to(dev)
     lse = torch.full((w["B"], w["Hq"], w["N"]), float("nan"), device=dev)
-    o, lse = fa.fwd(q, k, v, causal=w["causal"], scale=w["scale"], cu_seqlens=cu,
+    # packed: the K/V cache's V kept packed (fa_pack_v; the *_packed entry
+    # points); otherwise V itself is read and transposed on chip.
+    vt = fa.pack_v(v, cu_seqlens=cuk, max_seqlen=w["Nk"] if cuk is not None else None) \
+        if packed else None
+    o, lse = fa.fwd(q, k, None if packed else v, causal=w["causal"], scale=w["scale"],
+                    cu_seqlens=cu, vt=vt,
                     cu_seqlens_k=cuk, max_seqlen=w["N"] if cu is not None else None,
                     max_seqlen_k=w["Nk"] if cu is not None else None,
                     out_dtype=out_dtype or torch.float32, lse=lse, num_splits=num_splits)
@@ -57,9 +62,10 @@ def test_decode_parity_auto_splits(i):
     w = _make(case, seed=800 + i)
     Oref, Lref = _oracle(w)
     for od in ("fp32", w["dtype"]):
-        G.say(f"decode case {case} out={od}")
-        O, L = _run(w, out_dtype=G.torch_dtype(od))
-        G.say(f"  errors {G.compare_qk(w, O, L, Oref, Lref, od)}")
+        for packed in (False, True):
+            G.say(f"decode case {case} out={od} packed={packed}")
+            O, L = _run(w, out_dtype=G.torch_dtype(od), packed=packed)
+            G.say(f"  errors {G.compare_qk(w, O, L, Oref.copy(), Lref.copy(), od)}")
 
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 16, 40])
@@ -68,9 +74,10 @@ def test_decode_explicit_splits(splits):
     empty splits (more splits than the shortest sequence has tiles)."""
     w = _make(("bf16", 128, 3, 8, 2, [1, 2, 1], [2500, 70, 640], True), seed=850)
     Oref, Lref = _oracle(w)
-    G.say(f"decode with {splits} splits")
-    O, L = _run(w, num_splits=splits)
-    G.say(f"  errors {G.compare_qk(w, O, L, Oref, Lref)}")
+    for packed in (False, True):
+        G.say(f"decode with {splits} splits packed={packed}")
+        O, L = _run(w, num_splits=splits, packed=packed)
+        G.say(f"  errors {G.compare_qk(w, O, L, Oref.copy(), Lref.copy())}")
 
 
 def test_splits_on_prefill_shape():

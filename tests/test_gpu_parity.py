@@ -27,14 +27,22 @@ def gpu_ready():
 
 
 def _compare(w, O, L, Oref, Lref, out_dtype="fp32", strict=None, bar=None):
+    """Element-wise bars.  Every output the oracle defines must have been
+    written: O finite everywhere, L finite wherever the oracle's is (callers
+    pre-fill L with NaN, so a row the kernel skipped fails here), and no NaN
+    can hide in a maximum."""
+    assert O.shape == Oref.shape and L.shape == Lref.shape
+    assert np.isfinite(O).all(), "non-finite O"
+    fin = np.isfinite(Lref)
+    assert np.isfinite(L[fin]).all(), "an L row the oracle defines is missing or not finite"
+    assert np.array_equal(np.isneginf(L), np.isneginf(Lref)), "rows without keys"
     eo = np.abs(O - Oref)
     if bar is None:
         bar = G.o_bar(w["dtype"], out_dtype, Oref)
     worst_o = float(eo.max()) if eo.size else 0.0
-    assert np.isfinite(O).all()
     assert (eo <= bar).all(), f"O error {worst_o:.3e}"
-    el = np.abs(L - Lref)
-    worst_l = float(np.nanmax(el)) if el.size else 0.0
+    el = np.abs(np.where(fin, L - Lref, 0.0))
+    worst_l = float(el.max()) if el.size else 0.0
     assert worst_l <= G.L_TOL, f"L error {worst_l:.3e}"
     if strict is not None:
         assert worst_o <= strict and worst_l <= strict, (worst_o, worst_l)
@@ -61,6 +69,10 @@ MEDIUM = [
     ("fp32", 64, 2, 2, 1, [31, 90], True),
     ("bf16", 128, 3, 8, 2, [100, 0, 64], True),      # an empty sequence
     ("fp32", 64, 3, 2, 1, [0, 40, 0], False),
+    # Units (sequence x group of 4 query heads) a multiple of 8: the launch
+    # deals each unit's workgroups to one XCD (non-causal, and causal d=64).
+    ("bf16", 128, 2, 16, 4, 333, False),
+    ("fp16", 64, 4, 8, 2, 200, True),
 ]
 
 
@@ -107,11 +119,30 @@ def test_tiny_fp32_workload_full():
     G.say(f"  errors {_compare(w, O, L, Oref, Lref, strict=G.FP32_STRICT)}")
 
 
+def test_causal_unit_major_varlen():
+    """A causal varlen launch more than 4 rounds of workgroups deep takes the
+    unit-major order with each unit on one XCD (8 sequences x 8 groups of 4
+    query heads, row blocks of 64 rows: 1152 workgroups)."""
+    lens = [1100, 700, 1030, 900, 64, 1, 1099, 512]
+    w = workloads.make_custom(8, 32, 8, 128, "bf16", seed=520, lengths=lens)
+    w["causal"], w["scale"] = True, 128 ** -0.5
+    q, k, v = G.f64_inputs(w)
+    Oref, Lref = oracle.attention(q, k, v, causal=True, scale=w["scale"],
+                                  cu_seqlens=w["cu_seqlens"],
+                                  workers=min(16, oracle.default_workers()))
+    G.say("causal varlen, unit-major order")
+    O, L = G.run_gpu(w, lse_fill=float("nan"))
+    for b, n in enumerate(lens):
+        assert np.isnan(L[b, :, n:]).all(), "padded lse rows must stay untouched"
+        L[b, :, n:] = Lref[b, :, n:] = 0.0
+    G.say(f"  errors {_compare(w, O, L, Oref, Lref)}")
+
+
 @pytest.mark.parametrize("name", ["mha_fp16", "gqa_bf16"])
 def test_workload_full(name):
     w = workloads.make_inputs(name)
     G.say(f"workload {name}")
-    O, L = G.run_gpu(w)
+    O, L = G.run_gpu(w, lse_fill=float("nan"))
     q, k, v = G.f64_inputs(w)
     Oref, Lref = oracle.attention(q, k, v, causal=w["causal"], scale=w["scale"],
                                   workers=min(16, oracle.default_workers()))
@@ -141,12 +172,35 @@ def _picks_varlen(w, rng, per_head=4):
 
 
 @pytest.mark.parametrize("name", ["long_bf16", "varlen_bf16"])
-def test_workload_sampled_rows(name):
+def test_workload_sampled_rows_and_whole_heads(name):
+    """The two largest workloads at full size, in the bench's launch
+    configuration: every L row written and finite; sampled rows of every
+    (sequence, head) (first, last, block and tile boundaries, random); and
+    query heads 0 and 31 (two different K/V heads) of every sequence
+    compared element by element in full."""
     w = workloads.make_inputs(name)
     G.say(f"workload {name}")
     O, L = G.run_gpu(w, lse_fill=float("nan"))
+    if w["cu_seqlens"] is None:
+        assert np.isfinite(L).all(), "an L row is missing or not finite"
     rng = np.random.default_rng(99)
     q, k, v = G.f64_inputs(w)
+    heads = (0, w["Hq"] - 1)
+    picks_all = []
+    lens = [w["N"]] * w["B"] if w["cu_seqlens"] is None else list(np.diff(w["cu_seqlens"]))
+    for b, n in enumerate(lens):
+        for h in heads:
+            picks_all += [(b, h, r) for r in range(int(n))]
+    G.say(f"  oracle over {len(picks_all)} rows of heads {heads}")
+    Oall, Lall = G.oracle_rows_parallel(q, k, v, causal=w["causal"], scale=w["scale"],
+                                        picks=picks_all, cu_seqlens=w["cu_seqlens"])
+    if w["cu_seqlens"] is None:
+        got_o = np.stack([O[b, h, r] for b, h, r in picks_all])
+    else:
+        cu = w["cu_seqlens"]
+        got_o = np.stack([O[cu[b] + r, h] for b, h, r in picks_all])
+    got_l = np.array([L[b, h, r] for b, h, r in picks_all])
+    G.say(f"  whole heads: errors {_compare(w, got_o, got_l, Oall, Lall)}")
     if w["cu_seqlens"] is None:
         picks = _picks_fixed(w, rng)
         got_o = np.stack([O[b, h, r] for b, h, r in picks])
@@ -315,68 +369,160 @@ def test_pack_v_layout(dtype, d, lens, varlen):
         assert np.array_equal(got[b, g, t], tile), (b, g, t)
 
 
-def test_packed_reuse_and_library_workspace_agree():
+@pytest.mark.parametrize("case", [
+    ("bf16", 128, 2, 8, 2, 333, True), ("bf16", 128, 2, 8, 2, 333, False),
+    ("fp16", 64, 2, 6, 6, 300, True), ("fp16", 64, 1, 4, 2, 130, False),
+    ("fp16", 64, 3, 4, 2, [200, 7, 128], True), ("bf16", 128, 3, 8, 2, [100, 0, 64], True)])
+def test_row_major_and_packed_agree(case):
+    """fa_fwd reads V's rows and transposes them on chip; fa_fwd_packed reads
+    V packed by fa_pack_v, reused across calls.  Both feed the same operands,
+    in the same order, to the same products: bitwise equal O and L."""
     import torch
 
     import exact_io_aware_amd as fa
-    w = _make(("bf16", 128, 2, 8, 2, 333, True), seed=11)
-    q, k, v = (G.to_device(w[x], "bf16", "cuda:0") for x in "qkv")
-    G.say("packed vt reuse vs fa_fwd workspace")
-    o1, l1 = fa.fwd(q, k, v, causal=True)
-    vt = fa.pack_v(v)
-    o2, l2 = fa.fwd(q, k, None, causal=True, vt=vt)
-    o3, l3 = fa.fwd(q, k, None, causal=True, vt=vt)
-    o4, l4 = fa.fwd(q, k, v, causal=True, library_workspace=True)
+    w = _make(case, seed=11)
+    dt = w["dtype"]
+    q, k, v = (G.to_device(w[x], dt, "cuda:0") for x in "qkv")
+    cu = None if w["cu_seqlens"] is None else torch.from_numpy(w["cu_seqlens"]).to("cuda:0")
+    ms = w["N"] if cu is not None else None
+    G.say(f"row-major V vs packed V {case}")
+    # lse pre-filled with NaN: padded varlen rows stay NaN in every call.
+    nanl = lambda: torch.full((w["B"], w["Hq"], w["N"]), float("nan"), device="cuda:0")  # noqa
+    o1, l1 = fa.fwd(q, k, v, causal=w["causal"], cu_seqlens=cu, max_seqlen=ms, lse=nanl())
+    vt = fa.pack_v(v, cu_seqlens=cu, max_seqlen=ms)
+    o2, l2 = fa.fwd(q, k, None, causal=w["causal"], vt=vt, cu_seqlens=cu, max_seqlen=ms,
+                    lse=nanl())
+    o3, l3 = fa.fwd(q, k, None, causal=w["causal"], vt=vt, cu_seqlens=cu, max_seqlen=ms,
+                    lse=nanl())
     torch.cuda.synchronize()
-    for o, l in ((o2, l2), (o3, l3), (o4, l4)):
-        assert torch.equal(o1, o) and torch.equal(l1, l)
-    Oref, Lref = _oracle(w)
-    _compare(w, o4.double().cpu().numpy(), l4.double().cpu().numpy(), Oref, Lref)
+    nan7 = lambda t: torch.nan_to_num(t, nan=7.0)  # noqa: E731 (unwritten padded rows)
+    for o, l in ((o2, l2), (o3, l3)):
+        assert torch.equal(o1, o) and torch.equal(nan7(l1), nan7(l))
 
 
-def test_library_workspace_varlen_fp16():
-    w = _make(("fp16", 64, 3, 4, 2, [200, 7, 128], True), seed=12)
-    Oref, Lref = _oracle(w)
+def _device_bytes_in_use():
+    """Bytes the device has in use (the HIP runtime's own view, so
+    allocations made outside torch's allocator count too)."""
+    import torch
+    free, total = torch.cuda.mem_get_info()
+    return total - free
+
+
+@pytest.mark.parametrize("name", ["gqa_bf16", "varlen_bf16"])
+def test_fa_fwd_allocates_nothing(name):
+    """The O(N) memory claim (HolySheep, Chinese edition, "IO 感知的算法设计"):
+    fa_fwd allocates nothing at all -- no N x N scores (8 GiB for gqa_bf16's
+    32 heads of 4096 x 4096 bf16 scores per sequence) and no workspace --
+    with o and lse allocated by the caller.  Checked through torch's
+    allocator (delta 0) and the device's own free-memory count (no growth by
+    more than the runtime's page rounding)."""
     import torch
 
     import exact_io_aware_amd as fa
-    q, k, v = (G.to_device(w[x], "fp16", "cuda:0") for x in "qkv")
-    cu = torch.from_numpy(w["cu_seqlens"]).to("cuda:0")
-    G.say("fa_fwd own workspace, varlen fp16")
-    o, l = fa.fwd(q, k, v, causal=True, cu_seqlens=cu, max_seqlen=200, library_workspace=True)
-    torch.cuda.synchronize()
-    L = l.double().cpu().numpy()
-    for b, n in enumerate(np.diff(w["cu_seqlens"])):
-        L[b, :, n:] = Lref[b, :, n:] = 0.0
-    _compare(w, o.double().cpu().numpy(), L, Oref, Lref)
-
-
-def test_no_score_matrix_in_device_memory():
-    """The O(N) memory claim: a call allocates no N x N scores.  With V
-    already packed the call allocates nothing beyond o and lse; the default
-    path adds only the packed-V workspace (the size of V)."""
-    import torch
-
-    import exact_io_aware_amd as fa
-    w = workloads.make_inputs("gqa_bf16")
+    w = workloads.make_inputs(name)
     q, k, v = (G.to_device(w[x], "bf16", "cuda:0") for x in "qkv")
+    cu = None if w["cu_seqlens"] is None else torch.from_numpy(w["cu_seqlens"]).to("cuda:0")
     o = torch.empty(q.shape, dtype=torch.float32, device="cuda:0")
     lse = torch.empty((w["B"], w["Hq"], w["N"]), dtype=torch.float32, device="cuda:0")
-    vt = fa.pack_v(v)
-    G.say("device memory during a call")
+    G.say(f"device memory during fa_fwd ({name})")
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
     base = torch.cuda.memory_allocated()
-    fa.fwd(q, k, None, causal=True, out=o, lse=lse, vt=vt)
+    dev0 = _device_bytes_in_use()
+    for _ in range(3):
+        fa.fwd(q, k, v, causal=True, out=o, lse=lse, cu_seqlens=cu,
+               max_seqlen=w["N"] if cu is not None else None, num_splits=1)
     torch.cuda.synchronize()
     assert torch.cuda.max_memory_allocated() - base == 0
-    torch.cuda.reset_peak_memory_stats()
-    base = torch.cuda.memory_allocated()
-    fa.fwd(q, k, v, causal=True, out=o, lse=lse)
+    assert _device_bytes_in_use() - dev0 <= (2 << 20)
+    assert torch.isfinite(o).all()
+
+
+# --- any finite scale, streams, debug checks ----------------------------------
+
+@pytest.mark.parametrize("case", [
+    ("bf16", 128, 2, 8, 2, 333, True), ("fp16", 64, 2, 4, 4, 200, False),
+    ("fp32", 64, 1, 2, 2, 150, True), ("bf16", 64, 3, 4, 2, [200, 7, 128], False)])
+@pytest.mark.parametrize("scale", [-0.125, 0.0, -1.0, 0.3])
+def test_any_finite_scale(case, scale):
+    """Negative and zero scales: the scores are scale * q.k as written, so a
+    negative scale ranks keys in reverse and scale 0 averages V over the
+    visible keys (L = ln of their count); checked against the oracle, on the
+    default path and (16-bit) with packed V."""
+    import torch
+
+    import exact_io_aware_amd as fa
+    w = _make(case, seed=600 + int(10 * scale))
+    w["scale"] = scale
+    Oref, Lref = _oracle(w)
+    paths = [False] if w["dtype"] == "fp32" else [False, True]
+    for packed in paths:
+        G.say(f"scale {scale} case {case} packed={packed}")
+        q, k, v = (G.to_device(w[x], w["dtype"], "cuda:0") for x in "qkv")
+        cu = None if w["cu_seqlens"] is None else torch.from_numpy(w["cu_seqlens"]).to("cuda:0")
+        ms = w["N"] if cu is not None else None
+        vt = fa.pack_v(v, cu_seqlens=cu, max_seqlen=ms) if packed else None
+        lse = torch.full((w["B"], w["Hq"], w["N"]), float("nan"), device="cuda:0")
+        o, l = fa.fwd(q, k, None if packed else v, causal=w["causal"], scale=scale,
+                      cu_seqlens=cu, max_seqlen=ms, vt=vt, lse=lse)
+        torch.cuda.synchronize()
+        O, L = o.double().cpu().numpy(), l.double().cpu().numpy()
+        Lr = Lref.copy()
+        if cu is not None:
+            for b, n in enumerate(np.diff(w["cu_seqlens"])):
+                assert np.isnan(L[b, :, n:]).all()
+                L[b, :, n:] = Lr[b, :, n:] = 0.0
+        strict = G.FP32_STRICT if w["dtype"] == "fp32" else None
+        bar = None
+        if abs(scale) > w["d"] ** -0.5:
+            # Scores larger than the workloads' (|scale| above 1/sqrt(d)): the
+            # derived bar of the stress inputs (rounding of P for P.V).
+            qf, kf, vf = G.f64_inputs(w)
+            A, _ = oracle.attention(qf, kf, np.abs(vf), causal=w["causal"], scale=scale,
+                                    cu_seqlens=w["cu_seqlens"])
+            bar = G.o_bar_derived(w["dtype"], A)
+        G.say(f"  errors {_compare(w, O, L, Oref, Lr, strict=strict, bar=bar)}")
+
+
+def test_side_stream_matches_default_stream():
+    """Forward and backward enqueued on a side stream (tensors made by the
+    binding belong to that stream) give the default stream's results."""
+    import torch
+
+    import exact_io_aware_amd as fa
+    w = _make(("bf16", 128, 2, 8, 2, 300, True), seed=21)
+    q, k, v = (G.to_device(w[x], "bf16", "cuda:0") for x in "qkv")
+    g = workloads.make_custom(2, 8, 8, 128, "bf16", seed=22, N=300)
+    do = G.to_device(g["q"], "bf16", "cuda:0")
+    G.say("side stream vs default stream")
+    o0, l0 = fa.fwd(q, k, v, causal=True)
+    dq0, dk0, dv0 = fa.bwd(q, k, v, o0, l0, do, causal=True)
     torch.cuda.synchronize()
-    delta = torch.cuda.max_memory_allocated() - base
-    ws = fa.workspace_bytes(w["B"], w["Hkv"], w["N"], w["d"], fa.FA_BF16)
-    assert ws == v.numel() * 2
-    assert delta <= ws + (2 << 20)
-    scores = w["B"] * w["Hq"] * w["N"] * w["N"] * 2          # one bf16 score matrix
-    assert delta * 100 < scores
+    s = torch.cuda.Stream()
+    for _ in range(2):
+        o1, l1 = fa.fwd(q, k, v, causal=True, stream=s)
+        dq1, dk1, dv1 = fa.bwd(q, k, v, o1, l1, do, causal=True, stream=s)
+        # Busy work on the default stream meanwhile must not disturb them.
+        junk = torch.empty(1 << 24, device="cuda:0").fill_(3.0)
+        del junk
+        s.synchronize()
+        assert torch.equal(o0, o1) and torch.equal(l0, l1)
+        assert torch.equal(dq0, dq1) and torch.equal(dk0, dk1) and torch.equal(dv0, dv1)
+
+
+def test_debug_mode_rejects_corrupt_offsets():
+    """FA_DEBUG=1: every entry point that takes packed offsets checks them on
+    the device first; corrupt ones (cu[0] != 0, decreasing, a length above N)
+    give FA_ERR_SEQLENS and no attention kernel runs (the NaN-filled outputs
+    stay untouched).  All offsets stay inside the buffers.  Runs in a child
+    process, since the mode is read once per process."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, FA_DEBUG="1")
+    G.say("FA_DEBUG=1 child process")
+    r = subprocess.run([sys.executable, "-u", "-m", "tests.debug_seqlens_check"], cwd=root,
+                       env=env, capture_output=True, text=True, timeout=300)
+    print(r.stdout[-3000:], r.stderr[-3000:])
+    assert r.returncode == 0 and "DEBUG_SEQLENS_OK" in r.stdout

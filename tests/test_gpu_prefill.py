@@ -38,7 +38,7 @@ def _make(case, seed):
     return w
 
 
-def _run(w, out_dtype=None, library_workspace=False):
+def _run(w, out_dtype=None, packed=False):
     import torch
 
     import exact_io_aware_amd as fa
@@ -49,11 +49,13 @@ def _run(w, out_dtype=None, library_workspace=False):
         cu = torch.from_numpy(w["cu_seqlens"]).to(dev)
         cuk = torch.from_numpy(w["cu_seqlens_k"]).to(dev)
     lse = torch.full((w["B"], w["Hq"], w["N"]), float("nan"), device=dev)
-    o, lse = fa.fwd(q, k, v, causal=w["causal"], scale=w["scale"], cu_seqlens=cu,
+    # packed: V packed by fa_pack_v first (the *_packed entry points).
+    vt = fa.pack_v(v, cu_seqlens=cuk, max_seqlen=w["Nk"] if cuk is not None else None) \
+        if packed else None
+    o, lse = fa.fwd(q, k, None if packed else v, causal=w["causal"], scale=w["scale"], cu_seqlens=cu,
                     cu_seqlens_k=cuk, max_seqlen=w["N"] if cu is not None else None,
                     max_seqlen_k=w["Nk"] if cu is not None else None,
-                    out_dtype=out_dtype or torch.float32, lse=lse,
-                    library_workspace=library_workspace)
+                    out_dtype=out_dtype or torch.float32, lse=lse, vt=vt)
     torch.cuda.synchronize()
     return o.double().cpu().numpy(), lse.double().cpu().numpy()
 
@@ -77,11 +79,13 @@ def test_prefill_parity(i):
         G.say(f"  errors {G.compare_qk(w, O, L, Oref, Lref, od)}")
 
 
-def test_prefill_library_workspace_matches_packed():
+def test_prefill_row_major_matches_packed():
+    """fa_fwd_kv (V read transposed on chip) and fa_fwd_kv_packed (V packed by
+    fa_pack_v) feed the same operands to the same products: bitwise equal."""
     w = _make(("bf16", 128, 3, 8, 2, [5, 64, 100], [300, 64, 101], True), seed=760)
-    G.say("fa_fwd_kv own workspace vs packed")
+    G.say("fa_fwd_kv vs fa_fwd_kv_packed")
     O1, L1 = _run(w)
-    O2, L2 = _run(w, library_workspace=True)
+    O2, L2 = _run(w, packed=True)
     assert np.array_equal(O1, O2)
     assert np.array_equal(np.nan_to_num(L1, nan=7.0), np.nan_to_num(L2, nan=7.0))
 

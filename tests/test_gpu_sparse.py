@@ -47,7 +47,7 @@ def _make(case, seed):
     return w
 
 
-def _run(w, out_dtype=None, library_workspace=False, mask=None):
+def _run(w, out_dtype=None, packed=False, mask=None):
     import torch
 
     import exact_io_aware_amd as fa
@@ -59,11 +59,13 @@ def _run(w, out_dtype=None, library_workspace=False, mask=None):
         cuk = torch.from_numpy(w["cu_seqlens_k"]).to(dev)
     bm = torch.from_numpy(np.ascontiguousarray(w["block_mask"] if mask is None else mask)).to(dev)
     lse = torch.full((w["B"], w["Hq"], w["N"]), float("nan"), device=dev)
-    o, lse = fa.fwd(q, k, v, causal=w["causal"], scale=w["scale"], cu_seqlens=cu,
+    # packed: V packed by fa_pack_v first (the *_packed entry points).
+    vt = fa.pack_v(v, cu_seqlens=cuk, max_seqlen=w["Nk"] if cuk is not None else None) \
+        if packed else None
+    o, lse = fa.fwd(q, k, None if packed else v, causal=w["causal"], scale=w["scale"], cu_seqlens=cu,
                     cu_seqlens_k=cuk, max_seqlen=w["N"] if cu is not None else None,
                     max_seqlen_k=w["Nk"] if cu is not None else None,
-                    out_dtype=out_dtype or torch.float32, lse=lse, block_mask=bm,
-                    library_workspace=library_workspace)
+                    out_dtype=out_dtype or torch.float32, lse=lse, block_mask=bm, vt=vt)
     torch.cuda.synchronize()
     return o.double().cpu().numpy(), lse.double().cpu().numpy()
 
@@ -123,11 +125,12 @@ def test_sparse_empty_mask():
     assert not O.any() and np.isneginf(L).all()
 
 
-def test_sparse_library_workspace_matches_packed():
+def test_sparse_row_major_matches_packed():
+    """fa_fwd_sparse and fa_fwd_sparse_packed: bitwise equal."""
     w = _make(CASES[7], seed=961)
-    G.say("fa_fwd_sparse own workspace vs packed")
+    G.say("fa_fwd_sparse vs fa_fwd_sparse_packed")
     O1, L1 = _run(w)
-    O2, L2 = _run(w, library_workspace=True)
+    O2, L2 = _run(w, packed=True)
     assert np.array_equal(O1, O2)
     assert np.array_equal(np.nan_to_num(L1, nan=7.0), np.nan_to_num(L2, nan=7.0))
 
