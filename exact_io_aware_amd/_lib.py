@@ -13,6 +13,7 @@ STATUS = {
     "FA_ERR_GQA": -4, "FA_ERR_DTYPE": -5, "FA_ERR_ALIGN": -6, "FA_ERR_ALIAS": -7,
     "FA_ERR_SCALE": -8, "FA_ERR_DEVICE": -9, "FA_ERR_LAUNCH": -10,
     "FA_ERR_WORKSPACE": -11, "FA_ERR_ALLOC": -12, "FA_ERR_SEQLENS": -13,
+    "FA_ERR_SCRATCH": -14,
 }
 
 _lib = None
@@ -53,6 +54,11 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_kv_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, i, vp,
                                     z, vp, i, i]
     lib.fa_fwd_kv_split.restype = i
+    lib.fa_fwd_kv_split_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp,
+                                            i, vp, i, i]
+    lib.fa_fwd_kv_split_noalloc.restype = i
+    lib.fa_noalloc_scratch_bytes.argtypes = []
+    lib.fa_noalloc_scratch_bytes.restype = z
     lib.fa_fwd_sparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, vp, i, i,
                                   vp, i, i]
     lib.fa_fwd_sparse.restype = i
@@ -196,6 +202,19 @@ def fwd_kv_split_raw(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, cu_q
     return load().fa_fwd_kv_split(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, int(causal), scale,
                                   cu_q, cu_k, n_splits, part, part_bytes, stream, in_dtype,
                                   out_dtype)
+
+
+def fwd_kv_split_noalloc_raw(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, cu_q,
+                             cu_k, n_splits, stream, in_dtype, out_dtype) -> int:
+    """fa_fwd_kv_split_noalloc with raw integer device addresses."""
+    return load().fa_fwd_kv_split_noalloc(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, int(causal),
+                                          scale, cu_q, cu_k, n_splits, stream, in_dtype,
+                                          out_dtype)
+
+
+def noalloc_scratch_bytes() -> int:
+    """fa_noalloc_scratch_bytes: size of the library's fixed scratch."""
+    return load().fa_noalloc_scratch_bytes()
 
 
 def bwd_workspace_bytes(B, Hq, Hkv, N, d, in_dtype) -> int:

@@ -137,6 +137,41 @@ int fa_fwd_kv_split_packed(const void* q, const void* k, const void* vt, size_t 
   return fa::launch_fwd(a, stream);
 }
 
+int fa_fwd_kv_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                            float scale, const int* cu_seqlens_q, const int* cu_seqlens_k,
+                            int num_splits, void* stream, int in_dtype, int out_dtype) {
+  int st = fa::check_args(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale,
+                          cu_seqlens_q, cu_seqlens_k, in_dtype, out_dtype);
+  if (st != FA_OK) return st;
+  if (in_dtype == FA_F32) return FA_ERR_DTYPE;
+  if (num_splits < 1 || num_splits > 256) return FA_ERR_SHAPE;
+  const uint64_t need = num_splits > 1 ? fa::split_workspace_bytes(B, Hq, Nq, d, num_splits) : 0;
+  if (need > fa::kNoAllocScratchBytes) return FA_ERR_SCRATCH;
+  st = device_status();
+  if (st != FA_OK) return st;
+  void* part = nullptr;
+  if (num_splits > 1) {
+    part = fa::noalloc_scratch();
+    if (!part) return FA_ERR_DEVICE;
+  }
+  st = fa::check_split_args(part, need, o, lse, B, Hq, Hkv, Nq, Nk, d, num_splits, in_dtype,
+                            out_dtype, cu_seqlens_q != nullptr);
+  if (st != FA_OK) return st;
+  st = debug_seqlens(cu_seqlens_q, cu_seqlens_k, B, Nq, Nk, stream);
+  if (st != FA_OK) return st;
+  fa::LaunchArgs a{q, k, v, o, lse, nullptr, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, Nq, Nk,
+                   d, causal, scale, in_dtype, out_dtype};
+  if (num_splits > 1) {
+    a.n_splits = num_splits;
+    a.o_part = (float*)part;
+    a.lse_part = (float*)((char*)part + (size_t)num_splits * B * Hq * Nq * d * 4);
+  }
+  return fa::launch_fwd(a, stream);
+}
+
+size_t fa_noalloc_scratch_bytes(void) { return (size_t)fa::kNoAllocScratchBytes; }
+
 int fa_fwd_packed(const void* q, const void* k, const void* vt, size_t vt_bytes, void* o,
                   float* lse, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                   const int* cu_seqlens, void* stream, int in_dtype, int out_dtype) {
@@ -307,6 +342,8 @@ const char* fa_status_string(int status) {
     case FA_ERR_WORKSPACE: return "workspace too small: see fa_workspace_bytes";
     case FA_ERR_ALLOC: return "could not allocate device memory (no entry point allocates)";
     case FA_ERR_SEQLENS: return "corrupt cu_seqlens: cu[0] != 0, decreasing, or a length above N";
+    case FA_ERR_SCRATCH: return "split-KV partials exceed the library's fixed scratch "
+                                "(fa_noalloc_scratch_bytes)";
     default: return "unknown status";
   }
 }

@@ -772,6 +772,30 @@ const char* kernel_name_kv(int in_dtype, int d, int causal, int varlen, int out_
 // The debug check's verdict, one per device.
 __device__ int g_seqlens_bad;
 
+// Fixed device memory for the split-KV partials of fa_fwd_kv_split_noalloc
+// (callers that cannot allocate: graph capture, serving loops).  Every GPU
+// the library runs on holds its own copy until the process ends.  In host
+// code `scratch` names a host-side stand-in, never the device memory: the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::once_flag g_scratch_once[kMaxScratchDevices];
+void* g_scratch_ptr[kMaxScratchDevices];
+}  // namespace
+
+void* noalloc_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    g_scratch_ptr[dev] =
+        hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess ? ptr : nullptr;
+  });
+  return g_scratch_ptr[dev];
+}
+
 int debug_check_seqlens(const int* cu, int B, int n_max, void* stream) {
   static std::mutex mu;                       // one verdict slot per device
   std::lock_guard<std::mutex> lock(mu);

@@ -223,6 +223,12 @@ const char* kernel_name(int in_dtype, int d, int causal, int varlen, int out_dty
 const char* kernel_name_kv(int in_dtype, int d, int causal, int varlen, int out_dtype, int Hq,
                            int Hkv, int Nq, int sparse = 0, int vpack = 0);
 
+// Size of the library's fixed device scratch (fa_fwd_kv_split_noalloc's
+// split-KV partials), and its device address on the current device
+// (nullptr if unavailable).  Calls that overlap on one device share it.
+constexpr uint64_t kNoAllocScratchBytes = 16ull << 20;
+void* noalloc_scratch();
+
 // Debug mode (FA_DEBUG=1): check a packed offset array (B + 1 entries in
 // device memory) on `stream` and wait for the verdict: FA_OK,
 // FA_ERR_SEQLENS if an entry fails seqlens_entry_ok, or FA_ERR_LAUNCH.

@@ -102,7 +102,8 @@ typedef enum {
   FA_ERR_LAUNCH = -10,  /* the kernel launch failed */
   FA_ERR_WORKSPACE = -11, /* a caller workspace below its stated size */
   FA_ERR_ALLOC = -12,   /* reserved: no entry point allocates memory */
-  FA_ERR_SEQLENS = -13  /* FA_DEBUG=1 only: corrupt cu_seqlens contents */
+  FA_ERR_SEQLENS = -13, /* FA_DEBUG=1 only: corrupt cu_seqlens contents */
+  FA_ERR_SCRATCH = -14  /* fa_fwd_kv_split_noalloc: partials above the fixed scratch */
 } fa_status;
 
 /* Exact attention forward (see the header comment).  q, k, v: inputs in
@@ -208,6 +209,25 @@ int fa_fwd_kv_split_packed(const void* q, const void* k, const void* vt, size_t 
                            int causal, float scale, const int* cu_seqlens_q,
                            const int* cu_seqlens_k, int num_splits, void* part,
                            size_t part_bytes, void* stream, int in_dtype, int out_dtype);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * fa_fwd_kv_split with the split-KV partials in a fixed device buffer the
+ * library holds instead of a caller workspace.  Same results as
+ * fa_fwd_kv_split with the same num_splits (the same kernels).  The buffer
+ * is fa_noalloc_scratch_bytes() bytes (16 MiB) on each device the library
+ * runs on, kept until the process ends; calls whose partials,
+ * fa_split_workspace_bytes(B, Hq, Nq, d, num_splits), exceed it return
+ * FA_ERR_SCRATCH before anything is enqueued.  Every call on one device
+ * uses the same buffer, so calls that overlap in time on one device (other
+ * streams, other threads) race: the caller serialises them.  Calls no
+ * hipMalloc, hipFree or allocating library routine.  Other arguments and
+ * errors as fa_fwd_kv_split. */
+int fa_fwd_kv_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                            float scale, const int* cu_seqlens_q, const int* cu_seqlens_k,
+                            int num_splits, void* stream, int in_dtype, int out_dtype);
+size_t fa_noalloc_scratch_bytes(void);
 
 /* Backward pass: the gradients dQ, dK, dV of sum(O * dO) for the forward of
  * fa_fwd (same B, Hq, Hkv, N, d, causal, scale, cu_seqlens and layouts).
