@@ -26,12 +26,21 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s at 1 MI355X (% of MFMA peak), bf16 causal d=128 N=4096"
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
-PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-# The attention kernel's sources (a counter summary is used only while these
+# MI355X dense MFMA peaks by input type (the fp32 path's products run on the
+# fp32 MFMA), at the 2.4 GHz peak engine clock, and HBM3E bandwidth.
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
+PEAK_CLOCK_GHZ = 2.4
+PEAK_HBM_GBS = 8000.0
+XCDS = 8
+# Sources of each kernel family (a counter summary is used only while they
 # are unchanged).
-KERNEL_SRCS = [os.path.join(ROOT, "exact_io_aware_amd", "csrc", f)
-               for f in ("fa_fwd_mfma.h", "fa_device.h")]
+_CSRC = os.path.join(ROOT, "exact_io_aware_amd", "csrc")
+KERNEL_SRCS = {
+    "fa_fwd_mfma": ("fa_fwd_mfma.h", "fa_device.h"),
+    "fa_decode_mfma": ("fa_fwd_kernels.hip", "fa_device.h"),
+    "fa_fwd_f32": ("fa_fwd_kernels.hip", "fa_device.h"),
+    "fa_bwd": ("fa_bwd_kernels.hip", "fa_device.h"),
+}
 
 
 def parse():
@@ -54,25 +63,39 @@ def parse():
     return ap.parse_args()
 
 
-def source_digest() -> str:
+def source_digest(kernel: str) -> str:
+    """sha256 (first 16 hex digits) of the sources of the kernel's family."""
+    fam = next(k for k in KERNEL_SRCS if kernel.startswith(k))
     h = hashlib.sha256()
-    for path in KERNEL_SRCS:
-        with open(path, "rb") as f:
+    for name in KERNEL_SRCS[fam]:
+        with open(os.path.join(_CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel: str, workload: str):
-    """HBM bytes per launch from a committed counter summary, if it was taken
-    on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+def counters_for(kernel: str, workload: str):
+    """The committed counter summary of this kernel on this workload
+    (profiles/counters_<workload>.json), if it was taken on the current
+    kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha") != source_digest() or t.get("kernel") != kernel:
+    if t.get("kernel") != kernel or t.get("kernel_source_sha") != source_digest(kernel):
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t
+
+
+def clock_of(counters, launch_ms: float):
+    """Shader clock of the timed launches: the kernel's GPU-active cycles
+    per XCD (GRBM_GUI_ACTIVE of the counter run, summed over the XCDs) over
+    the live average launch time; None for launches under 50 us."""
+    if counters is None or not counters.get("grbm_gui_active_per_dispatch"):
+        return None
+    if counters.get("dispatch_ns", 0) < 50000:   # a launch's fixed cost dominates
+        return None
+    return counters["grbm_gui_active_per_dispatch"] / XCDS / (launch_ms * 1e6)
 
 
 def cpu_baseline(w, heads: int):
@@ -292,6 +315,15 @@ def main():
     # The rest of a step: the gaps between launches.
     gap_ms = [marks[i][1].elapsed_time(marks[i + 1][0]) for i in range(args.steps - 1)]
 
+    ctr = counters_for(kname, w["name"]) if args.which == "fwd" else None
+    ghz = clock_of(ctr, avg_launch_ms)
+    clock = None
+    if ghz is not None:
+        clock = {"ghz": round(ghz, 3),
+                 "source": "GRBM_GUI_ACTIVE per XCD (committed counter run) / live launch time",
+                 "counter_run_ghz": round(ctr["grbm_gui_active_per_dispatch"] / XCDS /
+                                          ctr["dispatch_ns"], 3)}
+    traffic = ctr["hbm_bytes_per_launch"] if ctr else None
     if decode:
         # HBM-bound: algorithmic bytes = Q, K and the packed V^T read once,
         # O (out dtype) and L written once; per attention call.
@@ -304,13 +336,16 @@ def main():
         gbs = nbytes / (avg_launch_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                    "traffic": traffic_for(kname, w["name"]),
+                    "traffic": traffic, "clock": clock,
                     "algorithmic_bytes_per_launch": nbytes, "num_splits": n_splits}
     else:
+        peak = PEAK_TFLOPS[w["dtype"]]
         roofline = {"bound": "mfma", "achieved": round(achieved, 2),
-                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                    "traffic": traffic_for(kname, w["name"]) if args.which == "fwd" else None}
+                    "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(achieved / peak, 4), "traffic": traffic, "clock": clock}
+        if ghz is not None:
+            # The same fraction against the peak at the measured clock.
+            roofline["frac_at_clock"] = round(achieved / (peak * ghz / PEAK_CLOCK_GHZ), 4)
     rec = {
         "metric": (METRIC if args.which == "fwd" and w["name"] == "gqa_bf16" else
                    f"attention {args.which} TFLOP/s at 1 MI355X (% of MFMA peak), {w['name']}"),
