@@ -95,6 +95,66 @@ def grad_bar(dtype: str) -> float:
     return 4.0 * {"bf16": 2.0 ** -8, "fp16": 2.0 ** -11}[dtype]
 
 
+def grad_term_sums(w: dict):
+    """Per-element sums of absolute terms of the three gradients, the scale of
+    the backward's rounding error element by element (test infrastructure,
+    float64 numpy; not the oracle).
+
+    The backward rounds P (for dV = P^T dO) and dS = P (dP - D) (for dK and
+    dQ) to the input precision and sums in fp32; D comes from the forward's
+    O, which carries that pass's P rounding.  So, with A_r = sum_c |dO_rc|
+    (P |V|)_rc (a bound on |D_r| and, times u, on its error):
+
+        |err dV_jc| <~ u * sum_r P_rj |dO_rc|
+        |err dK_jc| <~ 3u * |scale| * sum_r P_rj (|dP_rj| + A_r) |Q_rc|
+        |err dQ_rc| <~ 3u * |scale| * sum_j P_rj (|dP_rj| + A_r) |K_jc|
+
+    (dS: u from its own rounding and u from P's, each of P |dP - D| <=
+    P (|dP| + A_r), plus P |err D_r| <= u P A_r.)
+
+    Returns (T_dQ, T_dK, T_dV) in the layouts of q, k, v (grouped K/V heads
+    sum over their query heads)."""
+    q, k, v = f64_inputs(w)
+    import workloads
+    do = workloads.to_f64(w["dout"], w["dtype"])
+    scale, causal, cu = w["scale"], w["causal"], w["cu_seqlens"]
+    Hq, Hkv = q.shape[-2] if cu is not None else q.shape[1], k.shape[-2] if cu is not None else k.shape[1]
+    tq, tk, tv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    B = len(cu) - 1 if cu is not None else q.shape[0]
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            if cu is None:
+                qs, ks, vs, ds = q[b, h], k[b, g], v[b, g], do[b, h]
+            else:
+                a, e = int(cu[b]), int(cu[b + 1])
+                qs, ks, vs, ds = q[a:e, h], k[a:e, g], v[a:e, g], do[a:e, h]
+            n = qs.shape[0]
+            if n == 0:
+                continue
+            s_ = scale * (qs @ ks.T)
+            if causal:
+                s_ = np.where(np.tril(np.ones((n, n), dtype=bool)), s_, -np.inf)
+            m = s_.max(axis=1, keepdims=True)
+            p_ = np.exp(s_ - m)
+            p_ /= p_.sum(axis=1, keepdims=True)
+            dp = np.abs(ds @ vs.T)
+            arow = (np.abs(ds) * (p_ @ np.abs(vs))).sum(axis=1, keepdims=True)
+            wgt = p_ * (dp + arow)
+            rq = abs(scale) * (wgt @ np.abs(ks))
+            rk = abs(scale) * (wgt.T @ np.abs(qs))
+            rv = p_.T @ np.abs(ds)
+            if cu is None:
+                tq[b, h] = rq
+                tk[b, g] += rk
+                tv[b, g] += rv
+            else:
+                tq[a:e, h] = rq
+                tk[a:e, g] += rk
+                tv[a:e, g] += rv
+    return tq, tk, tv
+
+
 def compare_qk(w, O, L, Oref, Lref, out_dtype="fp32"):
     """Element-wise bars; rows that see no key must give O = 0, L = -inf;
     L rows past a packed sequence's query count stay untouched (NaN)."""
