@@ -498,6 +498,11 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16, D, CAUSAL), 2) void fa_f
     // or the empty row groups of a decode step) only takes part in the
     // loads and barriers.
     if (!active) return;
+    // Past the step that drains the wave's last block (causal: a wave's
+    // rows end before its workgroup's) there is nothing left to add.
+    if constexpr (!SPARSE) {
+      if (blk0 + st - 1 >= wave_blk_end) return;
+    }
     int kb;
     bool live;
     blk(st, e_st, kb, live);
