@@ -630,7 +630,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_f32(FwdParams p) {
 // ---------------------------------------------------------------------------
 // Debug check of packed offsets (FA_DEBUG=1): entry i of cu (i = 0 .. B)
 // must satisfy seqlens_entry_ok (cu[0] = 0, non-decreasing, each length at
-// most n_max).  One workgroup; the verdict (0 good, 1 bad) goes to *bad.
+// most n_max).  One workgroup; the outcome (0 good, 1 bad) goes to *bad.
 __global__ __launch_bounds__(256) void fa_check_seqlens_kernel(const int* cu, int B, int n_max,
                                                                int* bad) {
   int fail = 0;
@@ -769,7 +769,7 @@ const char* kernel_name_kv(int in_dtype, int d, int causal, int varlen, int out_
   return v ? v->name : nullptr;
 }
 
-// The debug check's verdict, one per device.
+// The debug check's outcome, one per device.
 __device__ int g_seqlens_bad;
 
 // Fixed device memory for the split-KV partials of fa_fwd_kv_split_noalloc
@@ -797,7 +797,7 @@ void* noalloc_scratch() {
 }
 
 int debug_check_seqlens(const int* cu, int B, int n_max, void* stream) {
-  static std::mutex mu;                       // one verdict slot per device
+  static std::mutex mu;                       // one outcome slot per device
   std::lock_guard<std::mutex> lock(mu);
   int* bad = nullptr;
   if (hipGetSymbolAddress((void**)&bad, HIP_SYMBOL(g_seqlens_bad)) != hipSuccess || !bad)
@@ -806,12 +806,12 @@ int debug_check_seqlens(const int* cu, int B, int n_max, void* stream) {
   if (hipLaunchKernel((const void*)fa_check_seqlens_kernel, dim3(1), dim3(256), args, 0,
                       (hipStream_t)stream) != hipSuccess)
     return FA_ERR_LAUNCH;
-  int verdict = 1;
-  if (hipMemcpyAsync(&verdict, bad, sizeof(int), hipMemcpyDeviceToHost, (hipStream_t)stream) !=
+  int outcome = 1;
+  if (hipMemcpyAsync(&outcome, bad, sizeof(int), hipMemcpyDeviceToHost, (hipStream_t)stream) !=
           hipSuccess ||
       hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
     return FA_ERR_LAUNCH;
-  return verdict == 0 ? FA_OK : FA_ERR_SEQLENS;
+  return outcome == 0 ? FA_OK : FA_ERR_SEQLENS;
 }
 
 int launch_fwd(const LaunchArgs& a, void* stream) {

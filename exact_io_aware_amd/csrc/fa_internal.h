@@ -230,7 +230,7 @@ constexpr uint64_t kNoAllocScratchBytes = 16ull << 20;
 void* noalloc_scratch();
 
 // Debug mode (FA_DEBUG=1): check a packed offset array (B + 1 entries in
-// device memory) on `stream` and wait for the verdict: FA_OK,
+// device memory) on `stream` and wait for the outcome: FA_OK,
 // FA_ERR_SEQLENS if an entry fails seqlens_entry_ok, or FA_ERR_LAUNCH.
 // Synchronises `stream`; calls are serialised.
 int debug_check_seqlens(const int* cu, int B, int n_max, void* stream);

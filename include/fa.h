@@ -69,7 +69,7 @@
  * checking them would need a device-to-host read: the caller must pass valid
  * offsets.  With the environment variable FA_DEBUG=1 (read once per
  * process) every entry point that takes packed offsets first checks them
- * on the device and waits for the verdict: corrupt offsets give
+ * on the device and waits for the outcome: corrupt offsets give
  * FA_ERR_SEQLENS and no attention kernel runs.  That mode synchronises the
  * stream (it cannot be captured into a graph) and serialises the checks of
  * concurrent calls.  The Kotaemon page's caveats warn that a misconfigured

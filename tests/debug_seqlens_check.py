@@ -84,7 +84,7 @@ def main() -> int:
             else:
                 assert torch.isnan(o).all() and torch.isnan(lse).all(), (label, entry)
             print(f"  {entry}: status {st}", flush=True)
-    # The predicate itself, on the host, agrees with the device verdicts.
+    # The predicate itself, on the host, agrees with the device outcomes.
     for label, offs, want in cases:
         assert fa.check_seqlens(np.array(offs, np.int32), len(offs) - 1, N) == S[want]
     print("DEBUG_SEQLENS_OK", flush=True)

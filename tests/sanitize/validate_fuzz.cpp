@@ -1,6 +1,6 @@
 // Host-only driver of the argument checks (fa_validate.cpp) for a build with
 // AddressSanitizer and UndefinedBehaviorSanitizer: a table of cases with
-// known verdicts, then a deterministic sweep of extreme and random
+// known outcomes, then a deterministic sweep of extreme and random
 // arguments (sizes near the 32- and 64-bit limits, odd addresses, NaN and
 // infinite scales) through every check, so that an overflow or an
 // out-of-bounds read in the checks is reported by the sanitizers.
@@ -64,7 +64,7 @@ float pick_scale() {
 
 int main() {
   using namespace fa;
-  // Known verdicts (the layout of a small GQA launch at fake, aligned,
+  // Known outcomes (the layout of a small GQA launch at fake, aligned,
   // non-overlapping addresses; the checks never dereference them).
   const uintptr_t q = 0x100000, k = 0x200000, v = 0x300000, o = 0x400000, l = 0x500000;
   auto base = [&](float scale, int d, int dt, uintptr_t oo) {

@@ -1,6 +1,6 @@
 """The argument checks (fa_validate.cpp) built for the host alone with g++
 under AddressSanitizer and UndefinedBehaviorSanitizer, driven by
-tests/sanitize/validate_fuzz.cpp: known verdicts plus a sweep of extreme and
+tests/sanitize/validate_fuzz.cpp: known outcomes plus a sweep of extreme and
 random arguments.  Any sanitizer report fails the test.  No GPU needed."""
 from __future__ import annotations
 
