@@ -56,6 +56,10 @@ def parse():
     ap.add_argument("--cpu-sample-heads", type=int, default=0,
                     help="query heads (from the first sequences) the oracle is timed on; "
                          "0 = the whole workload")
+    ap.add_argument("--cold", action="store_true",
+                    help="overwrite a 512 MiB buffer before every step, so the inputs come "
+                         "from HBM and not from the 256 MB last-level cache; the fill is "
+                         "outside the attention launch's events but inside ms_per_step")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
                          "(reads and writes that many bytes once), to scale memory "
@@ -265,7 +269,11 @@ def main():
                          dtype=torch.uint8, device=dev)
         bwd_state = (dout, o_f, lse_f, ws)
 
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
+
     def step(mark=None):
+        if scrub is not None:
+            scrub.fill_(1)     # evicts the inputs from the caches
         if bwd_state is not None:
             dout, o_f, lse_f, ws = bwd_state
             if mark is not None:
@@ -352,6 +360,7 @@ def main():
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "cache": "cold (512 MiB written before each step)" if args.cold else "warm",
         "dtype": w["dtype"], "data": "synthetic",
         "config": {"workload": w["name"], "B": w["B"], "Hq": w["Hq"], "Hkv": w["Hkv"],
                    "N": w["N"], "Nk": Nk, "d": w["d"], "causal": w["causal"],
