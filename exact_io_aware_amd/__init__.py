@@ -11,5 +11,6 @@ from ._lib import (  # noqa: F401
     bwd_workspace_bytes, num_splits, split_workspace_bytes, supported, version,
     workspace_bytes,
 )
+from .autograd import attention  # noqa: F401
 from .bwd import bwd  # noqa: F401
 from .fwd import fwd, flops, pack_v  # noqa: F401
