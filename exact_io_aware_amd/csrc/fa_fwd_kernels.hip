@@ -185,33 +185,34 @@ __global__ __launch_bounds__(256, 1) void fa_decode_mfma(FwdParams p) {
   // (bounded buffers); the loads are issued unconditionally so every path
   // keeps the same loads in flight.
   struct Stage { u32x4 x[LOADS]; };
-  auto gload = [&](int j, Stage& st) __attribute__((always_inline)) {
+  struct TileRes { rsrc_t rk, rv; };
+  auto tile_res = [&](int j) __attribute__((always_inline)) -> TileRes {
     const int t = t0 + wave + NW * j;
     const int kb = 64 * t;
     const bool in = j < my_tiles;
     const int rows = __builtin_amdgcn_readfirstlane(in ? max(0, min(len_k - kb, 64)) : 0);
-    const rsrc_t rk = make_rsrc(kp + (long long)min(kb, len_k) * kv_rs_bytes,
-                                (uint32_t)rows * kv_rs_bytes);
-    const rsrc_t rv = VPACK ? make_rsrc(vtp + (long long)(in ? t : 0) * TILE_BYTES,
-                                        in ? (uint32_t)TILE_BYTES : 0u)
-                            : make_rsrc(vp + (long long)min(kb, len_k) * kv_rs_bytes,
-                                        (uint32_t)rows * kv_rs_bytes);
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int q = 64 * i + lane;
-      if (i < TILE_BYTES / 1024) {
-        const int r = q / CPR, pc = q % CPR;
-        st.x[i] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, r * kv_rs_bytes + 16 * pc, 0, kNT));
-      } else if (VPACK) {
-        st.x[i] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, 16 * (q - TILE_BYTES / 16), 0, kNT));
-      } else {
-        const int qv = q - TILE_BYTES / 16;
-        const int r = qv / CPR, pc = qv % CPR;
-        st.x[i] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, r * kv_rs_bytes + 16 * pc, 0, kNT));
-      }
+    TileRes r;
+    r.rk = make_rsrc(kp + (long long)min(kb, len_k) * kv_rs_bytes, (uint32_t)rows * kv_rs_bytes);
+    r.rv = VPACK ? make_rsrc(vtp + (long long)(in ? t : 0) * TILE_BYTES,
+                             in ? (uint32_t)TILE_BYTES : 0u)
+                 : make_rsrc(vp + (long long)min(kb, len_k) * kv_rs_bytes,
+                             (uint32_t)rows * kv_rs_bytes);
+    return r;
+  };
+  auto gload1 = [&](const TileRes& r, int i) __attribute__((always_inline)) -> u32x4 {
+    const int q = 64 * i + lane;
+    if (i < TILE_BYTES / 1024) {
+      const int rr = q / CPR, pc = q % CPR;
+      return __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(r.rk, rr * kv_rs_bytes + 16 * pc, 0, kNT));
+    } else if (VPACK) {
+      return __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(r.rv, 16 * (q - TILE_BYTES / 16), 0, kNT));
+    } else {
+      const int qv = q - TILE_BYTES / 16;
+      const int rr = qv / CPR, pc = qv % CPR;
+      return __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(r.rv, rr * kv_rs_bytes + 16 * pc, 0, kNT));
     }
   };
   // ... and into the wave's LDS slot, swizzled for the operand reads: K
@@ -219,22 +220,19 @@ __global__ __launch_bounds__(256, 1) void fa_decode_mfma(FwdParams p) {
   // chunk vc of row vr at vc ^ vt_swz(vr) (rows of 128 bytes); row-major V
   // chunk pc of row r at pc ^ rm_swz(r) (rows of RB bytes).
   char* const my_slot = slots + wave * STAGE;
-  auto swrite = [&](const Stage& st) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int q = 64 * i + lane;
-      if (i < TILE_BYTES / 1024) {
-        const int r = q / CPR, pc = q % CPR;
-        *(u32x4*)(my_slot + r * RB + ((pc ^ k_swz<D>(r)) << 4)) = st.x[i];
-      } else if (VPACK) {
-        const int qv = q - TILE_BYTES / 16;
-        const int vr = qv >> 3, vc = qv & 7;
-        *(u32x4*)(my_slot + TILE_BYTES + vr * 128 + ((vc ^ vt_swz(vr)) << 4)) = st.x[i];
-      } else {
-        const int qv = q - TILE_BYTES / 16;
-        const int r = qv / CPR, pc = qv % CPR;
-        *(u32x4*)(my_slot + TILE_BYTES + r * RB + ((pc ^ rm_swz<D>(r)) << 4)) = st.x[i];
-      }
+  auto swrite1 = [&](const u32x4& x, int i) __attribute__((always_inline)) {
+    const int q = 64 * i + lane;
+    if (i < TILE_BYTES / 1024) {
+      const int r = q / CPR, pc = q % CPR;
+      *(u32x4*)(my_slot + r * RB + ((pc ^ k_swz<D>(r)) << 4)) = x;
+    } else if (VPACK) {
+      const int qv = q - TILE_BYTES / 16;
+      const int vr = qv >> 3, vc = qv & 7;
+      *(u32x4*)(my_slot + TILE_BYTES + vr * 128 + ((vc ^ vt_swz(vr)) << 4)) = x;
+    } else {
+      const int qv = q - TILE_BYTES / 16;
+      const int r = qv / CPR, pc = qv % CPR;
+      *(u32x4*)(my_slot + TILE_BYTES + r * RB + ((pc ^ rm_swz<D>(r)) << 4)) = x;
     }
   };
 
@@ -330,11 +328,21 @@ __global__ __launch_bounds__(256, 1) void fa_decode_mfma(FwdParams p) {
 
   // Tile j + 1 loads into the registers while tile j, written to the slot,
   // is computed (its second half only when it holds keys before k_stop).
+  // Each staged register is reloaded with tile j + 1 as soon as its part of
+  // tile j is in the slot, so a wave keeps a whole tile's loads in flight.
   Stage st;
-  gload(0, st);
+  {
+    const TileRes r0 = tile_res(0);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) st.x[i] = gload1(r0, i);
+  }
   for (int j = 0; j < my_tiles; ++j) {
-    swrite(st);
-    gload(j + 1, st);
+    const TileRes rn = tile_res(j + 1);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      swrite1(st.x[i], i);
+      st.x[i] = gload1(rn, i);
+    }
     const int kb = 64 * (t0 + wave + NW * j);
     compute(kb, 0);
     if (kb + 32 < k_stop) compute(kb + 32, 1);
