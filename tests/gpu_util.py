@@ -173,36 +173,3 @@ def compare_qk(w, O, L, Oref, Lref, out_dtype="fp32"):
     if w["dtype"] == "fp32":
         assert eo.max() <= FP32_STRICT and el.max() <= FP32_STRICT
     return float(eo.max()), float(el.max())
-
-
-def oracle_rows_parallel(q, k, v, *, causal, scale, picks, cu_seqlens=None, workers=None,
-                         chunk=1024):
-    """The oracle's attention_rows over many picks, cut into chunks run by a
-    thread pool (numpy's products and exponentials release the interpreter
-    lock; one BLAS thread per worker).  Same results as one call."""
-    import concurrent.futures
-
-    import oracle
-    picks = list(picks)
-    if workers is None:
-        workers = min(16, oracle.default_workers())
-    parts = [picks[i:i + chunk] for i in range(0, len(picks), chunk)]
-
-    def one(part):
-        return oracle.attention_rows(q, k, v, causal=causal, scale=scale, picks=part,
-                                     cu_seqlens=cu_seqlens)
-
-    try:
-        from threadpoolctl import threadpool_limits
-        limit = threadpool_limits(1)
-    except Exception:   # pragma: no cover - threadpoolctl is installed here
-        limit = None
-    try:
-        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
-            res = list(ex.map(one, parts))
-    finally:
-        if limit is not None:
-            limit.restore_original_limits()
-    O = np.concatenate([r[0] for r in res]) if res else np.empty((0, v.shape[-1]))
-    L = np.concatenate([r[1] for r in res]) if res else np.empty(0)
-    return O, L
