@@ -135,24 +135,23 @@ def test_sparse_row_major_matches_packed():
     assert np.array_equal(np.nan_to_num(L1, nan=7.0), np.nan_to_num(L2, nan=7.0))
 
 
-def test_streaming_workload_sampled_heads():
+def test_streaming_workload_full():
     """The streaming_bf16 workload at full size (B=4, 32 query heads,
     N=4096, sink + 1024-key window), in the launch configuration the bench
-    times; four (sequence, head) units checked against the oracle in full."""
+    times, against the oracle on every sequence and head."""
     w = workloads.make_inputs("streaming_bf16")
     w["Nk"], w["cu_seqlens_k"] = w["N"], None
     G.say("workload streaming_bf16")
     O, L = _run(w)
     q, k, v = G.f64_inputs(w)
-    for b, h in ((0, 0), (1, 13), (2, 22), (3, 31)):
-        g = h // 4
-        Oref, Lref = oracle.attention_block_sparse(
-            q[b:b + 1, h:h + 1], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1], w["block_mask"],
-            causal=True, scale=w["scale"])
-        eo = np.abs(O[b, h] - Oref[0, 0]).max()
-        el = np.abs(L[b, h] - Lref[0, 0]).max()
-        G.say(f"  unit ({b},{h}) errors O {eo:.3e} L {el:.3e}")
-        assert eo <= G.O_TOL["bf16"] and el <= G.L_TOL
+    Oref, Lref = oracle.attention_block_sparse(q, k, v, w["block_mask"], causal=True,
+                                               scale=w["scale"],
+                                               workers=min(16, oracle.default_workers()))
+    assert np.isfinite(O).all() and np.isfinite(L).all()
+    eo = np.abs(O - Oref).max()
+    el = np.abs(L - Lref).max()
+    G.say(f"  errors O {eo:.3e} L {el:.3e}")
+    assert eo <= G.O_TOL["bf16"] and el <= G.L_TOL
 
 
 def test_sparse_longest_tile_list():
