@@ -117,19 +117,23 @@ def test_backward_gradients_in_input_dtype_and_deterministic():
         assert (np.abs(x - r) <= bar).all(), name
 
 
-def test_backward_headline_shape_full():
-    """The backward of gqa_bf16 at full size (B=4, Hq=32, Hkv=8, N=4096,
-    d=128, causal), checked against the oracle on every sequence and head."""
-    w = workloads.make_inputs("gqa_bf16")
-    w["dout"] = workloads.make_custom(4, 32, 32, 128, "bf16", seed=1103, N=4096)["q"]
-    G.say("backward gqa_bf16")
+@pytest.mark.parametrize("name", ["gqa_bf16", "mha_fp16"])
+def test_backward_workload_full(name):
+    """The backward at the full size of the workloads bench.py times for it
+    (gqa_bf16: B=4, Hq=32, Hkv=8, N=4096, d=128; mha_fp16: B=8, H=12,
+    N=2048, d=64; causal; dO drawn as bench.py draws it), checked against
+    the oracle on every sequence and head."""
+    w = workloads.make_inputs(name)
+    w["dout"] = workloads.make_custom(w["B"], w["Hq"], w["Hq"], w["d"], w["dtype"],
+                                      seed=w["seed"] + 100, N=w["N"])["q"]
+    G.say(f"backward {name}")
     got = _gpu(w)
     q, k, v = G.f64_inputs(w)
-    do = workloads.to_f64(w["dout"], "bf16")
+    do = workloads.to_f64(w["dout"], w["dtype"])
     ref = oracle.attention_backward(q, k, v, do, causal=True, scale=w["scale"],
                                     workers=min(16, oracle.default_workers()))
-    for name, a, r in zip(("dq", "dk", "dv"), got, ref):
+    for name_, a, r in zip(("dq", "dk", "dv"), got, ref):
         err = np.abs(a - r)
-        G.say(f"  {name}: max err {err.max():.3e}, max |ref| {np.abs(r).max():.3e}")
+        G.say(f"  {name_}: max err {err.max():.3e}, max |ref| {np.abs(r).max():.3e}")
         assert np.isfinite(a).all()
-        assert err.max() <= G.grad_bar("bf16") * np.abs(r).max(), name
+        assert err.max() <= G.grad_bar(w["dtype"]) * np.abs(r).max(), name_
