@@ -3,7 +3,6 @@ long key/value cache, with the keys split across workgroups and the partial
 results merged through their logsumexps (split-KV).  Needs an MI355X."""
 from __future__ import annotations
 
-import numpy as np
 import pytest
 
 import oracle
