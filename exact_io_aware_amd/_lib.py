@@ -86,6 +86,10 @@ def load() -> ctypes.CDLL:
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
     lib.fa_version.restype = i
+    lib.fa_debug_force_order.argtypes = [i]
+    lib.fa_debug_force_order.restype = i
+    lib.fa_debug_forced_order.argtypes = []
+    lib.fa_debug_forced_order.restype = i
     _lib = lib
     return lib
 
@@ -96,6 +100,19 @@ def status_string(status: int) -> str:
 
 def version() -> int:
     return load().fa_version()
+
+
+def debug_force_order(order: int) -> None:
+    """fa_debug_force_order: -1 restores the library's own launch order; 0-3
+    force unit-major / +XCD remap / row-block-major / +XCD remap."""
+    st = load().fa_debug_force_order(order)
+    if st != 0:
+        raise ValueError(f"fa_debug_force_order({order}): {status_string(st)}")
+
+
+def debug_forced_order() -> int:
+    """The launch order currently forced (-1: the library's own choice)."""
+    return load().fa_debug_forced_order()
 
 
 def kernel_name(in_dtype: int, d: int, causal: bool, varlen: bool, out_dtype: int):

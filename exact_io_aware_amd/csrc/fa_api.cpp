@@ -1,6 +1,7 @@
 // C ABI of libfa (declared and documented in include/fa.h).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -56,9 +57,32 @@ int debug_seqlens(const int* cu_q, const int* cu_k, int B, int Nq, int Nk, void*
   return st;
 }
 
+// The forced launch order: FA_FORCE_ORDER (-1 .. 3) at first use, then
+// whatever fa_debug_force_order sets.
+std::atomic<int>& order_setting() {
+  static std::atomic<int> v{[] {
+    const char* e = std::getenv("FA_FORCE_ORDER");
+    if (e == nullptr) return -1;
+    char* end = nullptr;
+    const long x = std::strtol(e, &end, 10);
+    return (end != e && *end == '\0' && x >= -1 && x <= 3) ? (int)x : -1;
+  }()};
+  return v;
+}
+
 }  // namespace
 
+int fa::forced_order() { return order_setting().load(std::memory_order_relaxed); }
+
 extern "C" {
+
+int fa_debug_force_order(int order) {
+  if (order < -1 || order > 3) return FA_ERR_SHAPE;
+  order_setting().store(order, std::memory_order_relaxed);
+  return FA_OK;
+}
+
+int fa_debug_forced_order(void) { return fa::forced_order(); }
 
 int fa_fwd_check(const void* q, const void* k, const void* v, const void* o,
                  const float* lse, int B, int Hq, int Hkv, int N, int d,

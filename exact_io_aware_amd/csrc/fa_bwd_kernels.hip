@@ -725,6 +725,10 @@ int launch_bwd(const BwdArgs& a, void* stream) {
         cus > 0 && per_cu > 0)
       p.rb_major = plan.total_wg <= 4ull * (uint64_t)cus * (uint64_t)per_cu;
   }
+  if (const int fo = forced_order(); fo >= 0) {     // a test of order independence
+    p.xcd_remap = (fo & 1) && p.n_units % 8 == 0;
+    p.rb_major = (fo & 2) ? 1 : 0;
+  }
   p.kv_blocks = (a.N + 255) / 256;
   p.scale = a.scale; p.scale_log2 = a.scale * kLog2e;
   const long long d = a.d;

@@ -880,6 +880,10 @@ int launch_fwd(const LaunchArgs& a, void* stream) {
     p.mask_bs = a.mask_batches > 1 ? slab * a.mask_heads : 0;
   }
   if (n_splits > 1) p.xcd_remap = 0;
+  if (const int fo = forced_order(); fo >= 0) {     // a test of order independence
+    p.xcd_remap = (fo & 1) && a.in_dtype != FA_F32 && n_splits == 1 && p.n_units % 8 == 0;
+    p.rb_major = (fo & 2) ? 1 : 0;
+  }
   const long long d = a.d;
   if (varlen) {
     p.q_bs = 0; p.q_hs = d; p.q_rs = (long long)a.Hq * d;

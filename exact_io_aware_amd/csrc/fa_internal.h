@@ -229,6 +229,10 @@ const char* kernel_name_kv(int in_dtype, int d, int causal, int varlen, int out_
 constexpr uint64_t kNoAllocScratchBytes = 16ull << 20;
 void* noalloc_scratch();
 
+// The launch order fa_debug_force_order (or FA_FORCE_ORDER) sets: -1 for the
+// library's own choice, else bit 0 = XCD remap, bit 1 = row-block-major.
+int forced_order();
+
 // Debug mode (FA_DEBUG=1): check a packed offset array (B + 1 entries in
 // device memory) on `stream` and wait for the outcome: FA_OK,
 // FA_ERR_SEQLENS if an entry fails seqlens_entry_ok, or FA_ERR_LAUNCH.

@@ -324,6 +324,28 @@ const char* fa_kernel_name_ex(int in_dtype, int d, int causal, int varlen, int o
  * FA_ERR_SHAPE for B < 0.  Makes no HIP call. */
 int fa_check_seqlens(const int* cu_seqlens, int B, int n_max);
 
+/* Testing aid for order independence (no counterpart on the pages: every
+ * workgroup of the attention kernels writes only its own rows of O and L,
+ * or of dQ, and reads only the inputs, so the order in which workgroups are
+ * handed out must not change a single bit; a difference means a race).
+ * Forces that order for the 16-bit forward kernels (fa_fwd, fa_fwd_kv,
+ * fa_fwd_sparse, the split-KV and packed forms; not the decode kernel) and
+ * for the dQ kernel of fa_bwd: -1 = the library's own choice (the default),
+ * 0 = unit-major, 1 = unit-major with the XCD remap, 2 = row-block-major,
+ * 3 = row-block-major with the XCD remap.  The remap applies only where the
+ * launch allows it (the number of (sequence, head group) units a multiple
+ * of 8, no KV split); the fp32 kernel, the decode kernel and the dK/dV
+ * kernel keep their single order.  The initial value is FA_FORCE_ORDER from
+ * the environment (the same numbers), else -1.  Process-wide; each launch
+ * reads it once, so set it only while no launch is being prepared on
+ * another thread.  Returns FA_OK, or FA_ERR_SHAPE for an order outside
+ * -1 .. 3 (the setting is then unchanged).  Makes no HIP call. */
+int fa_debug_force_order(int order);
+
+/* The launch order currently forced (-1 .. 3, as fa_debug_force_order
+ * takes it).  Makes no HIP call. */
+int fa_debug_forced_order(void);
+
 /* 1 if fa_fwd supports (in_dtype, d, causal), else 0 — so a caller can pick
  * another attention path when this one does not apply. */
 int fa_supported(int in_dtype, int d, int causal);

@@ -405,3 +405,33 @@ def test_sparse_flops_count_admitted_pairs():
             one = bm[:1, :1]
             want1 = 6 * oracle.sparse_pair_count(one[0, 0], nq, nk, causal)
             assert fa.flops(3, 16, [nq, nq], causal, [nk, nk], block_mask=one) == 4.0 * 16 * want1
+
+
+def test_force_order_setting():
+    """fa_debug_force_order takes -1 .. 3 and nothing else; no device call."""
+    before = fa.debug_forced_order()
+    try:
+        for order in (-1, 0, 1, 2, 3):
+            fa.debug_force_order(order)
+            assert fa.debug_forced_order() == order
+        for bad in (-2, 4, 1000):
+            assert fa.load().fa_debug_force_order(bad) == _lib.STATUS["FA_ERR_SHAPE"]
+            assert fa.debug_forced_order() == 3, "a rejected order leaves the setting alone"
+    finally:
+        fa.debug_force_order(before)
+
+
+@pytest.mark.parametrize("env,expected", [("2", 2), ("0", 0), ("-1", -1), ("7", -1),
+                                          ("rb", -1), ("", -1), (None, -1)])
+def test_force_order_from_environment(env, expected):
+    """FA_FORCE_ORDER gives the initial setting; anything outside -1 .. 3 is
+    ignored.  A fresh process reads it at first use."""
+    import sys
+    envs = dict(os.environ)
+    envs.pop("FA_FORCE_ORDER", None)
+    if env is not None:
+        envs["FA_FORCE_ORDER"] = env
+    code = "import exact_io_aware_amd as fa; print(fa.debug_forced_order())"
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                         check=True, env=envs, cwd=ROOT)
+    assert int(out.stdout.strip().splitlines()[-1]) == expected
