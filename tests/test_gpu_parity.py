@@ -273,6 +273,45 @@ def test_large_and_growing_scores(mult, ramp):
     G.say(f"  errors {_compare(w, O, L, Oref, Lref, bar=G.o_bar_derived('bf16', A))}")
 
 
+def _store(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float values (exactly representable) in the workload's storage form."""
+    if dtype == "bf16":
+        return workloads.round_to_bf16_bits(x.astype(np.float32))
+    return x.astype(np.float16)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp16", 64)])
+def test_shift_invariance(dtype, d):
+    """softmax is unchanged when every score of a row moves by one constant:
+    with K's first component 1 for every key, setting Q's first component of
+    row i to t_i adds scale * t_i to all of row i's scores.  O must stay
+    within the bar of the unshifted run (and of the oracle), and L must move
+    by exactly scale * t_i (up to fp32 rounding of L itself).  The shifts
+    reach +-724 at d = 128 and +-1024 at d = 64 in score units."""
+    w = _make((dtype, d, 2, 8, 2, 333, True), seed=51)
+    q, k, _ = G.f64_inputs(w)
+    k = k.copy()
+    k[..., 0] = 1.0
+    q0 = q.copy()
+    q0[..., 0] = 0.0
+    shifts = np.array([0.0, 8192.0, -8192.0, 512.0, -512.0, 64.0])
+    t = shifts[np.arange(q0[..., 0].size) % shifts.size].reshape(q0.shape[:-1])
+    q1 = q0.copy()
+    q1[..., 0] = t
+    w0, w1 = dict(w), dict(w)
+    w0["k"] = w1["k"] = _store(k, dtype)
+    w0["q"], w1["q"] = _store(q0, dtype), _store(q1, dtype)
+    G.say(f"shift invariance {dtype} d={d}")
+    O0, L0 = G.run_gpu(w0, lse_fill=float("nan"))
+    O1, L1 = G.run_gpu(w1, lse_fill=float("nan"))
+    Oref, Lref = _oracle(w1)
+    G.say(f"  errors {_compare(w1, O1, L1, Oref, Lref)}")
+    bar = G.O_TOL[dtype]
+    assert np.abs(O1 - O0).max() <= bar
+    dl = np.abs((L1 - L0) - w["scale"] * t)
+    assert dl.max() <= G.L_TOL + 2e-7 * np.abs(L1).max(), dl.max()
+
+
 def test_kernel_reported():
     import exact_io_aware_amd as fa
     assert fa.kernel_name(fa.FA_BF16, 128, True, False, fa.FA_F32) == \
