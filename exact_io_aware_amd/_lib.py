@@ -1,10 +1,12 @@
 """ctypes binding of libfa.so (include/fa.h).  Argument marshalling only."""
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+POISON_LIB_PATH = os.path.join(os.path.dirname(LIB_PATH), "libfa_poison.so")
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_OK = 0
@@ -19,16 +21,37 @@ STATUS = {
 _lib = None
 
 
+def _open(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m exact_io_aware_amd.build` "
+            "(there is no fallback path)")
+    return _bind(ctypes.CDLL(path))
+
+
 def load() -> ctypes.CDLL:
     """Load libfa.so once.  Raises if it has not been built."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(
-            f"{LIB_PATH} is missing: build it with `python -m exact_io_aware_amd.build` "
-            "(there is no fallback path)")
-    lib = ctypes.CDLL(LIB_PATH)
+    if _lib is None:
+        _lib = _open(LIB_PATH)
+    return _lib
+
+
+@contextlib.contextmanager
+def poisoned_lds():
+    """Test aid: while the block runs, every call goes to libfa_poison.so,
+    the same kernels built with their LDS filled with NaN before use (so a
+    read of LDS the kernel never wrote shows up as NaN).  Not thread-safe."""
+    global _lib
+    saved = load()
+    _lib = _open(POISON_LIB_PATH)
+    try:
+        yield _lib
+    finally:
+        _lib = saved
+
+
+def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, i, i]
     lib.fa_fwd.restype = i
@@ -90,7 +113,8 @@ def load() -> ctypes.CDLL:
     lib.fa_debug_force_order.restype = i
     lib.fa_debug_forced_order.argtypes = []
     lib.fa_debug_forced_order.restype = i
-    _lib = lib
+    lib.fa_build_flags.argtypes = []
+    lib.fa_build_flags.restype = i
     return lib
 
 

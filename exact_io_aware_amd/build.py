@@ -16,6 +16,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa.so")
+# The test build: the same kernels with their LDS filled with NaN before use
+# (FA_POISON_LDS=1; csrc/fa_poison.h).  Only tests load it.
+POISON_LIB = os.path.join(PKG, "libfa_poison.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["fa_fwd_mfma_bf16_d128.hip", "fa_fwd_mfma_f16_d128.hip", "fa_fwd_mfma_bf16_d64.hip",
@@ -53,15 +56,19 @@ def _jobs() -> int:
     return max(1, min(n, 16, len(SOURCES)))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile libfa.so; returns its path.  Raises on a compiler error."""
-    os.makedirs(OBJDIR, exist_ok=True)
+def build(verbose: bool = False, poison: bool = False) -> str:
+    """Compile libfa.so (poison: libfa_poison.so, the LDS-poisoning test
+    build); returns its path.  Raises on a compiler error."""
+    objdir = os.path.join(OBJDIR, "poison") if poison else OBJDIR
+    lib_path = POISON_LIB if poison else LIB
+    os.makedirs(objdir, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    defs = ["-DFA_POISON_LDS=1"] if poison else []
 
     def compile_one(src):
-        obj = os.path.join(OBJDIR, src + ".o")
-        return src, obj, _run([hipcc(), *HIPCC_FLAGS, *inc, "-c", os.path.join(CSRC, src),
-                               "-o", obj])
+        obj = os.path.join(objdir, src + ".o")
+        return src, obj, _run([hipcc(), *HIPCC_FLAGS, *defs, *inc, "-c",
+                               os.path.join(CSRC, src), "-o", obj])
 
     objs, errors, notes = [], [], []
     with concurrent.futures.ThreadPoolExecutor(max_workers=_jobs()) as ex:
@@ -70,16 +77,17 @@ def build(verbose: bool = False) -> str:
             (errors if rc != 0 else notes).extend(msgs)
     if errors:
         raise RuntimeError("hipcc failed:\n" + "\n".join(errors))
-    tmp = LIB + ".tmp"
+    tmp = lib_path + ".tmp"
     rc, msgs = _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
     if rc != 0:
         raise RuntimeError("link failed:\n" + "\n".join(msgs))
     notes.extend(msgs)
     if verbose and notes:
         print("\n".join(notes), file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build(verbose=True, poison=True))

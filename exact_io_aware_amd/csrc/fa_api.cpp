@@ -9,6 +9,7 @@
 
 #include "fa.h"
 #include "fa_internal.h"
+#include "fa_poison.h"
 
 namespace {
 
@@ -83,6 +84,8 @@ int fa_debug_force_order(int order) {
 }
 
 int fa_debug_forced_order(void) { return fa::forced_order(); }
+
+int fa_build_flags(void) { return fa::kPoisonLds ? FA_BUILD_POISON_LDS : 0; }
 
 int fa_fwd_check(const void* q, const void* k, const void* v, const void* o,
                  const float* lse, int B, int Hq, int Hkv, int N, int d,

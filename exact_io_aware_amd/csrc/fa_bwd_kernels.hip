@@ -37,6 +37,7 @@
 #include "fa.h"
 #include "fa_device.h"
 #include "fa_internal.h"
+#include "fa_poison.h"
 
 namespace fa {
 namespace {
@@ -135,6 +136,16 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv(BwdParams p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
+  if constexpr (kPoisonLds) {                // test build only
+    poison_lds(q_l0, TILE_BYTES, tid, NT);
+    poison_lds(q_l1, TILE_BYTES, tid, NT);
+    poison_lds(do_l0, TILE_BYTES, tid, NT);
+    poison_lds(do_l1, TILE_BYTES, tid, NT);
+    poison_lds(ld_l0, sizeof(ld_l0), tid, NT);
+    poison_lds(ld_l1, sizeof(ld_l1), tid, NT);
+    poison_lds(v_own, sizeof(v_own), tid, NT);
+    __syncthreads();
+  }
 
   // Key-block-major order: every (sequence, K/V head) takes its first key
   // block before any takes its second, so with the causal mask (early keys
@@ -418,6 +429,13 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16, D, CAUSAL), 2) void fa_b
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
+  if constexpr (kPoisonLds) {                // test build only
+    poison_lds(k_l0, TILE_BYTES, tid, NT);
+    poison_lds(k_l1, TILE_BYTES, tid, NT);
+    poison_lds(v_l0, TILE_BYTES, tid, NT);
+    poison_lds(v_l1, TILE_BYTES, tid, NT);
+    __syncthreads();
+  }
 
   // Workgroups are dealt round-robin over the 8 XCDs (workgroup j on XCD
   // j % 8).  With xcd_remap, XCD x takes the units u with u % 8 == x, each

@@ -20,6 +20,7 @@
 #include "fa_device.h"
 #include "fa_fwd_common.h"
 #include "fa_internal.h"
+#include "fa_poison.h"
 
 namespace fa {
 namespace {
@@ -58,6 +59,10 @@ __global__ __launch_bounds__(256) void fa_vt_pack(VtParams p) {
   __shared__ __attribute__((aligned(16))) char vl[64 * RB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if constexpr (kPoisonLds) {                // test build only
+    poison_lds(vl, sizeof(vl), tid, blockDim.x);
+    __syncthreads();
+  }
   const T* src = (const T*)p.v + (VARLEN ? (long long)seq0 * p.kv_rs : (long long)b * p.kv_bs) +
                  (long long)kvh * p.kv_hs + (long long)kb * p.kv_rs;
   const uint32_t rs_bytes = (uint32_t)p.kv_rs * 2;
@@ -120,6 +125,13 @@ __global__ __launch_bounds__(256, 1) void fa_decode_mfma(FwdParams p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
+  if constexpr (kPoisonLds) {                // test build only
+    poison_lds(slots, sizeof(slots), tid, blockDim.x);
+    poison_lds(q_lds, sizeof(q_lds), tid, blockDim.x);
+    poison_lds(m_s, sizeof(m_s), tid, blockDim.x);
+    poison_lds(l_s, sizeof(l_s), tid, blockDim.x);
+    __syncthreads();
+  }
 
   int wg = blockIdx.x, split = 0;
   if (p.n_splits > 1) {
@@ -489,6 +501,11 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_f32(FwdParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
+  if constexpr (kPoisonLds) {                // test build only
+    poison_lds(ks, sizeof(ks), tid, blockDim.x);
+    poison_lds(vs, sizeof(vs), tid, blockDim.x);
+    __syncthreads();
+  }
 
   const int unit = blockIdx.x / p.n_rblocks;
   int rb = blockIdx.x - unit * p.n_rblocks;

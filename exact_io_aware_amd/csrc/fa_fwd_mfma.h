@@ -53,6 +53,7 @@
 #include "fa_device.h"
 #include "fa_fwd_common.h"
 #include "fa_internal.h"
+#include "fa_poison.h"
 
 namespace fa {
 namespace {
@@ -108,6 +109,13 @@ __global__ __launch_bounds__(64 * waves_per_wg(FA_BF16, D, CAUSAL), 2) void fa_f
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hf = lane >> 5;
+  if constexpr (kPoisonLds) {                // test build only
+    poison_lds(k_lds0, TILE_BYTES, tid, NT);
+    poison_lds(k_lds1, TILE_BYTES, tid, NT);
+    poison_lds(v_lds0, TILE_BYTES, tid, NT);
+    poison_lds(v_lds1, TILE_BYTES, tid, NT);
+    __syncthreads();
+  }
 
   // a1: workgroup -> (unit = sequence b x head group, row block).
   // Workgroups are dealt round-robin over the 8 XCDs (workgroup j on XCD

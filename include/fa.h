@@ -353,6 +353,13 @@ int fa_supported(int in_dtype, int d, int causal);
 /* Static description of a status code; never NULL. */
 const char* fa_status_string(int status);
 
+/* Build flags of this library: bit 0 (FA_BUILD_POISON_LDS) is set in the
+ * LDS-poisoning test build (libfa_poison.so), whose kernels fill their LDS
+ * with NaN before use so that a read of LDS they never wrote shows in the
+ * result; the normal build returns 0.  Makes no HIP call. */
+#define FA_BUILD_POISON_LDS 1
+int fa_build_flags(void);
+
 /* Library version as major*10000 + minor*100 + patch (the Kotaemon page's
  * caveats recommend pinning versions). */
 int fa_version(void);

@@ -435,3 +435,17 @@ def test_force_order_from_environment(env, expected):
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
                          check=True, env=envs, cwd=ROOT)
     assert int(out.stdout.strip().splitlines()[-1]) == expected
+
+
+def test_poisoning_build_is_the_same_interface():
+    """libfa_poison.so (the LDS-poisoning test build) exports every declared
+    symbol and reports its flag; libfa.so does not."""
+    assert fa.load().fa_build_flags() == 0
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.POISON_LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)$", out, re.M))
+    assert set(declared_functions()) <= exported
+    with _lib.poisoned_lds() as lib:
+        assert lib.fa_build_flags() == 1
+        assert fa.load() is lib
+    assert fa.load().fa_build_flags() == 0
