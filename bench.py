@@ -102,9 +102,12 @@ def clock_of(counters, launch_ms: float):
     return counters["grbm_gui_active_per_dispatch"] / XCDS / (launch_ms * 1e6)
 
 
-def cpu_baseline(w, heads: int):
+def cpu_baseline(w, heads: int, o_gpu=None, lse_gpu=None):
     """The oracle, as it stands, on the first `heads` query heads (whole
-    sequences) of the workload, over a process pool of the host's cores."""
+    sequences) of the workload, over a process pool of the host's cores.
+    With the timed run's outputs (o_gpu, lse_gpu: host float64 arrays in the
+    workload's layout) it also reports their largest differences from the
+    oracle on that sample."""
     import numpy as np
 
     import oracle
@@ -124,32 +127,51 @@ def cpu_baseline(w, heads: int):
         ks = np.ascontiguousarray(k[:T, :hq // G])
         vs = np.ascontiguousarray(v[:T, :hq // G])
         t0 = time.perf_counter()
-        oracle.attention(qs, ks, vs, causal=w["causal"], scale=w["scale"], cu_seqlens=cu,
-                         workers=workers)
+        ref = oracle.attention(qs, ks, vs, causal=w["causal"], scale=w["scale"], cu_seqlens=cu,
+                               workers=workers)
         dt = time.perf_counter() - t0
         fl = hq * sum(oracle.unit_flops(int(n), w["d"], w["causal"]) for n in np.diff(cu))
+        got = None if o_gpu is None else (o_gpu[:T, :hq], lse_gpu[:nb, :hq])
+        if got is not None:     # the oracle's L spans the sample's longest sequence
+            got = (got[0], got[1][..., :int(np.diff(cu).max()) if nb else 0])
     else:
         qs = np.ascontiguousarray(q[:nb, :hq])
         ks = np.ascontiguousarray(k[:nb, :hq // G])
         vs = np.ascontiguousarray(v[:nb, :hq // G])
         t0 = time.perf_counter()
         if w.get("block_mask") is not None:
-            oracle.attention_block_sparse(qs, ks, vs, w["block_mask"], causal=w["causal"],
-                                          scale=w["scale"], workers=workers)
+            ref = oracle.attention_block_sparse(qs, ks, vs, w["block_mask"], causal=w["causal"],
+                                                scale=w["scale"], workers=workers)
             fl = nb * hq * 4.0 * w["d"] * oracle.sparse_pair_count(
                 w["block_mask"][0, 0], w["N"], w["Nk"], w["causal"])
         elif w["Nk"] != w["N"]:
-            oracle.attention_qk(qs, ks, vs, causal=w["causal"], scale=w["scale"],
-                                workers=workers)
+            ref = oracle.attention_qk(qs, ks, vs, causal=w["causal"], scale=w["scale"],
+                                      workers=workers)
             fl = nb * hq * 4.0 * w["d"] * oracle.pair_count(w["N"], w["Nk"], w["causal"])
         else:
-            oracle.attention(qs, ks, vs, causal=w["causal"], scale=w["scale"], workers=workers)
+            ref = oracle.attention(qs, ks, vs, causal=w["causal"], scale=w["scale"],
+                                   workers=workers)
             fl = nb * hq * oracle.unit_flops(w["N"], w["d"], w["causal"])
         dt = time.perf_counter() - t0
-    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
-            "sample": f"{nb} sequence(s) x {hq} query heads of {w['name']} "
-                      f"({nb * hq} of {w['B'] * w['Hq']} head-sequences), float64 numpy, "
-                      f"{dt:.2f} s wall"}
+        got = None if o_gpu is None else (o_gpu[:nb, :hq], lse_gpu[:nb, :hq])
+    rec = {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+           "sample": f"{nb} sequence(s) x {hq} query heads of {w['name']} "
+                     f"({nb * hq} of {w['B'] * w['Hq']} head-sequences), float64 numpy, "
+                     f"{dt:.2f} s wall"}
+    if got is not None:
+        # The oracle's L is NaN past a packed sequence's end (no such row)
+        # and -inf for a row with no visible key; the kernel's must be -inf
+        # exactly there too.
+        o_ref, l_ref = ref
+        row = ~np.isnan(l_ref)
+        fin = np.isfinite(l_ref)
+        rec["errors"] = {
+            "o_max_abs": float(np.max(np.abs(got[0] - o_ref))) if got[0].size else 0.0,
+            "l_max_abs": float(np.max(np.abs(got[1][fin] - l_ref[fin]))) if fin.any() else 0.0,
+            "l_neginf_match": bool(np.array_equal(np.isneginf(got[1][row]),
+                                                  np.isneginf(l_ref[row]))),
+            "of": "the timed run's O and L on the sample above, against the oracle"}
+    return rec
 
 
 def cpu_baseline_bwd(w, heads: int):
@@ -383,10 +405,20 @@ def main():
         torch.mul(src, 1.0, out=dst)   # one elementwise pass: n*4 bytes in, n*4 out
         torch.cuda.synchronize()
         rec["copy_calibration_bytes"] = n * 4
+    rec["device"] = {"name": torch.cuda.get_device_properties(dev).name,
+                     "arch": torch.cuda.get_device_properties(dev).gcnArchName,
+                     "cus": torch.cuda.get_device_properties(dev).multi_processor_count,
+                     "hip": torch.version.hip, "torch": torch.__version__,
+                     "library_version": fa.version(), "seed": w["seed"],
+                     "kernel_source_sha": source_digest(kname) if args.which == "fwd" else
+                     source_digest("fa_bwd")}
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = (cpu_baseline_bwd(w, args.cpu_sample_heads)
-                               if args.which == "bwd" else
-                               cpu_baseline(w, args.cpu_sample_heads))
+        if args.which == "bwd":
+            rec["cpu_baseline"] = cpu_baseline_bwd(w, args.cpu_sample_heads)
+        else:
+            rec["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_heads,
+                                               o.double().cpu().numpy(),
+                                               lse.double().cpu().numpy())
     print(json.dumps(rec), flush=True)
 
 
