@@ -120,7 +120,24 @@ def cpu_baseline(w, heads: int, o_gpu=None, lse_gpu=None):
     nb = min(w["B"], max(1, heads // w["Hq"]))
     hq = min(heads, w["Hq"])
     workers = oracle.default_workers()
-    if w["cu_seqlens"] is not None:
+    if w["cu_seqlens"] is not None and w.get("cu_seqlens_k") is not None:
+        # Packed sequences with their own key counts (the queries are the
+        # last tokens of each sequence).
+        cu, cuk = w["cu_seqlens"][:nb + 1], w["cu_seqlens_k"][:nb + 1]
+        T, Tk = int(cu[-1]), int(cuk[-1])
+        qs = np.ascontiguousarray(q[:T, :hq])
+        ks = np.ascontiguousarray(k[:Tk, :hq // G])
+        vs = np.ascontiguousarray(v[:Tk, :hq // G])
+        t0 = time.perf_counter()
+        ref = oracle.attention_qk(qs, ks, vs, causal=w["causal"], scale=w["scale"],
+                                  cu_seqlens_q=cu, cu_seqlens_k=cuk, workers=workers)
+        dt = time.perf_counter() - t0
+        fl = hq * 4.0 * w["d"] * sum(oracle.pair_count(int(a), int(c), w["causal"])
+                                     for a, c in zip(np.diff(cu), np.diff(cuk)))
+        got = None if o_gpu is None else (o_gpu[:T, :hq], lse_gpu[:nb, :hq])
+        if got is not None:     # the oracle's L spans the sample's most queries
+            got = (got[0], got[1][..., :int(np.diff(cu).max()) if nb else 0])
+    elif w["cu_seqlens"] is not None:
         cu = w["cu_seqlens"][:nb + 1]
         T = int(cu[-1])
         qs = np.ascontiguousarray(q[:T, :hq])

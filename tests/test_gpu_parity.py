@@ -139,7 +139,7 @@ def test_causal_unit_major_varlen():
     G.say(f"  errors {_compare(w, O, L, Oref, Lref)}")
 
 
-@pytest.mark.parametrize("name", ["mha_fp16", "gqa_bf16"])
+@pytest.mark.parametrize("name", ["mha_fp16", "gqa_bf16", "gqa_bf16_tp8"])
 def test_workload_full(name):
     w = workloads.make_inputs(name)
     G.say(f"workload {name}")

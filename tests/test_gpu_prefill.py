@@ -111,6 +111,21 @@ def test_chunks_reassemble_full_sequence():
         assert (lc - lf[:, :, i0:i0 + c]).abs().max().item() <= 1e-4
 
 
+def test_zigzag_share_workload_full():
+    """long_bf16_sp8 (one GPU's zig-zag share of long_bf16: 2048 queries
+    against 2048 keys and 2048 queries against 32768 keys, packed) at full
+    size, every row of every head against the oracle."""
+    w = workloads.make_inputs("long_bf16_sp8")
+    G.say("workload long_bf16_sp8")
+    O, L = _run(w)
+    q, k, v = G.f64_inputs(w)
+    Oref, Lref = oracle.attention_qk(q, k, v, causal=True, scale=w["scale"],
+                                     cu_seqlens_q=w["cu_seqlens"],
+                                     cu_seqlens_k=w["cu_seqlens_k"],
+                                     workers=min(16, oracle.default_workers()))
+    G.say(f"  errors {G.compare_qk(w, O, L, Oref, Lref)}")
+
+
 def test_prefill_workload_full():
     """The prefill_bf16 workload at full size (B=4, 32 query heads, the last
     1024 queries of 8192-token sequences), checked against the oracle on

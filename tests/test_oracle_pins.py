@@ -120,6 +120,21 @@ def test_varlen_lengths():
     assert w["N"] == lens.max()
 
 
+def test_shard_workloads():
+    """One GPU's shares: gqa_bf16 by K/V head (1 of 8) and long_bf16 by
+    zig-zag query rows (GPU 0 of 8: the first and the last 2048 rows)."""
+    t = workloads.make_inputs("gqa_bf16_tp8")
+    assert t["q"].shape == (4, 4, 4096, 128) and t["k"].shape == (4, 1, 4096, 128)
+    s = workloads.make_inputs("long_bf16_sp8")
+    assert list(s["cu_seqlens"]) == [0, 2048, 4096]
+    assert list(s["cu_seqlens_k"]) == [0, 2048, 2048 + 32768]
+    assert s["q"].shape == (4096, 32, 128) and s["k"].shape == (34816, 8, 128)
+    assert (s["N"], s["Nk"]) == (2048, 32768)
+    # Zig-zag balance: this share's visible pairs are 1/8 of long_bf16's.
+    share = sum(oracle.pair_count(2048, nk, True) for nk in (2048, 32768))
+    assert share * 8 == oracle.pair_count(32768, 32768, True)
+
+
 def test_workload_shapes():
     for name, wl in workloads.WORKLOADS.items():
         if wl.varlen or wl.N > 4096:

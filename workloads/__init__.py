@@ -22,6 +22,13 @@ storage precision with round-to-nearest-even.  The five named workloads are:
                   streaming block mask of 64 x 64 blocks: every query block
                   sees key block 0 (the "sink") and the 16 key blocks ending
                   at its own (a 1024-key window), causal
+* ``gqa_bf16_tp8`` one GPU's share of gqa_bf16 split over 8 GPUs by K/V
+                  head: B=4, Hq=4, Hkv=1, N=4096, d=128, bf16, causal
+* ``long_bf16_sp8`` one GPU's share of long_bf16 split over 8 GPUs by query
+                  rows in zig-zag order (GPU 0: rows [0, 2048) and
+                  [30720, 32768) of the 32768-token sequence): two packed
+                  sequences of 2048 queries, the last queries of 2048 and
+                  32768 keys, Hq=32, Hkv=8, d=128, bf16, causal
 
 When a workload has more keys than queries (``Nk``), k and v are drawn with
 the key count and the queries are the last tokens of each sequence.
@@ -69,6 +76,8 @@ class Workload:
     Nk: int = 0          # keys per sequence when more than the queries (0: = N)
     sink_blocks: int = 0     # block-sparse streaming mask (0 window: dense)
     window_blocks: int = 0
+    lengths_q: tuple = ()    # varlen with given query and key counts per sequence
+    lengths_k: tuple = ()
 
     @property
     def scale(self) -> float:
@@ -87,6 +96,9 @@ WORKLOADS = {
         Workload("decode_bf16", 32, 32, 8, 1, 128, "bf16", True, 1007, Nk=8192),
         Workload("streaming_bf16", 4, 32, 8, 4096, 128, "bf16", True, 1008,
                  sink_blocks=1, window_blocks=16),
+        Workload("gqa_bf16_tp8", 4, 4, 1, 4096, 128, "bf16", True, 1009),
+        Workload("long_bf16_sp8", 2, 32, 8, 2048, 128, "bf16", True, 1010, varlen=True,
+                 lengths_q=(2048, 2048), lengths_k=(2048, 32768)),
     ]
 }
 
@@ -217,11 +229,13 @@ def make_inputs(w: Workload | str) -> dict:
     if isinstance(w, str):
         w = WORKLOADS[w]
     rng = np.random.default_rng(w.seed)
-    lengths = None
-    if w.varlen:
+    lengths = lengths_k = None
+    if w.lengths_q:
+        lengths, lengths_k = list(w.lengths_q), list(w.lengths_k)
+    elif w.varlen:
         lengths = varlen_lengths(rng, w.B, w.len_lo, w.len_hi)
     out = _draw(rng, w.B, w.Hq, w.Hkv, w.d, w.dtype,
-                None if w.varlen else w.N, lengths, Nk=w.Nk or None)
+                None if w.varlen else w.N, lengths, Nk=w.Nk or None, lengths_k=lengths_k)
     out["causal"] = w.causal
     out["scale"] = w.scale
     out["name"] = w.name
