@@ -6,7 +6,7 @@ It only draws and rounds inputs; it holds none of the attention arithmetic.
 Each workload is a shape, an input precision and a seed.  Inputs are drawn
 as N(0, 1) in float32 with ``numpy.random.default_rng(seed)`` (in the order
 lengths (varlen only), q, k, v, each in C order) and then rounded to the
-storage precision with round-to-nearest-even.  The five named workloads are:
+storage precision with round-to-nearest-even.  The named workloads are:
 
 * ``tiny_fp32``   B=1, H=2, N=256, d=64, fp32, non-causal (exactness case)
 * ``mha_fp16``    B=8, H=12, N=2048, d=64, fp16, causal
