@@ -155,9 +155,10 @@ def grad_term_sums(w: dict):
     return tq, tk, tv
 
 
-def compare_qk(w, O, L, Oref, Lref, out_dtype="fp32"):
-    """Element-wise bars; rows that see no key must give O = 0, L = -inf;
-    L rows past a packed sequence's query count stay untouched (NaN)."""
+def compare_qk(w, O, L, Oref, Lref, out_dtype="fp32", bar=None):
+    """Element-wise bars (``bar``, if given, replaces the stated O bar); rows
+    that see no key must give O = 0, L = -inf; L rows past a packed
+    sequence's query count stay untouched (NaN)."""
     if w["cu_seqlens"] is not None:
         for b, n in enumerate(np.diff(w["cu_seqlens"])):
             assert np.isnan(L[b, :, n:]).all(), "padded lse rows must stay untouched"
@@ -166,7 +167,8 @@ def compare_qk(w, O, L, Oref, Lref, out_dtype="fp32"):
     assert np.array_equal(np.isneginf(L), none), "rows without keys"
     assert np.isfinite(O).all()
     eo = np.abs(O - Oref)
-    bar = o_bar(w["dtype"], out_dtype, Oref)
+    if bar is None:
+        bar = o_bar(w["dtype"], out_dtype, Oref)
     assert (eo <= bar).all(), f"O error {eo.max():.3e}"
     el = np.abs(np.where(none, 0.0, L - Lref))
     assert el.max() <= L_TOL, f"L error {el.max():.3e}"
