@@ -52,3 +52,51 @@ def test_committed_counter_summaries_are_well_formed():
         for key in ("hbm_bytes_per_launch", "grbm_gui_active_per_dispatch", "dispatch_ns"):
             assert t[key] > 0, (name, key)
         assert t["commands"], name
+
+
+def _custom(lengths_q=None, lengths_k=None, N=None, Nk=None):
+    import workloads
+    w = workloads.make_custom_qk(2, 4, 2, 64, "bf16", seed=5, Nq=N, Nk=Nk,
+                                 lengths_q=lengths_q, lengths_k=lengths_k)
+    w.update(causal=True, scale=0.125, name="custom", seed=5)
+    return w
+
+
+def test_cpu_baseline_reports_the_timed_outputs_errors():
+    """The CPU-baseline leg compares the outputs it is handed with the oracle
+    on its sample: exact outputs give zero error; a disturbed O entry, an L
+    row or a missing -inf show up (fixed, packed, and packed with separate
+    key counts)."""
+    import numpy as np
+
+    import bench
+    import oracle
+    import workloads
+    cases = [dict(N=70, Nk=70), dict(N=30, Nk=90),
+             dict(lengths_q=[33, 5], lengths_k=[33, 5]),
+             dict(lengths_q=[8, 20], lengths_k=[40, 0])]
+    for kw in cases:
+        w = _custom(**kw)
+        q, k, v = (workloads.to_f64(w[x], "bf16") for x in "qkv")
+        if w["cu_seqlens"] is None:
+            O, L = oracle.attention_qk(q, k, v, causal=True, scale=0.125)
+        else:
+            O, L = oracle.attention_qk(q, k, v, causal=True, scale=0.125,
+                                       cu_seqlens_q=w["cu_seqlens"],
+                                       cu_seqlens_k=w["cu_seqlens_k"])
+            if kw["lengths_q"] == kw["lengths_k"]:
+                w["cu_seqlens_k"] = None     # equal counts: the plain packed form
+        Lg = np.where(np.isnan(L), 7.0, L)  # the kernel leaves padding rows alone
+        e = bench.cpu_baseline(w, 0, O, Lg)["errors"]
+        assert e["o_max_abs"] == 0.0 and e["l_max_abs"] == 0.0 and e["l_neginf_match"], kw
+        O2 = O.copy()
+        O2.reshape(-1)[5] += 1e-3
+        L2 = Lg.copy()
+        fin = np.argwhere(np.isfinite(L))[0]
+        L2[tuple(fin)] += 2e-3
+        e = bench.cpu_baseline(w, 0, O2, L2)["errors"]
+        assert abs(e["o_max_abs"] - 1e-3) < 1e-12 and abs(e["l_max_abs"] - 2e-3) < 1e-12, kw
+        if np.isneginf(L).any():
+            L3 = Lg.copy()
+            L3[np.isneginf(L)] = 0.0
+            assert not bench.cpu_baseline(w, 0, O, L3)["errors"]["l_neginf_match"], kw
